@@ -1,0 +1,380 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused GEMM + tensor/expert-parallel data-movement path on
+one MI355X, for one rank's share of a TP=8 / EP=8 layer step.
+
+One step (all on one GPU, inputs resident in HBM):
+  1. AllGather-GEMM, dense MLP layer 0 at TP=8: the rank's own 512 x 12288
+     chunk is in place; the other seven chunks are pushed into the gathered
+     buffer by a side stream (fm_chunk_push, per-chunk flags) while
+     fm_ag_gemm computes Output1 = X[4096 x 12288] * W1[12288 x 6144] (fp16).
+  2. GEMM-ReduceScatter, dense MLP layer 1: Output1 * W2[6144 x 12288] added
+     into eight fp32 [512 x 12288] rank slices (fm_gemm_rs).
+  3. MoE layer at EP=8, rank 0: 16384 tokens x 4096, 64 experts top-2 with a
+     log-Zipf(1.2) router bias, 8 local experts with W1 [4096 x 2816] and
+     W2 [2816 x 4096] (bf16): route + gather-GEMM (fm_moe_gather_gemm), then
+     GEMM + weighted scatter-reduce (fm_moe_gemm_scatter).
+
+value = algorithmic flops of the whole step / step time, in TFLOP/s.
+Also reported: per-operator TFLOP/s and fraction of the 2516.6 TFLOP/s dense
+fp16/bf16 MFMA peak, and the effective communication time
+ECT = OverallTime - GEMM_non-split (FLUX review, "核心公式") of the fused
+AllGather and ReduceScatter operators against the non-split GEMM (this
+library's and hipBLASLt's through torch.matmul) and against the naive
+chunk-by-chunk launch sequence.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = 2516.6          # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+METRIC = "fused AG/RS-GEMM TFLOP/s & % MFMA peak; ECT vs non-split GEMM"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--ect-iters", type=int, default=20)
+    ap.add_argument("--no-ect", action="store_true", help="skip the ECT comparisons")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256,
+                    help="rows of the AllGather-GEMM the CPU oracle computes as its sample")
+    return ap.parse_args()
+
+
+class Workload:
+    """Device buffers of the step, filled from the seeded generators."""
+
+    def __init__(self):
+        import numpy as np
+        import torch
+
+        import workloads as wl
+        dev = torch.device("cuda:0")
+        self.dev = dev
+        ag, rs, moe = wl.AG_TP8, wl.RS_TP8, wl.MOE_EP8
+        self.n, self.Mc, self.N1, self.K1 = ag["n_chunks"], ag["Mc"], ag["N"], ag["K"]
+        self.M = self.n * self.Mc
+        self.N2, self.K2, self.P = rs["N"], rs["K"], rs["n_ranks"]
+        assert self.K2 == self.N1 and rs["M"] == self.M
+        f16 = torch.float16
+        bf16 = torch.bfloat16
+
+        def up(bits, dt):
+            return torch.from_numpy(np.ascontiguousarray(bits)).view(dt).to(dev)
+
+        log("generating dense inputs")
+        chunks, W1, _ = wl.ag_inputs(self.n, self.Mc, self.N1, self.K1, wl.F16, seed=ag["seed"])
+        self.chunks_host = chunks
+        self.W1_host = W1
+        self.peers = [up(chunks[c], f16) for c in range(self.n)]
+        self.X = torch.empty((self.M, self.K1), dtype=f16, device=dev)
+        self.X[: self.Mc].copy_(self.peers[0])            # rank 0's own chunk
+        self.W1 = up(W1, f16)
+        self.Out1 = torch.empty((self.M, self.N1), dtype=f16, device=dev)
+        _, W2, seeds = wl.rs_inputs(self.M, self.N2, self.K2, self.P, wl.F16, seed=rs["seed"])
+        self.W2 = up(W2, f16)
+        self.dst = [torch.from_numpy(seeds[r]).to(dev) for r in range(self.P)]
+        self.flags = torch.zeros(self.n, dtype=torch.int32, device=dev)
+        self.counters = torch.zeros(self.n, dtype=torch.int32, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.epoch = 0
+
+        log("generating MoE inputs")
+        self.T, self.hidden, self.ffn = moe["T"], moe["hidden"], moe["ffn"]
+        self.n_local, self.topk = moe["n_local"], moe["topk"]
+        self.e0 = moe["rank"] * moe["n_local"]
+        inp = wl.moe_inputs(self.T, self.hidden, self.ffn, moe["n_experts"], self.n_local,
+                            self.topk, wl.BF16, seed=moe["seed"], zipf_s=moe["zipf_s"])
+        ids = inp["topk_ids"]
+        self.rows_local = int(((ids >= self.e0) & (ids < self.e0 + self.n_local)).sum())
+        self.mX = up(inp["X"], bf16)
+        self.mW1 = up(inp["W1"], bf16)
+        self.mW2 = up(inp["W2"], bf16)
+        self.ids = torch.from_numpy(ids).to(dev)
+        self.wts = torch.from_numpy(inp["topk_weights"]).to(dev)
+        self.mout = torch.from_numpy(inp["out_seed"]).to(dev)
+        self.H = torch.empty((self.T * self.topk, self.ffn), dtype=bf16, device=dev)
+        self.sp = torch.empty(self.T * self.topk, dtype=torch.int32, device=dev)
+        self.off = torch.zeros(self.n_local + 1, dtype=torch.int32, device=dev)
+
+        self.side = torch.cuda.Stream(device=dev)
+        self.order = list(range(self.n))                  # local chunk first, then ring order
+        self.flop_ag = 2.0 * self.M * self.N1 * self.K1
+        self.flop_rs = 2.0 * self.M * self.N2 * self.K2
+        self.flop_moe = 2.0 * 2 * self.rows_local * self.hidden * self.ffn
+        torch.cuda.synchronize()
+
+    # -- pieces of a step ----------------------------------------------------
+    def push_all(self, epoch):
+        import tile_gemm_communication_amd as fm
+        import torch
+        cs = torch.cuda.current_stream()
+        self.side.wait_stream(cs)
+        with torch.cuda.stream(self.side):
+            fm.fm_chunk_push(None, None, self.flags[0:1], self.counters[0:1], epoch,
+                             stream=self.side)
+            for c in self.order[1:]:
+                fm.fm_chunk_push(self.peers[c], self.X[c * self.Mc:(c + 1) * self.Mc],
+                                 self.flags[c:c + 1], self.counters[c:c + 1], epoch,
+                                 stream=self.side)
+
+    def ag(self, epoch):
+        import tile_gemm_communication_amd as fm
+        fm.fm_ag_gemm(self.X, self.W1, self.Out1, self.flags, epoch, self.n, order=self.order,
+                      err_word=self.err)
+
+    def rs(self):
+        import tile_gemm_communication_amd as fm
+        fm.fm_gemm_rs(self.Out1, self.W2, self.dst, rank=0)
+
+    def moe0(self):
+        import tile_gemm_communication_amd as fm
+        fm.fm_moe_gather_gemm(self.mX, self.ids, self.mW1, self.H, self.sp, self.off, self.e0)
+
+    def moe1(self):
+        import tile_gemm_communication_amd as fm
+        fm.fm_moe_gemm_scatter(self.H, self.mW2, self.sp, self.off, self.wts, self.mout)
+
+    def step(self, evs=None):
+        """One full step on the current stream (+ the side stream for arrival).
+        evs: optional list of 5 events bracketing AG | RS | MoE0 | MoE1."""
+        import torch
+        cs = torch.cuda.current_stream()
+        self.epoch += 1
+        self.push_all(self.epoch)
+        if evs: evs[0].record(cs)
+        self.ag(self.epoch)
+        if evs: evs[1].record(cs)
+        cs.wait_stream(self.side)
+        self.rs()
+        if evs: evs[2].record(cs)
+        self.moe0()
+        if evs: evs[3].record(cs)
+        self.moe1()
+        if evs: evs[4].record(cs)
+
+
+def time_loop(fn, iters, warmup):
+    """Median per-iteration time (ms) of fn() on the current stream, with events."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    cs = torch.cuda.current_stream()
+    times = []
+    for _ in range(iters):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(cs)
+        fn()
+        b.record(cs)
+        times.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(x.elapsed_time(y) for x, y in times)
+    return ms[len(ms) // 2], ms[0]
+
+
+def ect_block(w, iters):
+    """ECT of the fused AllGather / ReduceScatter operators."""
+    import torch
+
+    import tile_gemm_communication_amd as fm
+    cs = torch.cuda.current_stream()
+    res = {}
+
+    # --- AllGather-GEMM -----------------------------------------------------
+    def ns_fm():
+        fm.fm_gemm(w.X, w.W1, w.Out1)
+
+    def ns_blas():
+        torch.matmul(w.X, w.W1, out=w.Out1)
+
+    def fused():
+        w.epoch += 1
+        w.push_all(w.epoch)
+        w.ag(w.epoch)
+        cs.wait_stream(w.side)
+
+    chunk_ev = [torch.cuda.Event() for _ in range(w.n)]
+
+    def naive():
+        # the prior-art sequence: one GEMM launch per chunk, each after its chunk
+        w.epoch += 1
+        w.side.wait_stream(cs)
+        with torch.cuda.stream(w.side):
+            for c in w.order[1:]:
+                fm.fm_chunk_push(w.peers[c], w.X[c * w.Mc:(c + 1) * w.Mc], w.flags[c:c + 1],
+                                 w.counters[c:c + 1], w.epoch, stream=w.side)
+                chunk_ev[c].record(w.side)
+        for c in w.order:
+            if c != w.order[0]:
+                cs.wait_event(chunk_ev[c])
+            rows = slice(c * w.Mc, (c + 1) * w.Mc)
+            fm.fm_gemm(w.X[rows], w.W1, w.Out1[rows])
+        cs.wait_stream(w.side)
+
+    log("ECT: AllGather-GEMM")
+    for name, fn in [("nonsplit_fm_gemm", ns_fm), ("nonsplit_hipblaslt", ns_blas),
+                     ("fused", fused), ("naive_chunked", naive)]:
+        med, best = time_loop(fn, iters, 3)
+        res[f"ag_{name}_ms"] = round(med, 4)
+    nonsplit = min(res["ag_nonsplit_fm_gemm_ms"], res["ag_nonsplit_hipblaslt_ms"])
+    res["ag_ect_ms"] = round(res["ag_fused_ms"] - nonsplit, 4)
+    res["ag_ect_vs_fm_gemm_ms"] = round(res["ag_fused_ms"] - res["ag_nonsplit_fm_gemm_ms"], 4)
+    res["ag_ect_naive_ms"] = round(res["ag_naive_chunked_ms"] - nonsplit, 4)
+    res["ag_ect_frac_of_nonsplit"] = round(res["ag_ect_ms"] / nonsplit, 4)
+    assert int(w.err.item()) == 0, "fm_ag_gemm reported a timeout"
+
+    # --- GEMM-ReduceScatter -------------------------------------------------
+    tmp16 = torch.empty((w.M, w.N2), dtype=torch.float16, device=w.dev)
+    tmp32 = torch.empty((w.M, w.N2), dtype=torch.float32, device=w.dev)
+    Ms = w.M // w.P
+
+    def rs_ns_fm():
+        fm.fm_gemm(w.Out1, w.W2, tmp16)
+
+    def rs_ns_blas():
+        torch.matmul(w.Out1, w.W2, out=tmp16)
+
+    def rs_fused():
+        w.rs()
+
+    def rs_naive():
+        for s in range(w.P):
+            r = (s + 1) % w.P
+            rows = slice(r * Ms, (r + 1) * Ms)
+            fm.fm_gemm(w.Out1[rows], w.W2, tmp32[rows])
+            w.dst[r].add_(tmp32[rows])
+
+    log("ECT: GEMM-ReduceScatter")
+    for name, fn in [("nonsplit_fm_gemm", rs_ns_fm), ("nonsplit_hipblaslt", rs_ns_blas),
+                     ("fused", rs_fused), ("naive_chunked", rs_naive)]:
+        med, best = time_loop(fn, iters, 3)
+        res[f"rs_{name}_ms"] = round(med, 4)
+    nonsplit = min(res["rs_nonsplit_fm_gemm_ms"], res["rs_nonsplit_hipblaslt_ms"])
+    res["rs_ect_ms"] = round(res["rs_fused_ms"] - nonsplit, 4)
+    res["rs_ect_vs_fm_gemm_ms"] = round(res["rs_fused_ms"] - res["rs_nonsplit_fm_gemm_ms"], 4)
+    res["rs_ect_naive_ms"] = round(res["rs_naive_chunked_ms"] - nonsplit, 4)
+    res["rs_ect_frac_of_nonsplit"] = round(res["rs_ect_ms"] / nonsplit, 4)
+    res["nonsplit_fm_gemm_tflops_4096x12288x6144"] = round(
+        w.flop_rs / (res["rs_nonsplit_fm_gemm_ms"] * 1e-3) / 1e12, 1)
+    res["nonsplit_hipblaslt_tflops_4096x12288x6144"] = round(
+        w.flop_rs / (res["rs_nonsplit_hipblaslt_ms"] * 1e-3) / 1e12, 1)
+    return res
+
+
+def cpu_baseline(w, rows):
+    """The CPU oracle, untuned, on a bounded sample of the AllGather-GEMM:
+    `rows` output rows of Output1 = X * W1 (fp64 accumulation)."""
+    import numpy as np
+
+    import oracle
+    orc = oracle.load()
+    X = np.concatenate(list(w.chunks_host), axis=0)[:rows]
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    orc.gemm(0, X, w.W1_host)
+    dt = time.perf_counter() - t0
+    flop = 2.0 * rows * w.N1 * w.K1
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"AllGather-GEMM rows 0..{rows - 1} of 4096 "
+                      f"({rows}x{w.N1}x{w.K1}, fp64 accumulation)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the fused kernels "
+                                   "emulate the peers of a TP=8/EP=8 group on one device; "
+                                   "run with --gpus 1"}))
+        sys.exit(2)
+    import torch
+
+    import tile_gemm_communication_amd as fm
+    fm.lib()                                   # fail loudly if the library is missing
+    log(f"libfluxmi {fm.version()} on {torch.cuda.get_device_name(0)}")
+    w = Workload()
+    cs = torch.cuda.current_stream()
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        w.step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        w.step(evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    assert int(w.err.item()) == 0, "fm_ag_gemm reported a timeout"
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    names = ["ag_gemm", "gemm_rs", "moe_gather_gemm", "moe_gemm_scatter"]
+    durs = {n: sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)) / args.steps
+            for i, n in enumerate(names)}
+    flops = {"ag_gemm": w.flop_ag, "gemm_rs": w.flop_rs,
+             "moe_gather_gemm": w.flop_moe / 2, "moe_gemm_scatter": w.flop_moe / 2}
+    total_flop = sum(flops.values())
+    value = total_flop / (ms_step * 1e-3) / 1e12
+    ops = {n: {"ms": round(durs[n], 4),
+               "tflops": round(flops[n] / (durs[n] * 1e-3) / 1e12, 1),
+               "frac_peak": round(flops[n] / (durs[n] * 1e-3) / 1e12 / PEAK_TFLOPS, 4)}
+           for n in names}
+    dom = max(names, key=lambda n: durs[n])
+    achieved = flops[dom] / (durs[dom] * 1e-3) / 1e12
+    log(f"step {ms_step:.3f} ms, {value:.1f} TFLOP/s; " +
+        ", ".join(f"{n} {ops[n]['ms']:.3f} ms {ops[n]['tflops']} TF" for n in names))
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16/bf16 (fp32 accumulate)",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1)/sqrt(K) weights, log-Zipf router)",
+        "config": {
+            "workload": "one rank of a TP=8/EP=8 layer step: AllGather-GEMM 4096x6144x12288 "
+                        "(8 chunks of 512 rows, 7 pushed by a side stream) -> GEMM-ReduceScatter "
+                        "4096x12288x6144 into 8 fp32 slices (fp16); MoE 16384 tokens x 4096, "
+                        "64 experts top-2, 8 local, ffn 2816 (bf16)",
+            "moe_rows_local": w.rows_local,
+            "step_flop": total_flop,
+        },
+        "ops": ops,
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_ect:
+        out["ect"] = ect_block(w, args.ect_iters)
+    if not args.no_cpu_baseline:
+        log(f"CPU oracle sample ({args.cpu_rows} rows)")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

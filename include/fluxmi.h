@@ -1,0 +1,201 @@
+/*
+ * fluxmi.h -- C ABI of libfluxmi: tile-granular GEMM fused with the
+ * tensor-/expert-parallel data movement around it, for AMD Instinct MI355X
+ * (gfx950), one GPU's share of the work.
+ *
+ * Operators (after the Flux README's five kernels, "快速开始"):
+ *   fm_gemm              plain GEMM (the "gemm_only" reference point)
+ *   fm_ag_gemm           AllGather fused with GEMM (dense MLP layer 0)
+ *   fm_gemm_rs           GEMM fused with ReduceScatter (dense MLP layer 1)
+ *   fm_moe_gather_gemm   token gather fused with grouped expert GEMM (MoE layer 0)
+ *   fm_moe_gemm_scatter  grouped expert GEMM fused with top-k weighted
+ *                        scatter-reduce (MoE layer 1)
+ * plus the producer half of the chunk-arrival protocol (fm_chunk_push) and
+ * the routing index on its own (fm_moe_route).
+ *
+ * Conventions for every call:
+ *  - All matrices are dense and row-major.  A / X are [M, K]; B / W are [K, N].
+ *  - Every pointer argument that names a matrix, flag or index buffer is a
+ *    device pointer to memory owned by the caller; the library allocates
+ *    nothing, keeps no state between calls beyond cached device properties,
+ *    and never synchronizes the host.  Calls are enqueued on `stream` (NULL =
+ *    the null stream) and return before the work runs.
+ *  - 16-bit operands are IEEE binary16 (FM_F16) or bfloat16 (FM_BF16); every
+ *    product is accumulated in fp32; narrowing to 16 bits rounds to nearest
+ *    even.
+ *  - Shape requirements: sizes >= 0; N and K multiples of 8; matrix pointers
+ *    16-byte aligned.  A size of 0 in M or N makes the call a no-op; K == 0
+ *    yields a zero product.
+ *  - Errors: arguments are validated before anything is launched; an invalid
+ *    call returns FM_ERR_INVALID_ARG or FM_ERR_UNSUPPORTED and enqueues no
+ *    work.  FM_ERR_HIP means the launch itself failed.  A wait that gives up
+ *    inside a kernel cannot be returned; it is written to `err_word` instead
+ *    (see fm_ag_gemm).  No C++ exception crosses this interface.
+ *  - Calls that write the same output on one stream are ordered; calls on
+ *    different streams that write the same buffer race.
+ */
+#ifndef FLUXMI_H
+#define FLUXMI_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fm_status {
+    FM_OK = 0,
+    FM_ERR_INVALID_ARG = 1,   /* null / misaligned pointer, bad size or count */
+    FM_ERR_UNSUPPORTED = 2,   /* dtype combination or size the kernels do not cover */
+    FM_ERR_HIP = 3,           /* the HIP launch failed */
+    FM_ERR_TIMEOUT = 4        /* only ever written to err_word by a kernel */
+} fm_status_t;
+
+typedef enum fm_dtype {
+    FM_F16 = 0,
+    FM_BF16 = 1,
+    FM_F32 = 2
+} fm_dtype_t;
+
+/* Library version, major*10000 + minor*100 + patch. */
+int fm_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* fm_status_str(fm_status_t status);
+
+/*
+ * fm_gemm -- C[M,N] = A[M,K] * B[K,N].
+ * Defined by the GEMM in the FLUX review's MLP equations (section 三,
+ * "MLP 前向传播"); it is also the non-split GEMM that the effective
+ * communication time ECT = OverallTime - GEMM_non-split is measured against
+ * (same review, "核心公式").
+ *   ab   FM_F16 or FM_BF16: element type of A and B.
+ *   c    FM_F16, FM_BF16 (same as ab) or FM_F32: element type of C.
+ *   A    [M, K] row-major, B [K, N] row-major, C [M, N] row-major (written).
+ * C must not overlap A or B.
+ */
+fm_status_t fm_gemm(fm_dtype_t ab, fm_dtype_t c, int64_t M, int64_t N, int64_t K,
+                    const void* A, const void* B, void* C, hipStream_t stream);
+
+/*
+ * fm_ag_gemm -- Output1 = GEMM(AllGather(X), W1) with tile-granular overlap
+ * (FLUX review, "MLP 前向传播" first GEMM and "AllGather 重叠": the gather and
+ * the GEMM are split into tiles and fused in one kernel).
+ *   X        [M, K] gathered activation buffer.  Row chunk c = rows
+ *            [c*M/n_chunks, (c+1)*M/n_chunks) is written by a producer (a
+ *            peer, or fm_chunk_push on another stream) and may be read only
+ *            once flags[c] >= epoch.
+ *   W        [K, N] weight shard; C [M, N] output (written), dt elements.
+ *   n_chunks 1..64, and M % n_chunks == 0.
+ *   flags    device array of n_chunks uint32 ready flags.  A producer writes
+ *            the chunk, then publishes flags[c] = epoch with release
+ *            semantics.  Epochs grow from call to call so flags never need
+ *            resetting; the caller zero-fills them once.
+ *   order    host array of n_chunks chunk indices, the expected arrival order
+ *            (e.g. the local chunk first), or NULL for index order.  It only
+ *            orders the tiles; the result does not depend on it.
+ *   err_word device int32 or NULL.  If a wait exceeds spin_limit polls the
+ *            kernel writes FM_ERR_TIMEOUT there, abandons its remaining tiles
+ *            (C is then undefined) and exits; the call never hangs.
+ *   spin_limit  polls before giving up (each poll sleeps ~0.1 us); 0 selects
+ *            the default of 2^24 polls.
+ * The result equals fm_gemm on the fully gathered X, bit for bit.
+ */
+fm_status_t fm_ag_gemm(fm_dtype_t dt, int64_t M, int64_t N, int64_t K, int32_t n_chunks,
+                       const void* X, const void* W, void* C,
+                       const uint32_t* flags, uint32_t epoch, const int32_t* order,
+                       int32_t* err_word, int64_t spin_limit, hipStream_t stream);
+
+/*
+ * fm_chunk_push -- producer side of the chunk-arrival protocol: copy `bytes`
+ * from src to dst, then publish *flag = epoch (release, device scope) once
+ * every byte is visible.  This is what a peer rank's push (the review's
+ * "推送模式" in "拉取 vs 推送数据传输") does to this rank's gathered buffer; on
+ * one GPU src and dst are both local.
+ *   bytes    multiple of 16 (0 = publish the flag only); src/dst 16-byte aligned
+ *            and non-overlapping.
+ *   counter  device uint32 scratch owned by the caller, zero before the
+ *            first call and left zero after every call; one per flag in use.
+ *   n_workgroups  copy workgroups, 0 = default (64).
+ */
+fm_status_t fm_chunk_push(const void* src, void* dst, int64_t bytes, uint32_t* flag,
+                          uint32_t* counter, uint32_t epoch, int32_t n_workgroups,
+                          hipStream_t stream);
+
+/*
+ * fm_gemm_rs -- Output2 = ReduceScatter(GEMM(Output1, W2)), this rank's part
+ * (FLUX review, "MLP 前向传播" second GEMM and "ReduceScatter 重叠").
+ *   A        [M, K] (K = this rank's shard of the reduction), W [K, N].
+ *   dst      host array of n_ranks device pointers; dst[r] is the fp32
+ *            [M/n_ranks, N] slice owned by rank r and already holds the other
+ *            ranks' partial sums.  The call adds (A*W)[rows of r] into dst[r]
+ *            for every r: dst[r] += partial.
+ *   n_ranks  1..16, M % n_ranks == 0; rank in [0, n_ranks).
+ *            Tiles are taken slice by slice starting at (rank+1) % n_ranks
+ *            (the review's tile-coordinate swizzling, "瓦片坐标 Swizzling").
+ *   atomic   0: plain read-add-write (this call is the only writer of dst);
+ *            1: fp32 atomic adds (several concurrent writers allowed).
+ *   dt       FM_F16 or FM_BF16 for A and W.
+ */
+fm_status_t fm_gemm_rs(fm_dtype_t dt, int64_t M, int64_t N, int64_t K, int32_t n_ranks,
+                       int32_t rank, const void* A, const void* W, float* const* dst,
+                       int32_t atomic, hipStream_t stream);
+
+/*
+ * fm_moe_route -- expert-sorted row index of this rank's local experts
+ * (COMET article, "COMET 的技术原理": the tensor shared between the MoE
+ * layers is decomposed along the token dimension).
+ *   topk_ids      device int32 [T, topk]: expert of pair p = t*topk + k.
+ *   expert_begin  first local expert; local experts are
+ *                 [expert_begin, expert_begin + n_local), n_local 1..64.
+ *   expert_offsets  device int32 [n_local+1] (written): exclusive prefix sum
+ *                 of the local per-expert pair counts.
+ *   sorted_pairs  device int32 [T*topk] (written): positions
+ *                 [0, expert_offsets[n_local]) hold the local pair ids stably
+ *                 sorted by expert (increasing pair id within an expert); the
+ *                 rest is left untouched.
+ * Deterministic: identical bits on every call.
+ */
+fm_status_t fm_moe_route(int64_t T, int32_t topk, int32_t expert_begin, int32_t n_local,
+                         const int32_t* topk_ids, int32_t* sorted_pairs,
+                         int32_t* expert_offsets, hipStream_t stream);
+
+/*
+ * fm_moe_gather_gemm -- MoE layer 0 on this rank: route (as fm_moe_route),
+ * then for local expert e and its j-th pair p:
+ *   H[expert_offsets[e] + j, :] = X[p / topk, :] * W1[e]
+ * (Flux README: grouped GEMM of MoE MLP layer 0; the token gather is fused
+ * into the GEMM's A loads).  Row counts stay on the device: no host sync.
+ *   X   [T, hidden]; W1 [n_local, hidden, ffn]; H [T*topk, ffn] (rows past
+ *       expert_offsets[n_local] are left untouched).  dt FM_F16 or FM_BF16.
+ */
+fm_status_t fm_moe_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn,
+                               int32_t topk, int32_t expert_begin, int32_t n_local,
+                               const void* X, const int32_t* topk_ids, const void* W1,
+                               void* H, int32_t* sorted_pairs, int32_t* expert_offsets,
+                               hipStream_t stream);
+
+/*
+ * fm_moe_gemm_scatter -- MoE layer 1 on this rank with the top-k weighted
+ * combine fused into the GEMM epilogue (Flux README: grouped GEMM fused with
+ * the reduce-scatter of MoE MLP layer 1):
+ *   out[t, :] += sum over local pairs p = t*topk + k of
+ *                topk_weights[p] * (H[row(p), :] * W2[e(p)])
+ * where row(p) is p's position in sorted_pairs (from fm_moe_gather_gemm /
+ * fm_moe_route with the same arguments).
+ *   H [rows, ffn] with rows = expert_offsets[n_local]; W2 [n_local, ffn, hidden];
+ *   topk_weights device fp32 [T, topk]; out device fp32 [T, hidden] (accumulated
+ *   with fp32 atomic adds, so the order of the <= topk additions per element is
+ *   unspecified).
+ */
+fm_status_t fm_moe_gemm_scatter(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn,
+                                int32_t topk, int32_t n_local, const void* H, const void* W2,
+                                const int32_t* sorted_pairs, const int32_t* expert_offsets,
+                                const float* topk_weights, float* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLUXMI_H */

@@ -1,0 +1,145 @@
+"""GPU parity of the MoE path (fm_moe_route, fm_moe_gather_gemm,
+fm_moe_gemm_scatter) against the CPU oracle: routing buffers bit-exact,
+expert outputs and the weighted combine within the parity bar (on the delta
+out - seed)."""
+import numpy as np
+import pytest
+
+import workloads as wl
+from gpu_util import BF16, F16, assert_close, bits16, dev16, devf32, host64, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _i32(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to("cuda:0")
+
+
+def _route(ids, e0, nl):
+    import torch
+    import tile_gemm_communication_amd as fm
+    T, k = ids.shape
+    sp = torch.full((T * k,), -1, dtype=torch.int32, device="cuda:0")
+    off = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
+    fm.fm_moe_route(_i32(ids), e0, nl, sp, off)
+    torch.cuda.synchronize()
+    off_h = off.cpu().numpy()
+    return off_h, sp.cpu().numpy()[:off_h[-1]]
+
+
+@pytest.mark.parametrize("T,E,topk,e0,nl", [(256, 16, 2, 4, 4), (5000, 64, 2, 0, 8),
+                                            (3, 8, 1, 0, 8), (1000, 64, 4, 56, 8),
+                                            (20000, 128, 2, 0, 64)])
+def test_route_bit_exact(oracle, T, E, topk, e0, nl):
+    ids, _ = wl.moe_routing(T, E, topk, seed=T + E)
+    off, sp = _route(ids, e0, nl)
+    roff, rsp = oracle.moe_route(ids, e0, nl)
+    assert np.array_equal(off, roff) and np.array_equal(sp, rsp)
+
+
+def test_route_edges(oracle):
+    ids = np.full((50, 2), 9, dtype=np.int32)
+    off, sp = _route(ids, 0, 8)        # nothing local
+    assert off.tolist() == [0] * 9 and sp.size == 0
+    ids = np.zeros((37, 2), dtype=np.int32)
+    ids[:, 1] = 3
+    off, sp = _route(ids, 0, 4)        # two experts take everything, two are empty
+    roff, rsp = oracle.moe_route(ids, 0, 4)
+    assert np.array_equal(off, roff) and np.array_equal(sp, rsp)
+
+
+def _moe_run(inp, e0, nl, dt, H_in=None):
+    import torch
+    import tile_gemm_communication_amd as fm
+    ids, wts = inp["topk_ids"], inp["topk_weights"]
+    T, topk = ids.shape
+    ffn = inp["W1"].shape[2]
+    hidden = inp["X"].shape[1]
+    sp = torch.full((T * topk,), -1, dtype=torch.int32, device="cuda:0")
+    off = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
+    H = torch.zeros((T * topk, ffn), dtype=torch.float16 if dt == F16 else torch.bfloat16,
+                    device="cuda:0")
+    fm.fm_moe_gather_gemm(dev16(inp["X"], dt), _i32(ids), dev16(inp["W1"], dt), H, sp, off, e0)
+    out = devf32(inp["out_seed"])
+    Hsrc = H if H_in is None else dev16(H_in, dt)
+    fm.fm_moe_gemm_scatter(Hsrc, dev16(inp["W2"], dt), sp, off, devf32(wts), out)
+    torch.cuda.synchronize()
+    return off.cpu().numpy(), sp.cpu().numpy(), H, out
+
+
+@pytest.mark.parametrize("dt", [F16, BF16])
+@pytest.mark.parametrize("T,hidden,ffn,E,nl,e0", [(256, 256, 128, 16, 4, 4),
+                                                  (300, 136, 264, 8, 8, 0),
+                                                  (64, 512, 512, 64, 8, 0)])
+def test_moe_small(oracle, dt, T, hidden, ffn, E, nl, e0):
+    say(f"moe T={T} hidden={hidden} ffn={ffn} E={E} nl={nl} e0={e0} dt={dt}")
+    inp = wl.moe_inputs(T, hidden, ffn, E, nl, 2, dt, seed=T + hidden, zipf_s=1.2)
+    roff, rsp = oracle.moe_route(inp["topk_ids"], e0, nl)
+    Href = oracle.moe_layer0(dt, inp["X"], inp["W1"], rsp, roff, 2)
+    Hb = oracle.round_bf16(Href) if dt == BF16 else oracle.round_f16(Href)
+    off, sp, H, out = _moe_run(inp, e0, nl, dt, H_in=Hb)
+    rows = int(roff[-1])
+    assert np.array_equal(off, roff) and np.array_equal(sp[:rows], rsp)
+    assert_close(host64(H[:rows]), Href, "moe layer0 H")
+    ref = oracle.moe_layer1(dt, Hb, inp["W2"], inp["topk_ids"], inp["topk_weights"], rsp, roff,
+                            inp["out_seed"], e0)
+    assert_close(host64(out) - inp["out_seed"], ref - inp["out_seed"], "moe combine")
+
+
+def test_moe_one_hot_expert(oracle):
+    """All tokens routed to one local expert with weight 1 (top-1): the layer
+    reduces to seed + (X W1) W2 for that expert."""
+    T, hidden, ffn = 520, 128, 136
+    inp = wl.moe_inputs(T, hidden, ffn, 4, 4, 1, BF16, seed=5)
+    inp["topk_ids"] = np.full((T, 1), 2, dtype=np.int32)
+    inp["topk_weights"] = np.ones((T, 1), dtype=np.float32)
+    roff, rsp = oracle.moe_route(inp["topk_ids"], 0, 4)
+    Hb = oracle.round_bf16(oracle.moe_layer0(BF16, inp["X"], inp["W1"], rsp, roff, 1))
+    off, sp, H, out = _moe_run(inp, 0, 4, BF16, H_in=Hb)
+    ref = oracle.moe_layer1(BF16, Hb, inp["W2"], inp["topk_ids"], inp["topk_weights"], rsp, roff,
+                            inp["out_seed"], 0)
+    assert_close(host64(out) - inp["out_seed"], ref - inp["out_seed"], "one-hot combine")
+
+
+def test_full_moe_rank0(oracle):
+    """EP=8 rank 0: 16384 tokens x 4096, 64 experts top-2 (log-Zipf bias), 8
+    local experts, ffn 2816, bf16.  Routing bit-exact; layer 0 on sampled rows;
+    layer 1 on sampled tokens fed by the oracle's own layer 0."""
+    import torch
+    c = wl.MOE_EP8
+    say("full moe EP=8 rank 0")
+    inp = wl.moe_inputs(c["T"], c["hidden"], c["ffn"], c["n_experts"], c["n_local"], c["topk"],
+                        BF16, seed=c["seed"], zipf_s=c["zipf_s"])
+    e0 = c["rank"] * c["n_local"]
+    roff, rsp = oracle.moe_route(inp["topk_ids"], e0, c["n_local"])
+    off, sp, H, out = _moe_run(inp, e0, c["n_local"], BF16)
+    rows = int(roff[-1])
+    assert np.array_equal(off, roff) and np.array_equal(sp[:rows], rsp)
+    rng = np.random.default_rng(7)
+    srows = np.unique(np.concatenate([rng.integers(0, rows, 48), roff[:-1], roff[1:] - 1]))
+    srows = srows[(srows >= 0) & (srows < rows)]
+    Hs = oracle.moe_layer0_rows(BF16, inp["X"], inp["W1"], rsp, roff, 2, srows)
+    idx = torch.from_numpy(srows).to("cuda:0")
+    assert_close(host64(H[idx]), Hs, "full layer0 rows")
+    # End-to-end tokens: every local row of each sampled token comes from the
+    # oracle's layer 0 (rounded to bf16), then the oracle's combine.
+    toks = np.unique(rng.integers(0, c["T"], 24))
+    pos = {int(p): r for r, p in enumerate(rsp)}
+    need = sorted({pos[t * 2 + k] for t in toks for k in range(2) if (t * 2 + k) in pos})
+    Hfull = np.zeros((rows, c["ffn"]), dtype=np.uint16)
+    if need:
+        Hfull[need] = oracle.round_bf16(
+            oracle.moe_layer0_rows(BF16, inp["X"], inp["W1"], rsp, roff, 2, np.array(need)))
+    ref = oracle.moe_layer1_tokens(BF16, Hfull, inp["W2"], inp["topk_ids"], inp["topk_weights"],
+                                   rsp, roff, inp["out_seed"], e0, toks)
+    tidx = torch.from_numpy(toks).to("cuda:0")
+    assert_close(host64(out[tidx]) - inp["out_seed"][toks], ref - inp["out_seed"][toks],
+                 "full combine tokens")

@@ -1,0 +1,127 @@
+"""libfluxmi on the CPU side: the shared library loads, exports every entry
+point include/fluxmi.h declares, and rejects invalid arguments before any
+launch (these calls return during validation, so no GPU is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tile_gemm_communication_amd as fm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "fluxmi.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fm_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = fm.lib()
+    declared = _declared()
+    assert set(declared) == set(fm.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings():
+    assert fm.version() >= 100
+    for code, name in [(0, "FM_OK"), (1, "FM_ERR_INVALID_ARG"), (2, "FM_ERR_UNSUPPORTED"),
+                       (3, "FM_ERR_HIP"), (4, "FM_ERR_TIMEOUT")]:
+        assert fm.status_str(code) == name
+    assert fm.status_str(99) == "FM_ERR_UNKNOWN"
+
+
+# Fake, 16-byte-aligned device addresses: validation rejects the call before
+# any pointer is dereferenced or any kernel is launched.
+P = ctypes.c_void_p(0x10000)
+P2 = ctypes.c_void_p(0x20000)
+P3 = ctypes.c_void_p(0x30000)
+ODD = ctypes.c_void_p(0x10008)
+
+
+@pytest.mark.parametrize("args,want", [
+    ((0, 0, 64, 12, 64, P, P2, P3, None), fm.FM_ERR_INVALID_ARG),      # N % 8
+    ((0, 0, 64, 64, 60, P, P2, P3, None), fm.FM_ERR_INVALID_ARG),      # K % 8
+    ((0, 0, -1, 64, 64, P, P2, P3, None), fm.FM_ERR_INVALID_ARG),      # negative M
+    ((0, 0, 64, 64, 64, None, P2, P3, None), fm.FM_ERR_INVALID_ARG),   # null A
+    ((0, 0, 64, 64, 64, ODD, P2, P3, None), fm.FM_ERR_INVALID_ARG),    # misaligned A
+    ((0, 1, 64, 64, 64, P, P2, P3, None), fm.FM_ERR_UNSUPPORTED),      # f16 in, bf16 out
+    ((2, 2, 64, 64, 64, P, P2, P3, None), fm.FM_ERR_UNSUPPORTED),      # fp32 inputs
+    ((0, 0, 0, 64, 64, P, P2, P3, None), fm.FM_OK),                    # empty M: no-op
+])
+def test_gemm_validation(args, want):
+    assert fm.lib().fm_gemm(*args) == want
+
+
+def test_ag_gemm_validation():
+    L = fm.lib()
+    bad_order = (ctypes.c_int32 * 4)(0, 1, 1, 3)
+    ok_order = (ctypes.c_int32 * 4)(3, 1, 0, 2)
+    # M not divisible by n_chunks
+    assert L.fm_ag_gemm(0, 250, 64, 64, 4, P, P2, P3, P, 1, None, None, 0, None) == \
+        fm.FM_ERR_INVALID_ARG
+    # order is not a permutation
+    assert L.fm_ag_gemm(0, 256, 64, 64, 4, P, P2, P3, P, 1, ctypes.cast(bad_order, ctypes.c_void_p),
+                        None, 0, None) == fm.FM_ERR_INVALID_ARG
+    # null flags
+    assert L.fm_ag_gemm(0, 256, 64, 64, 4, P, P2, P3, None, 1,
+                        ctypes.cast(ok_order, ctypes.c_void_p), None, 0, None) == \
+        fm.FM_ERR_INVALID_ARG
+    # too many chunks
+    assert L.fm_ag_gemm(0, 130, 64, 64, 65, P, P2, P3, P, 1, None, None, 0, None) == \
+        fm.FM_ERR_INVALID_ARG
+    # negative spin limit
+    assert L.fm_ag_gemm(0, 256, 64, 64, 4, P, P2, P3, P, 1, None, None, -5, None) == \
+        fm.FM_ERR_INVALID_ARG
+    # empty problem with valid arguments is a no-op
+    assert L.fm_ag_gemm(0, 0, 64, 64, 4, P, P2, P3, P, 1, ctypes.cast(ok_order, ctypes.c_void_p),
+                        None, 0, None) == fm.FM_OK
+
+
+def test_gemm_rs_validation():
+    L = fm.lib()
+    dst = (ctypes.c_void_p * 4)(0x40000, 0x50000, 0x60000, 0x70000)
+    dst_bad = (ctypes.c_void_p * 4)(0x40000, 0x50004, 0x60000, 0x70000)
+    d = ctypes.cast(dst, ctypes.c_void_p)
+    assert L.fm_gemm_rs(0, 250, 64, 64, 4, 0, P, P2, d, 0, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_gemm_rs(0, 256, 64, 64, 4, 4, P, P2, d, 0, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_gemm_rs(0, 256, 64, 64, 4, 0, P, P2, d, 2, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_gemm_rs(0, 256, 64, 64, 17, 0, P, P2, d, 0, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_gemm_rs(0, 256, 64, 64, 4, 0, P, P2, ctypes.cast(dst_bad, ctypes.c_void_p), 0,
+                        None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_gemm_rs(0, 256, 64, 64, 4, 0, P, P2, None, 0, None) == fm.FM_ERR_INVALID_ARG
+
+
+def test_moe_validation():
+    L = fm.lib()
+    assert L.fm_moe_route(16, 2, 0, 65, P, P2, P3, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_moe_route(16, 0, 0, 8, P, P2, P3, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_moe_route(16, 2, 0, 8, P, P2, None, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_moe_gather_gemm(2, 16, 64, 64, 2, 0, 8, P, P, P, P, P, P, None) == \
+        fm.FM_ERR_UNSUPPORTED
+    assert L.fm_moe_gather_gemm(1, 16, 60, 64, 2, 0, 8, P, P, P, P, P, P, None) == \
+        fm.FM_ERR_INVALID_ARG
+    assert L.fm_moe_gemm_scatter(1, 16, 64, 64, 2, 8, ODD, P, P, P, P, P3, None) == \
+        fm.FM_ERR_INVALID_ARG
+    assert L.fm_moe_gemm_scatter(1, 16, 64, 64, 2, 0, P, P, P, P, P, P3, None) == \
+        fm.FM_ERR_INVALID_ARG
+
+
+def test_chunk_push_validation():
+    L = fm.lib()
+    assert L.fm_chunk_push(P, P2, 100, P3, P3, 1, 0, None) == fm.FM_ERR_INVALID_ARG   # 16 B
+    assert L.fm_chunk_push(P, P, 4096, P3, P3, 1, 0, None) == fm.FM_ERR_INVALID_ARG   # overlap
+    assert L.fm_chunk_push(P, P2, 64, None, P3, 1, 0, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_chunk_push(P, P2, 64, P3, None, 1, 0, None) == fm.FM_ERR_INVALID_ARG
+
+
+def test_oracle_is_not_reachable_from_the_product():
+    pkg = os.path.join(ROOT, "tile_gemm_communication_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                txt = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "import oracle" not in txt and "fm_oracle" not in txt, f

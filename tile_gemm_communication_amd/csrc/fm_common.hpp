@@ -1,0 +1,65 @@
+// fm_common.hpp -- types, vector aliases and small helpers shared by the
+// libfluxmi kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fluxmi.h"
+
+namespace fm {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;   // 4 wave64 per workgroup, one per SIMD
+constexpr int kBK = 64;         // K extent of one LDS stage (128 bytes per row)
+
+__host__ __device__ constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Element traits: the 16-bit input formats and how MFMA consumes them.
+struct F16 {
+  static constexpr fm_dtype_t id = FM_F16;
+  __device__ static inline f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  // Round two fp32 values to nearest-even 16-bit and pack (lo = x, hi = y).
+  __device__ static inline uint32_t pack2(float x, float y) {
+    _Float16 a = (_Float16)x, b = (_Float16)y;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+};
+
+struct BF16 {
+  static constexpr fm_dtype_t id = FM_BF16;
+  __device__ static inline f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline uint32_t pack2(float x, float y) {
+    __bf16 a = (__bf16)x, b = (__bf16)y;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+};
+
+// Output element traits for the plain-store epilogue.
+template <class E> struct Out16 {
+  static constexpr int bytes = 2;
+};
+
+// Device properties cached once per device (compute-unit count).
+int device_cu_count();
+
+// Translate the last HIP launch error into a status.
+inline fm_status_t launch_status() {
+  return hipGetLastError() == hipSuccess ? FM_OK : FM_ERR_HIP;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace fm

@@ -1,0 +1,351 @@
+// fm_gemm.hip -- dense persistent GEMM kernels and their C-ABI entry points:
+// plain GEMM, AllGather-GEMM (chunk-flag waits in the tile prologue) and
+// GEMM-ReduceScatter (fp32 add into per-rank row slices in the epilogue).
+//
+// FLUX review, section 三: "细粒度分解" / "内核融合" / "瓦片映射" -- communication
+// and computation are split into tiles, fused into one kernel, and each
+// dependent compute tile is bound to a thread block (here: a workgroup of a
+// persistent grid).  "AllGather 重叠" and "ReduceScatter 重叠" describe the two
+// fused forms implemented below.
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "fm_sched.hpp"
+#include "fm_tile.hpp"
+
+namespace fm {
+
+enum class Mode : int { Gemm = 0, AG = 1, RS = 2 };
+
+constexpr int kMaxRanks = 16;
+constexpr int kMaxChunks = 64;
+
+struct DenseArgs {
+  const char* A;
+  const char* B;
+  char* C;
+  int64_t M, N, K;
+  // AllGather: chunk flags
+  const uint32_t* flags;
+  int32_t* err_word;
+  int64_t chunk_rows;
+  int64_t spin_limit;
+  uint32_t epoch;
+  // ReduceScatter: destination slices
+  int32_t atomic;
+  int64_t slice_rows;
+  float* dst[kMaxRanks];
+  TileOrder order;
+};
+
+template <class E, int BM, int BN, Mode MODE, bool OUT32>
+__global__ __launch_bounds__(kThreads, 1) void dense_kernel(const DenseArgs args) {
+  using Eng = Engine<E, BM, BN>;
+  __shared__ __attribute__((aligned(16))) char smem[Eng::LDS_BYTES];
+  __shared__ int s_abort;
+
+  Eng eng(smem, args.K);
+  const int64_t M = args.M, N = args.N, K = args.K;
+  const int G = gridDim.x;
+  const int slot = xcd_slot(blockIdx.x, G);
+  const int64_t ncol = 8 * eng.b_colgroup();
+  eng.ldb_bytes = N * 2;
+  uint64_t ready = 0;
+
+  for (int L = slot; L < args.order.total; L += G) {
+    int tm_pos, tn;
+    band_coords(L, args.order.tiles_m, args.order.tiles_n, args.order.group_m, tm_pos, tn);
+    const int tm = args.order.has_morder ? (int)args.order.morder[tm_pos] : tm_pos;
+    const int64_t m0 = (int64_t)tm * BM;
+    const int64_t n0 = (int64_t)tn * BN;
+    const int64_t m_end = min(m0 + BM, M);
+
+    if constexpr (MODE == Mode::AG) {
+      // Tile prologue: wait for every chunk overlapping rows [m0, m_end).
+      if (threadIdx.x == 0) {
+        const bool ok = wait_chunks(args.flags, args.epoch, (int)(m0 / args.chunk_rows),
+                                    (int)((m_end - 1) / args.chunk_rows), ready,
+                                    args.spin_limit, args.err_word);
+        s_abort = ok ? 0 : 1;
+      }
+      __syncthreads();
+      const int abort_now = s_abort;
+      __syncthreads();
+      if (abort_now) return;
+    }
+
+#pragma unroll
+    for (int i = 0; i < Eng::A_LOADS; ++i) {
+      const int64_t row = min(m0 + eng.a_stage_row(i), M - 1);
+      eng.a_row[i] = args.A + row * K * 2;
+    }
+    eng.b_col = args.B + min(n0 + ncol, N - 8) * 2;
+    eng.run();
+
+    if constexpr (MODE == Mode::RS) {
+      // Epilogue: add the fp32 partial into the owning rank's row slice.
+      const int64_t Ms = args.slice_rows;
+      const int s_lo = (int)(m0 / Ms), s_hi = (int)((m_end - 1) / Ms);
+      for (int s = s_lo; s <= s_hi; ++s) {
+        float* base = args.dst[s];
+        const int64_t r0 = (int64_t)s * Ms, r1 = min(r0 + Ms, M);
+#pragma unroll
+        for (int i = 0; i < Eng::FM; ++i) {
+          const int64_t row = m0 + eng.out_row(i);
+          const bool rok = row >= r0 && row < r1;
+          float* prow = base + (row - r0) * N;
+          if (args.atomic) {
+#pragma unroll
+            for (int j = 0; j < Eng::FN; ++j)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int64_t col = n0 + eng.out_col(j, r);
+                if (rok && col < N) {
+                  const f32x4 v = eng.out_vals(i, j, r);
+                  unsafeAtomicAdd(prow + col + 0, v[0]);
+                  unsafeAtomicAdd(prow + col + 1, v[1]);
+                  unsafeAtomicAdd(prow + col + 2, v[2]);
+                  unsafeAtomicAdd(prow + col + 3, v[3]);
+                }
+              }
+          } else {
+            f32x4 old[Eng::FN][4];
+#pragma unroll
+            for (int j = 0; j < Eng::FN; ++j)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int64_t col = n0 + eng.out_col(j, r);
+                if (rok && col < N) old[j][r] = *reinterpret_cast<const f32x4*>(prow + col);
+              }
+#pragma unroll
+            for (int j = 0; j < Eng::FN; ++j)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int64_t col = n0 + eng.out_col(j, r);
+                if (rok && col < N)
+                  *reinterpret_cast<f32x4*>(prow + col) = old[j][r] + eng.out_vals(i, j, r);
+              }
+          }
+        }
+      }
+    } else {
+      // Epilogue: round (16-bit) or keep (fp32) and store runs of 4 columns.
+#pragma unroll
+      for (int i = 0; i < Eng::FM; ++i) {
+        const int64_t row = m0 + eng.out_row(i);
+        if (row >= M) continue;
+#pragma unroll
+        for (int j = 0; j < Eng::FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int64_t col = n0 + eng.out_col(j, r);
+            if (col >= N) continue;
+            const f32x4 v = eng.out_vals(i, j, r);
+            if constexpr (OUT32) {
+              *reinterpret_cast<f32x4*>(args.C + (row * N + col) * 4) = v;
+            } else {
+              const u32x2 p = {E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+              *reinterpret_cast<u32x2*>(args.C + (row * N + col) * 2) = p;
+            }
+          }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+namespace {
+
+struct TileCfg {
+  int bm, bn;
+};
+
+// Tile shape for an M x N output on G CUs: the fewest full-machine waves of
+// work, weighting smaller tiles by their lower MFMA:load ratio.
+TileCfg choose_tile(int64_t M, int64_t N, int G) {
+  if (const char* env = std::getenv("FM_TILE")) {
+    int bm = 0, bn = 0;
+    if (std::sscanf(env, "%dx%d", &bm, &bn) == 2 && (bm == 128 || bm == 256) &&
+        (bn == 128 || bn == 256))
+      return {bm, bn};
+  }
+  // 256x256 is only taken when forced: with register-staged operands its 256
+  // accumulators per lane leave too few VGPRs and it spills.
+  const TileCfg cands[2] = {{256, 128}, {128, 128}};
+  const double eff[2] = {1.0, 0.8};
+  TileCfg best = cands[0];
+  double best_cost = 1e300;
+  for (int c = 0; c < 2; ++c) {
+    const int64_t tiles = cdiv(M, cands[c].bm) * cdiv(N, cands[c].bn);
+    const double waves = (double)cdiv(tiles, G);
+    const double cost = waves * cands[c].bm * cands[c].bn / eff[c];
+    if (cost < best_cost * 0.999) {
+      best_cost = cost;
+      best = cands[c];
+    }
+  }
+  return best;
+}
+
+int group_m_default() {
+  if (const char* env = std::getenv("FM_GROUP_M")) {
+    const int g = std::atoi(env);
+    if (g >= 1 && g <= 64) return g;
+  }
+  return 4;
+}
+
+void fill_order(TileOrder& o, int64_t M, int64_t N, TileCfg cfg) {
+  std::memset(&o, 0, sizeof(o));
+  o.tiles_m = (int)cdiv(M, cfg.bm);
+  o.tiles_n = (int)cdiv(N, cfg.bn);
+  o.total = o.tiles_m * o.tiles_n;
+  o.group_m = std::min(group_m_default(), o.tiles_m);
+  o.has_morder = 0;
+}
+
+// Stable order of M-tiles by a key (arrival position / destination rank).
+void set_morder(TileOrder& o, const std::vector<int>& key) {
+  if (o.tiles_m > kMaxMOrder) return;   // identity order still covers every tile
+  std::vector<int> idx(o.tiles_m);
+  for (int i = 0; i < o.tiles_m; ++i) idx[i] = i;
+  std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return key[a] < key[b]; });
+  for (int i = 0; i < o.tiles_m; ++i) o.morder[i] = (uint16_t)idx[i];
+  o.has_morder = 1;
+}
+
+bool valid_ab(fm_dtype_t dt) { return dt == FM_F16 || dt == FM_BF16; }
+
+template <Mode MODE, bool OUT32>
+fm_status_t launch_dense(fm_dtype_t dt, TileCfg cfg, const DenseArgs& args, hipStream_t stream) {
+  const int G = std::min(args.order.total, device_cu_count());
+  if (G <= 0) return FM_OK;
+  const dim3 grid(G), block(kThreads);
+#define FM_LAUNCH(E, BM, BN) \
+  hipLaunchKernelGGL((dense_kernel<E, BM, BN, MODE, OUT32>), grid, block, 0, stream, args)
+  if (dt == FM_F16) {
+    if (cfg.bm == 256 && cfg.bn == 256) FM_LAUNCH(F16, 256, 256);
+    else if (cfg.bm == 256) FM_LAUNCH(F16, 256, 128);
+    else FM_LAUNCH(F16, 128, 128);
+  } else {
+    if (cfg.bm == 256 && cfg.bn == 256) FM_LAUNCH(BF16, 256, 256);
+    else if (cfg.bm == 256) FM_LAUNCH(BF16, 256, 128);
+    else FM_LAUNCH(BF16, 128, 128);
+  }
+#undef FM_LAUNCH
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace fm
+
+using namespace fm;
+
+extern "C" fm_status_t fm_gemm(fm_dtype_t ab, fm_dtype_t c, int64_t M, int64_t N, int64_t K,
+                               const void* A, const void* B, void* C, hipStream_t stream) {
+  if (!valid_ab(ab) || !(c == ab || c == FM_F32)) return FM_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 0 || N % 8 || K % 8) return FM_ERR_INVALID_ARG;
+  if (!A || !B || !C || !aligned16(A) || !aligned16(B) || !aligned16(C)) return FM_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return FM_OK;
+  if (M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 31)) return FM_ERR_UNSUPPORTED;
+  const TileCfg cfg = choose_tile(M, N, device_cu_count());
+  DenseArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.A = (const char*)A;
+  args.B = (const char*)B;
+  args.C = (char*)C;
+  args.M = M;
+  args.N = N;
+  args.K = K;
+  fill_order(args.order, M, N, cfg);
+  if (c == FM_F32) return launch_dense<Mode::Gemm, true>(ab, cfg, args, stream);
+  return launch_dense<Mode::Gemm, false>(ab, cfg, args, stream);
+}
+
+extern "C" fm_status_t fm_ag_gemm(fm_dtype_t dt, int64_t M, int64_t N, int64_t K,
+                                  int32_t n_chunks, const void* X, const void* W, void* C,
+                                  const uint32_t* flags, uint32_t epoch, const int32_t* order,
+                                  int32_t* err_word, int64_t spin_limit, hipStream_t stream) {
+  if (!valid_ab(dt)) return FM_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 0 || N % 8 || K % 8) return FM_ERR_INVALID_ARG;
+  if (n_chunks < 1 || n_chunks > kMaxChunks || M % n_chunks) return FM_ERR_INVALID_ARG;
+  if (!X || !W || !C || !flags || !aligned16(X) || !aligned16(W) || !aligned16(C))
+    return FM_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(flags) & 3u) || spin_limit < 0) return FM_ERR_INVALID_ARG;
+  std::vector<int> pos(n_chunks, -1);
+  for (int a = 0; a < n_chunks; ++a) {
+    const int c = order ? order[a] : a;
+    if (c < 0 || c >= n_chunks || pos[c] != -1) return FM_ERR_INVALID_ARG;
+    pos[c] = a;
+  }
+  if (M == 0 || N == 0) return FM_OK;
+  if (M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 31)) return FM_ERR_UNSUPPORTED;
+  const TileCfg cfg = choose_tile(M, N, device_cu_count());
+  DenseArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.A = (const char*)X;
+  args.B = (const char*)W;
+  args.C = (char*)C;
+  args.M = M;
+  args.N = N;
+  args.K = K;
+  args.flags = flags;
+  args.epoch = epoch;
+  args.chunk_rows = M / n_chunks;
+  args.err_word = err_word;
+  args.spin_limit = spin_limit ? spin_limit : (1ll << 24);
+  fill_order(args.order, M, N, cfg);
+  // Tiles of the earliest-arriving chunks first (a tile that straddles chunks
+  // is keyed by the last of them to arrive).
+  std::vector<int> key(args.order.tiles_m);
+  for (int tm = 0; tm < args.order.tiles_m; ++tm) {
+    const int64_t r0 = (int64_t)tm * cfg.bm, r1 = std::min<int64_t>(r0 + cfg.bm, M) - 1;
+    int k = 0;
+    for (int64_t c = r0 / args.chunk_rows; c <= r1 / args.chunk_rows; ++c) k = std::max(k, pos[c]);
+    key[tm] = k;
+  }
+  set_morder(args.order, key);
+  return launch_dense<Mode::AG, false>(dt, cfg, args, stream);
+}
+
+extern "C" fm_status_t fm_gemm_rs(fm_dtype_t dt, int64_t M, int64_t N, int64_t K,
+                                  int32_t n_ranks, int32_t rank, const void* A, const void* W,
+                                  float* const* dst, int32_t atomic, hipStream_t stream) {
+  if (!valid_ab(dt)) return FM_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 0 || N % 8 || K % 8) return FM_ERR_INVALID_ARG;
+  if (n_ranks < 1 || n_ranks > kMaxRanks || M % n_ranks || rank < 0 || rank >= n_ranks)
+    return FM_ERR_INVALID_ARG;
+  if (!A || !W || !dst || !aligned16(A) || !aligned16(W) || (atomic != 0 && atomic != 1))
+    return FM_ERR_INVALID_ARG;
+  for (int r = 0; r < n_ranks; ++r)
+    if (!dst[r] || !aligned16(dst[r])) return FM_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return FM_OK;
+  if (M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 31)) return FM_ERR_UNSUPPORTED;
+  const TileCfg cfg = choose_tile(M, N, device_cu_count());
+  DenseArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.A = (const char*)A;
+  args.B = (const char*)W;
+  args.M = M;
+  args.N = N;
+  args.K = K;
+  args.atomic = atomic;
+  args.slice_rows = M / n_ranks;
+  for (int r = 0; r < n_ranks; ++r) args.dst[r] = dst[r];
+  fill_order(args.order, M, N, cfg);
+  // Destination-rank order starting at rank+1, so that on a real TP group the
+  // ranks start on different slices (slice of a tile = slice of its first row).
+  std::vector<int> key(args.order.tiles_m);
+  for (int tm = 0; tm < args.order.tiles_m; ++tm) {
+    const int s = (int)(((int64_t)tm * cfg.bm) / args.slice_rows);
+    key[tm] = ((s - (rank + 1)) % n_ranks + n_ranks) % n_ranks;
+  }
+  set_morder(args.order, key);
+  return launch_dense<Mode::RS, false>(dt, cfg, args, stream);
+}

@@ -1,0 +1,65 @@
+// fm_push.hip -- producer side of the chunk-arrival protocol.
+//
+// A chunk is copied with coalesced 16-byte loads/stores by a small grid; every
+// workgroup makes its stores visible at device scope and checks in on a
+// counter; the last one to check in resets the counter and publishes the
+// chunk's flag with a release store.  This is the signalled one-sided put of
+// the FlagCX guide ("flagcxPutSignal": write the data, then bump the remote
+// signal) and the push mode of the FLUX review ("拉取 vs 推送数据传输"), with
+// the peer's buffer being local HBM on one GPU.
+#include "fm_common.hpp"
+
+namespace fm {
+
+__global__ __launch_bounds__(256) void push_kernel(const u32x4* __restrict__ src,
+                                                   u32x4* __restrict__ dst, int64_t n16,
+                                                   uint32_t* flag, uint32_t* counter,
+                                                   uint32_t epoch) {
+  const int64_t per = cdiv(n16, (int64_t)gridDim.x);
+  const int64_t begin = (int64_t)blockIdx.x * per;
+  const int64_t end = min(begin + per, n16);
+  int64_t i = begin + threadIdx.x;
+  for (; i + 3 * 256 < end; i += 4 * 256) {
+    const u32x4 a = src[i], b = src[i + 256], c = src[i + 512], d = src[i + 768];
+    dst[i] = a;
+    dst[i + 256] = b;
+    dst[i + 512] = c;
+    dst[i + 768] = d;
+  }
+  for (; i < end; i += 256) dst[i] = src[i];
+  __threadfence();   // this thread's stores are visible device-wide
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == gridDim.x - 1) {
+      __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(flag, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+}  // namespace fm
+
+using namespace fm;
+
+extern "C" fm_status_t fm_chunk_push(const void* src, void* dst, int64_t bytes, uint32_t* flag,
+                                     uint32_t* counter, uint32_t epoch, int32_t n_workgroups,
+                                     hipStream_t stream) {
+  if (!flag || !counter || bytes < 0 || bytes % 16 || n_workgroups < 0) return FM_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(flag) & 3u) || (reinterpret_cast<uintptr_t>(counter) & 3u))
+    return FM_ERR_INVALID_ARG;
+  if (bytes > 0 && (!src || !dst || !aligned16(src) || !aligned16(dst))) return FM_ERR_INVALID_ARG;
+  if (bytes > 0) {
+    const char* s = (const char*)src;
+    const char* d = (const char*)dst;
+    if (s < d + bytes && d < s + bytes) return FM_ERR_INVALID_ARG;   // overlap
+  }
+  const int64_t n16 = bytes / 16;
+  int wg = n_workgroups > 0 ? n_workgroups : 64;
+  if (n16 == 0) wg = 1;
+  else if (wg > cdiv(n16, 256)) wg = (int)cdiv(n16, 256);
+  hipLaunchKernelGGL(push_kernel, dim3(wg), dim3(256), 0, stream, (const u32x4*)src, (u32x4*)dst,
+                     n16, flag, counter, epoch);
+  return launch_status();
+}
