@@ -21,6 +21,9 @@ namespace fm {
 enum class Mode : int { Gemm = 0, AG = 1, RS = 2 };
 
 constexpr int kMaxRanks = 16;
+// In-tile byte offsets are 32-bit (tile rows x row pitch), which bounds each
+// dimension to 2^22 elements.
+constexpr int64_t kMaxDim = 1ll << 22;
 constexpr int kMaxChunks = 64;
 
 struct DenseArgs {
@@ -41,9 +44,20 @@ struct DenseArgs {
   TileOrder order;
 };
 
-template <class E, int BM, int BN, Mode MODE, bool OUT32>
+// Store a run of 4 consecutive outputs at element index idx of C.
+template <class E, bool OUT32>
+__device__ __forceinline__ void store_run(char* C, int64_t idx, const f32x4& v) {
+  if constexpr (OUT32) {
+    *reinterpret_cast<f32x4*>(C + idx * 4) = v;
+  } else {
+    const u32x2 p = {E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+    *reinterpret_cast<u32x2*>(C + idx * 2) = p;
+  }
+}
+
+template <class E, int BM, int BN, Mode MODE, bool OUT32, bool KTAIL>
 __global__ __launch_bounds__(kThreads, 1) void dense_kernel(const DenseArgs args) {
-  using Eng = Engine<E, BM, BN>;
+  using Eng = Engine<E, BM, BN, KTAIL>;
   __shared__ __attribute__((aligned(16))) char smem[Eng::LDS_BYTES];
   __shared__ int s_abort;
 
@@ -51,8 +65,6 @@ __global__ __launch_bounds__(kThreads, 1) void dense_kernel(const DenseArgs args
   const int64_t M = args.M, N = args.N, K = args.K;
   const int G = gridDim.x;
   const int slot = xcd_slot(blockIdx.x, G);
-  const int64_t ncol = 8 * eng.b_colgroup();
-  eng.ldb_bytes = N * 2;
   uint64_t ready = 0;
 
   for (int L = slot; L < args.order.total; L += G) {
@@ -77,80 +89,102 @@ __global__ __launch_bounds__(kThreads, 1) void dense_kernel(const DenseArgs args
       if (abort_now) return;
     }
 
+    eng.set_a_base(args.A + m0 * K * 2);
 #pragma unroll
-    for (int i = 0; i < Eng::A_LOADS; ++i) {
-      const int64_t row = min(m0 + eng.a_stage_row(i), M - 1);
-      eng.a_row[i] = args.A + row * K * 2;
+    for (int i = 0; i < Eng::A_DMA; ++i) {
+      const int64_t row = min(m0 + eng.a_dma_row(i), M - 1);
+      eng.set_a(i, (uint32_t)((row - m0) * K * 2));
     }
-    eng.b_col = args.B + min(n0 + ncol, N - 8) * 2;
+    eng.set_b(args.B, N * 2, n0, N);
     eng.run();
 
+    const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
     if constexpr (MODE == Mode::RS) {
       // Epilogue: add the fp32 partial into the owning rank's row slice.
       const int64_t Ms = args.slice_rows;
       const int s_lo = (int)(m0 / Ms), s_hi = (int)((m_end - 1) / Ms);
-      for (int s = s_lo; s <= s_hi; ++s) {
-        float* base = args.dst[s];
-        const int64_t r0 = (int64_t)s * Ms, r1 = min(r0 + Ms, M);
+      if (interior && s_lo == s_hi && !args.atomic) {
+        float* base = args.dst[s_lo] + (m0 - (int64_t)s_lo * Ms) * N + n0;
+        const uint32_t lane_off = (uint32_t)(eng.out_row(0) * N + eng.out_col(0, 0));
 #pragma unroll
-        for (int i = 0; i < Eng::FM; ++i) {
-          const int64_t row = m0 + eng.out_row(i);
-          const bool rok = row >= r0 && row < r1;
-          float* prow = base + (row - r0) * N;
-          if (args.atomic) {
+        for (int i = 0; i < Eng::FM; ++i)
 #pragma unroll
-            for (int j = 0; j < Eng::FN; ++j)
+          for (int j = 0; j < Eng::FN; ++j) {
+            // one 32x32 block at a time: 4 loads in flight, then 4 stores
+            eng.pin(i, j);
+            float* p = base + (uint32_t)(i * 32 * N) + lane_off + j * 32;
+            f32x4 old[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) old[r] = *reinterpret_cast<const f32x4*>(p + 8 * r);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              *reinterpret_cast<f32x4*>(p + 8 * r) = old[r] + eng.out_vals(i, j, r);
+          }
+      } else {
+        for (int s = s_lo; s <= s_hi; ++s) {
+          float* base = args.dst[s];
+          const int64_t r0 = (int64_t)s * Ms, r1 = min(r0 + Ms, M);
+#pragma unroll
+          for (int i = 0; i < Eng::FM; ++i) {
+            const int64_t row = m0 + eng.out_row(i);
+            const bool rok = row >= r0 && row < r1;
+            float* prow = base + (row - r0) * N;
+#pragma unroll
+            for (int j = 0; j < Eng::FN; ++j) {
+              eng.pin(i, j);
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const int64_t col = n0 + eng.out_col(j, r);
-                if (rok && col < N) {
-                  const f32x4 v = eng.out_vals(i, j, r);
+                if (!rok || col >= N) continue;
+                const f32x4 v = eng.out_vals(i, j, r);
+                if (args.atomic) {
                   unsafeAtomicAdd(prow + col + 0, v[0]);
                   unsafeAtomicAdd(prow + col + 1, v[1]);
                   unsafeAtomicAdd(prow + col + 2, v[2]);
                   unsafeAtomicAdd(prow + col + 3, v[3]);
+                } else {
+                  f32x4* q = reinterpret_cast<f32x4*>(prow + col);
+                  *q = *q + v;
                 }
               }
-          } else {
-            f32x4 old[Eng::FN][4];
-#pragma unroll
-            for (int j = 0; j < Eng::FN; ++j)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int64_t col = n0 + eng.out_col(j, r);
-                if (rok && col < N) old[j][r] = *reinterpret_cast<const f32x4*>(prow + col);
-              }
-#pragma unroll
-            for (int j = 0; j < Eng::FN; ++j)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int64_t col = n0 + eng.out_col(j, r);
-                if (rok && col < N)
-                  *reinterpret_cast<f32x4*>(prow + col) = old[j][r] + eng.out_vals(i, j, r);
-              }
+            }
           }
         }
       }
     } else {
       // Epilogue: round (16-bit) or keep (fp32) and store runs of 4 columns.
+      if (interior) {
+        // tile base (uniform) + 32-bit lane offset + per-block constants
+        constexpr int EB = OUT32 ? 4 : 2;
+        char* base = args.C + (m0 * N + n0) * EB;
+        const uint32_t lane_off = (uint32_t)(eng.out_row(0) * N + eng.out_col(0, 0)) * EB;
 #pragma unroll
-      for (int i = 0; i < Eng::FM; ++i) {
-        const int64_t row = m0 + eng.out_row(i);
-        if (row >= M) continue;
+        for (int i = 0; i < Eng::FM; ++i) {
+          char* row_base = base + (uint32_t)(i * 32 * N * EB) + lane_off;
 #pragma unroll
-        for (int j = 0; j < Eng::FN; ++j)
+          for (int j = 0; j < Eng::FN; ++j) {
+            eng.pin(i, j);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int64_t col = n0 + eng.out_col(j, r);
-            if (col >= N) continue;
-            const f32x4 v = eng.out_vals(i, j, r);
-            if constexpr (OUT32) {
-              *reinterpret_cast<f32x4*>(args.C + (row * N + col) * 4) = v;
-            } else {
-              const u32x2 p = {E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
-              *reinterpret_cast<u32x2*>(args.C + (row * N + col) * 2) = p;
+            for (int r = 0; r < 4; ++r)
+              store_run<E, OUT32>(row_base, j * 32 + 8 * r, eng.out_vals(i, j, r));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < Eng::FM; ++i) {
+          const int64_t row = m0 + eng.out_row(i);
+          if (row >= M) continue;
+#pragma unroll
+          for (int j = 0; j < Eng::FN; ++j) {
+            eng.pin(i, j);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int64_t col = n0 + eng.out_col(j, r);
+              if (col >= N) continue;
+              store_run<E, OUT32>(args.C, row * N + col, eng.out_vals(i, j, r));
             }
           }
+        }
       }
     }
   }
@@ -175,13 +209,11 @@ TileCfg choose_tile(int64_t M, int64_t N, int G) {
         (bn == 128 || bn == 256))
       return {bm, bn};
   }
-  // 256x256 is only taken when forced: with register-staged operands its 256
-  // accumulators per lane leave too few VGPRs and it spills.
-  const TileCfg cands[2] = {{256, 128}, {128, 128}};
-  const double eff[2] = {1.0, 0.8};
+  const TileCfg cands[3] = {{256, 256}, {256, 128}, {128, 128}};
+  const double eff[3] = {1.0, 0.85, 0.7};
   TileCfg best = cands[0];
   double best_cost = 1e300;
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < 3; ++c) {
     const int64_t tiles = cdiv(M, cands[c].bm) * cdiv(N, cands[c].bn);
     const double waves = (double)cdiv(tiles, G);
     const double cost = waves * cands[c].bm * cands[c].bn / eff[c];
@@ -198,7 +230,7 @@ int group_m_default() {
     const int g = std::atoi(env);
     if (g >= 1 && g <= 64) return g;
   }
-  return 4;
+  return 8;   // 8 M-tiles per band: the 32 tiles in flight per XCD form an 8 x 4 block
 }
 
 void fill_order(TileOrder& o, int64_t M, int64_t N, TileCfg cfg) {
@@ -227,8 +259,15 @@ fm_status_t launch_dense(fm_dtype_t dt, TileCfg cfg, const DenseArgs& args, hipS
   const int G = std::min(args.order.total, device_cu_count());
   if (G <= 0) return FM_OK;
   const dim3 grid(G), block(kThreads);
-#define FM_LAUNCH(E, BM, BN) \
-  hipLaunchKernelGGL((dense_kernel<E, BM, BN, MODE, OUT32>), grid, block, 0, stream, args)
+#define FM_LAUNCH(E, BM, BN)                                                                   \
+  do {                                                                                         \
+    if (args.K % kBK)                                                                          \
+      hipLaunchKernelGGL((dense_kernel<E, BM, BN, MODE, OUT32, true>), grid, block, 0, stream, \
+                         args);                                                                \
+    else                                                                                       \
+      hipLaunchKernelGGL((dense_kernel<E, BM, BN, MODE, OUT32, false>), grid, block, 0,        \
+                         stream, args);                                                        \
+  } while (0)
   if (dt == FM_F16) {
     if (cfg.bm == 256 && cfg.bn == 256) FM_LAUNCH(F16, 256, 256);
     else if (cfg.bm == 256) FM_LAUNCH(F16, 256, 128);
@@ -253,7 +292,7 @@ extern "C" fm_status_t fm_gemm(fm_dtype_t ab, fm_dtype_t c, int64_t M, int64_t N
   if (M < 0 || N < 0 || K < 0 || N % 8 || K % 8) return FM_ERR_INVALID_ARG;
   if (!A || !B || !C || !aligned16(A) || !aligned16(B) || !aligned16(C)) return FM_ERR_INVALID_ARG;
   if (M == 0 || N == 0) return FM_OK;
-  if (M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 31)) return FM_ERR_UNSUPPORTED;
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FM_ERR_UNSUPPORTED;
   const TileCfg cfg = choose_tile(M, N, device_cu_count());
   DenseArgs args;
   std::memset(&args, 0, sizeof(args));
@@ -285,7 +324,7 @@ extern "C" fm_status_t fm_ag_gemm(fm_dtype_t dt, int64_t M, int64_t N, int64_t K
     pos[c] = a;
   }
   if (M == 0 || N == 0) return FM_OK;
-  if (M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 31)) return FM_ERR_UNSUPPORTED;
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FM_ERR_UNSUPPORTED;
   const TileCfg cfg = choose_tile(M, N, device_cu_count());
   DenseArgs args;
   std::memset(&args, 0, sizeof(args));
@@ -326,7 +365,7 @@ extern "C" fm_status_t fm_gemm_rs(fm_dtype_t dt, int64_t M, int64_t N, int64_t K
   for (int r = 0; r < n_ranks; ++r)
     if (!dst[r] || !aligned16(dst[r])) return FM_ERR_INVALID_ARG;
   if (M == 0 || N == 0) return FM_OK;
-  if (M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 31)) return FM_ERR_UNSUPPORTED;
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FM_ERR_UNSUPPORTED;
   const TileCfg cfg = choose_tile(M, N, device_cu_count());
   DenseArgs args;
   std::memset(&args, 0, sizeof(args));

@@ -117,9 +117,9 @@ struct MoeArgs {
   int topk, n_local, tiles_n, group_m;
 };
 
-template <class E, int BM, int BN, bool SCATTER>
+template <class E, int BM, int BN, bool SCATTER, bool KTAIL>
 __global__ __launch_bounds__(kThreads, 1) void moe_kernel(const MoeArgs a) {
-  using Eng = Engine<E, BM, BN>;
+  using Eng = Engine<E, BM, BN, KTAIL>;
   __shared__ __attribute__((aligned(16))) char smem[Eng::LDS_BYTES];
   __shared__ int s_off[kMaxLocalExperts + 1];
   __shared__ int s_tile0[kMaxLocalExperts + 1];
@@ -142,8 +142,6 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(const MoeArgs a) {
   const int total = s_tile0[a.n_local];
   const int G = gridDim.x;
   const int slot = xcd_slot(blockIdx.x, G);
-  const int64_t ncol = 8 * eng.b_colgroup();
-  eng.ldb_bytes = N * 2;
 
   for (int L = slot; L < total; L += G) {
     int e = 0;
@@ -156,44 +154,73 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(const MoeArgs a) {
     const int m0 = tm * BM;
     const int64_t n0 = (int64_t)tn * BN;
 
+    eng.set_a_base(a.A);
 #pragma unroll
-    for (int i = 0; i < Eng::A_LOADS; ++i) {
-      const int lr = min(m0 + eng.a_stage_row(i), rows_e - 1);
+    for (int i = 0; i < Eng::A_DMA; ++i) {
+      const int lr = min(m0 + eng.a_dma_row(i), rows_e - 1);
       int64_t src_row;
       if constexpr (SCATTER) {
         src_row = row_base + lr;                              // H rows are expert-sorted
       } else {
         src_row = a.sorted_pairs[row_base + lr] / a.topk;     // gather: token of the pair
       }
-      eng.a_row[i] = a.A + src_row * K * 2;
+      eng.set_a(i, (uint32_t)(src_row * K * 2));
     }
-    eng.b_col = a.W + ((int64_t)e * K * N + min(n0 + ncol, N - 8)) * 2;
+    eng.set_b(a.W + (int64_t)e * K * N * 2, N * 2, n0, N);
     eng.run();
 
+    const bool interior = (m0 + BM <= rows_e) && (n0 + BN <= N);
+    if constexpr (SCATTER) {
+      // out[token] += weight * row, as fp32 atomics (a token may receive up to
+      // topk local contributions, in any order).
 #pragma unroll
-    for (int i = 0; i < Eng::FM; ++i) {
-      const int lr = m0 + eng.out_row(i);
-      if (lr >= rows_e) continue;
-      if constexpr (SCATTER) {
+      for (int i = 0; i < Eng::FM; ++i) {
+        const int lr = m0 + eng.out_row(i);
+        if (lr >= rows_e) continue;
         const int p = a.sorted_pairs[row_base + lr];
         const float w = a.weights[p];
-        float* orow = reinterpret_cast<float*>(a.out) + (int64_t)(p / a.topk) * N;
+        float* orow = reinterpret_cast<float*>(a.out) + (int64_t)(p / a.topk) * N + n0;
 #pragma unroll
-        for (int j = 0; j < Eng::FN; ++j)
+        for (int j = 0; j < Eng::FN; ++j) {
+          eng.pin(i, j);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int64_t col = n0 + eng.out_col(j, r);
-            if (col >= N) continue;
+            const int c = eng.out_col(j, r);
+            if (!interior && n0 + c >= N) continue;
             const f32x4 v = eng.out_vals(i, j, r);
-            unsafeAtomicAdd(orow + col + 0, w * v[0]);
-            unsafeAtomicAdd(orow + col + 1, w * v[1]);
-            unsafeAtomicAdd(orow + col + 2, w * v[2]);
-            unsafeAtomicAdd(orow + col + 3, w * v[3]);
+            unsafeAtomicAdd(orow + c + 0, w * v[0]);
+            unsafeAtomicAdd(orow + c + 1, w * v[1]);
+            unsafeAtomicAdd(orow + c + 2, w * v[2]);
+            unsafeAtomicAdd(orow + c + 3, w * v[3]);
           }
-      } else {
+        }
+      }
+    } else if (interior) {
+      char* base = a.out + ((int64_t)(row_base + m0) * N + n0) * 2;
+      const uint32_t lane_off = (uint32_t)(eng.out_row(0) * N + eng.out_col(0, 0)) * 2;
+#pragma unroll
+      for (int i = 0; i < Eng::FM; ++i) {
+        char* rb = base + (uint32_t)(i * 32 * N * 2) + lane_off;
+#pragma unroll
+        for (int j = 0; j < Eng::FN; ++j) {
+          eng.pin(i, j);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const f32x4 v = eng.out_vals(i, j, r);
+            const u32x2 pk = {E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+            *reinterpret_cast<u32x2*>(rb + (j * 32 + 8 * r) * 2) = pk;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < Eng::FM; ++i) {
+        const int lr = m0 + eng.out_row(i);
+        if (lr >= rows_e) continue;
         char* hrow = a.out + (int64_t)(row_base + lr) * N * 2;
 #pragma unroll
-        for (int j = 0; j < Eng::FN; ++j)
+        for (int j = 0; j < Eng::FN; ++j) {
+          eng.pin(i, j);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int64_t col = n0 + eng.out_col(j, r);
@@ -202,6 +229,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(const MoeArgs a) {
             const u32x2 pk = {E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
             *reinterpret_cast<u32x2*>(hrow + col * 2) = pk;
           }
+        }
       }
     }
   }
@@ -220,16 +248,21 @@ MoeTile moe_tile() {
         (bn == 128 || bn == 256))
       return {bm, bn};
   }
-  return {256, 128};
+  return {256, 256};
 }
 
 template <bool SCATTER>
 fm_status_t launch_moe(fm_dtype_t dt, MoeTile cfg, MoeArgs& a, hipStream_t stream) {
   a.tiles_n = (int)cdiv(a.N, cfg.bn);
-  a.group_m = 4;
+  a.group_m = 8;
   const dim3 grid(device_cu_count()), block(kThreads);
-#define FM_LAUNCH(E, BM, BN) \
-  hipLaunchKernelGGL((moe_kernel<E, BM, BN, SCATTER>), grid, block, 0, stream, a)
+#define FM_LAUNCH(E, BM, BN)                                                                  \
+  do {                                                                                        \
+    if (a.K % kBK)                                                                            \
+      hipLaunchKernelGGL((moe_kernel<E, BM, BN, SCATTER, true>), grid, block, 0, stream, a);  \
+    else                                                                                      \
+      hipLaunchKernelGGL((moe_kernel<E, BM, BN, SCATTER, false>), grid, block, 0, stream, a); \
+  } while (0)
   if (dt == FM_F16) {
     if (cfg.bm == 256 && cfg.bn == 256) FM_LAUNCH(F16, 256, 256);
     else if (cfg.bm == 256) FM_LAUNCH(F16, 256, 128);
@@ -281,7 +314,9 @@ extern "C" fm_status_t fm_moe_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidd
   if (T > 0 && ffn > 0 &&
       (!X || !W1 || !H || !aligned16(X) || !aligned16(W1) || !aligned16(H)))
     return FM_ERR_INVALID_ARG;
-  if (hidden >= (1ll << 31) || ffn >= (1ll << 31)) return FM_ERR_UNSUPPORTED;
+  // gathered-row byte offsets are 32-bit
+  if (hidden >= (1ll << 22) || ffn >= (1ll << 22) || T * hidden >= (1ll << 31))
+    return FM_ERR_UNSUPPORTED;
   st = fm_moe_route(T, topk, expert_begin, n_local, topk_ids, sorted_pairs, expert_offsets,
                     stream);
   if (st != FM_OK || T == 0 || ffn == 0) return st;
@@ -314,7 +349,7 @@ extern "C" fm_status_t fm_moe_gemm_scatter(fm_dtype_t dt, int64_t T, int64_t hid
   if (!H || !W2 || !sorted_pairs || !topk_weights || !out || !aligned16(H) || !aligned16(W2) ||
       !aligned16(out))
     return FM_ERR_INVALID_ARG;
-  if (hidden >= (1ll << 31) || ffn >= (1ll << 31) || T * topk >= (1ll << 31))
+  if (hidden >= (1ll << 22) || ffn >= (1ll << 22) || T * topk * ffn >= (1ll << 31))
     return FM_ERR_UNSUPPORTED;
   MoeArgs a;
   std::memset(&a, 0, sizeof(a));

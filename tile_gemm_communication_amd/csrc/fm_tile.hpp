@@ -2,84 +2,187 @@
 // kernel in libfluxmi (dense, AllGather, ReduceScatter, grouped MoE).
 //
 // One workgroup = 4 wave64 (one per SIMD) arranged 2x2 over a BM x BN output
-// tile; each wave owns a (BM/2) x (BN/2) sub-tile made of 32x32 blocks
-// computed with v_mfma_f32_32x32x16_{f16,bf16} into fp32 accumulators.
+// tile; each wave owns a (BM/2) x (BN/2) sub-tile of 32x32 blocks computed
+// with v_mfma_f32_32x32x16_{f16,bf16} into fp32 accumulators (AGPRs).
 //
-// Data path per K step of 64:
-//   HBM/L2 --128-bit loads--> VGPRs --ds_write--> LDS (two stages) --ds_read_b128--> MFMA
-// A tiles ([M,K] row-major) are stored in LDS as rows of 64 K-elements.  B
-// tiles ([K,N] row-major) are transposed while staging (an 8x8 / 4x8 block
-// transpose of 16-bit elements in registers) so that LDS holds B^T rows of 64
-// K-elements too; both MFMA operands are then single 16-byte LDS reads.
-// Each 128-byte LDS row is split into eight 16-byte chunks placed at
-// chunk ^ ((row ^ row>>3) & 7), which keeps both the staging writes and the
-// fragment reads free of bank conflicts.
+// Data path, one LDS stage = one K step of 64, two stages in flight:
+//   HBM/L2 --global_load_lds_dwordx4 (direct to LDS, no VGPR staging)--> LDS
+//   LDS --ds_read_b128 (A) / 2 x ds_read_b64_tr_b16 (B)--> VGPR fragments --> MFMA
+// LDS layout: [A stage 0 | A stage 1 | B stage 0 | B stage 1].  An A stage is
+// BM rows x 64 K-elements (128 B per row); a B stage is 64 K-rows x BN
+// N-elements, row-major like B itself.  The transposing LDS read hands each
+// lane the K-run of one B column that the MFMA operand needs, so B is never
+// transposed in registers.
 //
-// The MFMA is issued with B^T as the first operand and A as the second, so
-// the 32x32 result block is C^T in the instruction's layout: lane l holds row
-// m = l % 32 of C and, for item 4r+q, column n = 8r + 4(l/32) + q.  Every lane
-// therefore owns runs of 4 consecutive output columns, which the epilogues
-// store (or read-add-write) as 8- or 16-byte vectors.
+// Bank-conflict-free placement: rows are cut into 16-byte chunks; chunk c of
+// A row m is stored at c ^ ((m ^ m>>3) & 7) and chunk c of B row k at
+// c ^ BSWZ*(k & 3).  A direct-to-LDS load writes its 64 lanes' 16 bytes
+// contiguously, so the placement is realised by choosing which global chunk
+// each lane fetches.
+//
+// The loads are issued with inline assembly: the compiler then sees no LDS
+// DMA and does not order every later LDS read behind it; the ordering the
+// pipeline needs is explicit (s_waitcnt + barrier below).
+//
+// Pipeline per K step kt (buffer cur = kt & 1), fragments double-buffered:
+//   sub-steps 0..2: 16 MFMAs each, interleaved with the LDS reads of the next
+//                   sub-step's fragments;
+//   sub-step 3:     half the MFMAs; wait for this wave's DMA and reads;
+//                   barrier (stage kt+1 is complete and stage kt drained);
+//                   issue the DMA of stage kt+2 into buffer cur; read
+//                   sub-step 0 of stage kt+1 interleaved with the other half.
+//
+// The MFMA takes B^T as its first operand and A as its second, so a 32x32
+// result block is C^T in the instruction's layout: lane l holds row
+// m = l % 32 of C and, for item 4r+q, column n = 8r + 4(l/32) + q; every lane
+// owns runs of 4 consecutive output columns.
 #pragma once
 
 #include "fm_common.hpp"
 
 namespace fm {
 
-__device__ __forceinline__ int lds_swz(int row) { return (row ^ (row >> 3)) & 7; }
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * 128 + ((chunk ^ lds_swz(row)) << 4);
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define FM_LDS4(p) ((__attribute__((address_space(3))) s16x4*)(p))
+
+__device__ __forceinline__ int swz_a(int row) { return (row ^ (row >> 3)) & 7; }
+
+// s_waitcnt encodings (gfx9: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x0F70 | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_all0() { __builtin_amdgcn_s_waitcnt(0x0070); }
+
+// One 16-byte-per-lane direct-to-LDS load: lane i's 16 bytes from
+// sbase + voff_i land at LDS byte lds + 16 i.  sbase and lds are wave-uniform.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Scheduling hint: alternate MFMAs and LDS reads (one each, READS times),
+// then the remaining MFMAs.
+template <int MFMAS, int READS>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int q = 0; q < READS; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  if constexpr (MFMAS > READS) __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - READS, 0);
 }
 
-// Pack 16-bit element `c` (0..7) of two 8-element rows into one dword
-// (lo = row x, hi = row y).
-template <int c>
-__device__ __forceinline__ uint32_t pick2(const u32x4& x, const u32x4& y) {
-  constexpr uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-  return __builtin_amdgcn_perm(y[c >> 1], x[c >> 1], sel);
-}
-
-template <class E, int BM, int BN>
+template <class E, int BM, int BN, bool KTAIL, int BSWZ = 2>
 struct Engine {
   static constexpr int WM = BM / 2, WN = BN / 2;
-  static constexpr int FM = WM / 32, FN = WN / 32;
-  static constexpr int A_LOADS = BM / 32;   // 16-byte A chunks per thread per stage
-  static constexpr int B_ROWS = BN / 32;    // B rows (of 8 columns) per thread per stage
-  static constexpr int B_NG = BN / 8;       // 8-column groups across the tile
-  static constexpr int A_BYTES = BM * 128;
-  static constexpr int B_BYTES = BN * 128;
-  static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = 2 * STAGE;
+  static constexpr int FM = WM / 32, FN = WN / 32;     // 32x32 blocks per wave
+  static constexpr int A_STAGE = BM * 128;
+  static constexpr int B_ROW = BN * 2;
+  static constexpr int B_STAGE = 64 * B_ROW;
+  static constexpr int LDS_B = 2 * A_STAGE;             // B stages follow both A stages
+  static constexpr int LDS_BYTES = 2 * (A_STAGE + B_STAGE);
+  static constexpr int A_DMA = BM / 32;                 // DMA instructions per wave per stage
+  static constexpr int B_CPR = BN / 8;                  // 16-byte chunks per B row
+  static constexpr int B_RPI = 64 / B_CPR;              // B rows per 1 KB DMA instruction
+  static constexpr int B_DMA = BN / 32;
+  static constexpr int DMA = A_DMA + B_DMA;
+  static constexpr int READS = FM + 2 * FN;             // LDS reads per sub-step
+  static constexpr int MFMAS = FM * FN;                 // MFMAs per sub-step
   static_assert(BM == 128 || BM == 256, "BM must be 128 or 256");
-  static_assert(B_ROWS == 8 || B_ROWS == 4, "BN must be 128 or 256");
+  static_assert(BN == 128 || BN == 256, "BN must be 128 or 256");
+  static_assert(BSWZ == 2 || BSWZ == 4, "B swizzle step");
+  static_assert((WN / 8) % (4 * ((BSWZ == 2) ? 2 : 4)) == 0,
+                "the B swizzle must not reach the wave's column offset");
 
   char* smem;
-  int t, lane, wm, wn;
+  uint32_t lds0;   // LDS byte address of smem (wave-uniform)
+  int lane, w, wm, wn;
   int64_t K;
+  int KT;
 
   f32x16 acc[FM][FN];
-  u32x4 ra[A_LOADS];
-  u32x4 rb[B_ROWS];
+  u32x4 fa[2][FM];
+  u32x4 fb[2][FN];
 
-  // Per-tile operand sources (set by the kernel before run()).
-  const char* a_row[A_LOADS];   // start of the A row feeding staging slot i
-  const char* b_col;            // B + (this thread's 8-column group) elements
-  int64_t ldb_bytes;            // B row pitch in bytes
+  // DMA sources: wave-uniform bases (K offset 0) plus per-lane 32-bit offsets.
+  const char* a_base;
+  const char* b_base;
+  uint32_t a_off[A_DMA];
+  uint32_t b_off[B_DMA];
+  int64_t b_step;             // bytes of 64 B rows (one K step)
+
+  // LDS read offsets (bytes from smem): A by (sub-step, block parity), B by
+  // block-column variant; everything else is an immediate.
+  static constexpr int BV = (BSWZ == 2) ? 2 : 4;   // B address variants
+  uint32_t ra_off[4][2];
+  uint32_t rb_off[BV];
 
   __device__ __forceinline__ Engine(char* s, int64_t K_) : smem(s), K(K_) {
-    t = threadIdx.x;
+    const int t = threadIdx.x;
     lane = t & 63;
-    int w = t >> 6;
+    w = __builtin_amdgcn_readfirstlane(t >> 6);
     wm = w >> 1;
     wn = w & 1;
+    lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)s);
+    KT = (int)cdiv(K, kBK);
+    // A fragment of block i, sub-step ks: row m = wm*WM + 32i + r32, chunk
+    // 2ks + hi; swz_a(m) = s0 ^ 4(i&1) with s0 = (r32 ^ r32>>3) & 7.
+    const int r32 = lane & 31, hi = lane >> 5;
+    const int s0 = (r32 ^ (r32 >> 3)) & 7;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        ra_off[ks][p] = (wm * WM + r32) * 128 + (((2 * ks + hi) ^ s0 ^ (4 * p)) << 4);
+    // B fragment of block j: 16-lane group g = lane/16 covers columns
+    // 16(g&1)..+15 and K rows 8(g>>1)..+7; lane j16 of the group addresses
+    // K row +(j16>>2) and columns +4(j16&3).  Its chunk index is
+    // X + 4*BV*(j/BV) with X = wn*WN/8 + 4(j%BV) + 2(g&1) + ((j16&3)>>1), and
+    // the swizzle xors it with z = BSWZ*(row&3) < 4*BV, so the j/BV part is an
+    // immediate of 64*BV bytes per step.
+    const int g = lane >> 4, j16 = lane & 15;
+    const int z = BSWZ * ((j16 >> 2) & 3);
+#pragma unroll
+    for (int v = 0; v < BV; ++v) {
+      const int X = wn * WN / 8 + 4 * v + 2 * (g & 1) + ((j16 & 3) >> 1);
+      rb_off[v] = LDS_B + (8 * (g >> 1) + (j16 >> 2)) * B_ROW + ((X ^ z) << 4) + 8 * (j16 & 1);
+    }
   }
 
-  // Row (within the tile) of staging slot i, and this thread's A chunk.
-  __device__ __forceinline__ int a_stage_row(int i) const { return (t >> 3) + 32 * i; }
-  __device__ __forceinline__ int a_chunk() const { return t & 7; }
-  // This thread's B k-group and 8-column group.
-  __device__ __forceinline__ int b_group() const { return t / B_NG; }
-  __device__ __forceinline__ int b_colgroup() const { return t % B_NG; }
+  // -- DMA placement --------------------------------------------------------
+  // A instruction i of this wave fills tile rows w*BM/4 + 8i .. +7; lane L
+  // writes physical chunk L&7 of row +L/8, i.e. logical chunk (L&7)^swz.
+  __device__ __forceinline__ int a_dma_row(int i) const { return w * (BM / 4) + 8 * i + (lane >> 3); }
+  __device__ __forceinline__ int a_dma_chunk(int i) const { return (lane & 7) ^ swz_a(a_dma_row(i)); }
+  // B instruction i of this wave fills K rows (w*B_DMA + i)*B_RPI .. +B_RPI-1.
+  __device__ __forceinline__ int b_dma_row(int i) const { return (w * B_DMA + i) * B_RPI + lane / B_CPR; }
+  __device__ __forceinline__ int b_dma_chunk(int i) const {
+    return (lane % B_CPR) ^ (BSWZ * (b_dma_row(i) & 3));
+  }
+
+  // B operand: element (0,0) at B, row pitch ldb_bytes, tile columns from n0.
+  __device__ __forceinline__ void set_b(const char* B, int64_t ldb_bytes, int64_t n0, int64_t N) {
+    b_base = B;
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i) {
+      const int64_t n = min(n0 + 8 * b_dma_chunk(i), N - 8);
+      b_off[i] = (uint32_t)((int64_t)b_dma_row(i) * ldb_bytes + n * 2);
+    }
+    b_step = 64 * ldb_bytes;
+  }
+  // A operand: rows come from base + row_off(i) (bytes; < 4 GiB), where
+  // row_off(i) is the start of the global row DMA instruction i fetches.
+  __device__ __forceinline__ void set_a_base(const char* base) { a_base = base; }
+  __device__ __forceinline__ void set_a(int i, uint32_t row_off) {
+    a_off[i] = row_off + a_dma_chunk(i) * 16;
+  }
 
   __device__ __forceinline__ void zero_acc() {
 #pragma unroll
@@ -88,113 +191,112 @@ struct Engine {
       for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
   }
 
-  // Global -> registers for K step kt.  CHECK zero-fills K positions >= K.
-  template <bool CHECK>
-  __device__ __forceinline__ void gload(int kt) {
-    const int64_t k0 = (int64_t)kt * kBK;
-    const int64_t ka = k0 + 8 * a_chunk();
+  // Issue the DMA of K step kt into buffer buf.  check: mask K chunks >= K
+  // (those LDS slots are zero-filled with ordinary stores instead).
+  __device__ __forceinline__ void dma(int kt, int buf, const bool check) {
+    const int64_t ka = (int64_t)kt * kBK;
+    const char* sa = a_base + ka * 2;
+    const char* sb = b_base + (int64_t)kt * b_step;
+    const uint32_t la = lds0 + buf * A_STAGE + (w * (BM / 4)) * 128;
+    const uint32_t lb = lds0 + LDS_B + buf * B_STAGE + (w * B_DMA) * 1024;
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      if (!CHECK || ka < K)
-        ra[i] = *reinterpret_cast<const u32x4*>(a_row[i] + ka * 2);
+    for (int i = 0; i < A_DMA; ++i) {
+      if (!check || ka + 8 * a_dma_chunk(i) < K)
+        dma16(a_off[i], sa, la + i * 1024);
       else
-        ra[i] = u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(smem + (la - lds0) + i * 1024 + lane * 16) = u32x4{0, 0, 0, 0};
     }
-    const int64_t kb = k0 + (int64_t)b_group() * B_ROWS;
 #pragma unroll
-    for (int j = 0; j < B_ROWS; ++j) {
-      if (!CHECK || kb + j < K)
-        rb[j] = *reinterpret_cast<const u32x4*>(b_col + (kb + j) * ldb_bytes);
+    for (int i = 0; i < B_DMA; ++i) {
+      if (!check || ka + b_dma_row(i) < K)
+        dma16(b_off[i], sb, lb + i * 1024);
       else
-        rb[j] = u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(smem + (lb - lds0) + i * 1024 + lane * 16) = u32x4{0, 0, 0, 0};
     }
   }
 
-  // Registers -> LDS stage s (A as-is, B transposed).
-  __device__ __forceinline__ void lstore(int s) {
-    char* sa = smem + s * STAGE;
-    char* sb = sa + A_BYTES;
+  // -- fragments ------------------------------------------------------------
+  // Sub-step ks (K 16ks .. 16ks+15 of the stage in buffer buf) into slot.
+  __device__ __forceinline__ void read_frags(int buf, int ks, int slot) {
+    const char* sa = smem + buf * A_STAGE;
+    const char* sb = smem + buf * B_STAGE;
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i)
-      *reinterpret_cast<u32x4*>(sa + lds_off(a_stage_row(i), a_chunk())) = ra[i];
-    const int g = b_group();
-    const int nb = 8 * b_colgroup();
-    if constexpr (B_ROWS == 8) {
-      // rb[j] = 8 columns of K row (8g + j).  Column c becomes LDS row nb + c
-      // holding K elements 8g .. 8g+7 = logical chunk g.
-#define FM_BT8(c)                                                               \
-  {                                                                             \
-    u32x4 v = {pick2<c>(rb[0], rb[1]), pick2<c>(rb[2], rb[3]),                  \
-               pick2<c>(rb[4], rb[5]), pick2<c>(rb[6], rb[7])};                 \
-    *reinterpret_cast<u32x4*>(sb + lds_off(nb + c, g)) = v;                     \
-  }
-      FM_BT8(0) FM_BT8(1) FM_BT8(2) FM_BT8(3) FM_BT8(4) FM_BT8(5) FM_BT8(6) FM_BT8(7)
-#undef FM_BT8
-    } else {
-      // rb[j] = 8 columns of K row (4g + j): K elements 4g .. 4g+3 are the
-      // (g & 1) half of logical chunk g >> 1.
-#define FM_BT4(c)                                                               \
-  {                                                                             \
-    u32x2 v = {pick2<c>(rb[0], rb[1]), pick2<c>(rb[2], rb[3])};                 \
-    *reinterpret_cast<u32x2*>(sb + lds_off(nb + c, g >> 1) + ((g & 1) << 3)) = v; \
-  }
-      FM_BT4(0) FM_BT4(1) FM_BT4(2) FM_BT4(3) FM_BT4(4) FM_BT4(5) FM_BT4(6) FM_BT4(7)
-#undef FM_BT4
+    for (int i = 0; i < FM; ++i)
+      fa[slot][i] = *reinterpret_cast<const u32x4*>(sa + ra_off[ks][i & 1] + i * 32 * 128);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      s16x4 h[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const char* p = sb + rb_off[j % BV] + (16 * ks + 4 * hh) * B_ROW + (j / BV) * (64 * BV);
+        h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FM_LDS4(p));
+      }
+      fb[slot][j] =
+          __builtin_bit_cast(u32x4, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
     }
   }
 
-  // MFMA over one LDS stage (four K sub-steps of 16).
-  __device__ __forceinline__ void compute(int s) {
-    const char* sa = smem + s * STAGE;
-    const char* sb = sa + A_BYTES;
-    const int r32 = lane & 31;
-    const int half = lane >> 5;
+  __device__ __forceinline__ void mma(int slot, int i0, int i1) {
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int chunk = 2 * ks + half;
-      u32x4 fa[FM], fb[FN];
+    for (int i = 0; i < FM; ++i) {
+      if (i < i0 || i >= i1) continue;
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        fa[i] = *reinterpret_cast<const u32x4*>(sa + lds_off(wm * WM + i * 32 + r32, chunk));
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        fb[j] = *reinterpret_cast<const u32x4*>(sb + lds_off(wn * WN + j * 32 + r32, chunk));
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = E::mfma32(fb[j], fa[i], acc[i][j]);
+      for (int j = 0; j < FN; ++j) acc[i][j] = E::mfma32(fb[slot][j], fa[slot][i], acc[i][j]);
     }
   }
 
-  // Full K loop over KT steps; accumulators start at zero.  Ends with a
-  // workgroup barrier, so LDS may be reused right after.
+  // One K step kt.  The MFMAs and fragment reads are unconditional (at the
+  // last step the next-stage read fetches stale data that is never used), so
+  // the accumulators live in one place throughout; only the DMA of stage kt+2
+  // is conditional.
+  __device__ __forceinline__ void step(int kt) {
+    const int cur = kt & 1;
+    read_frags(cur, 1, 1);
+    mma(0, 0, FM);
+    interleave<MFMAS, READS>();
+    read_frags(cur, 2, 0);
+    mma(1, 0, FM);
+    interleave<MFMAS, READS>();
+    read_frags(cur, 3, 1);
+    mma(0, 0, FM);
+    interleave<MFMAS, READS>();
+    mma(1, 0, FM / 2);
+    wait_all0();          // own DMA of stage kt+1 and every read of stage kt are done
+    __syncthreads();      // ... for all waves: stage kt+1 complete, buffer cur drained
+    if (kt + 2 < KT) dma(kt + 2, cur, KTAIL && kt + 3 == KT);
+    read_frags(cur ^ 1, 0, 0);
+    mma(1, FM / 2, FM);
+    interleave<MFMAS / 2, (READS < MFMAS / 2 ? READS : MFMAS / 2)>();
+  }
+
+  // Full K loop; accumulators start at zero.  When it returns every wave has
+  // passed the last step's barrier, so no wave reads this tile's data any more
+  // and the next tile may start its DMA right away.  KTAIL selects the
+  // variant that masks a partial last K step (K % 64 != 0).
   __device__ __forceinline__ void run() {
     zero_acc();
-    const int KT = (int)cdiv(K, kBK);
-    if (KT == 0) {
-      __syncthreads();
-      return;
-    }
-    const bool tail = (K % kBK) != 0;
-    if (tail && KT == 1) gload<true>(0); else gload<false>(0);
-    lstore(0);
+    if (KT == 0) return;
+    dma(0, 0, KTAIL && KT == 1);
+    if (KT > 1) dma(1, 1, KTAIL && KT == 2);
+    if (KT > 1 && !(KTAIL && KT == 2))
+      wait_vmcnt<DMA>();   // stage 0 landed; the full stage 1 may still be in flight
+    else
+      wait_vmcnt<0>();     // a masked stage issues fewer loads: wait for all
     __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      const bool more = kt + 1 < KT;
-      if (more) {
-        if (tail && kt + 2 == KT) gload<true>(kt + 1); else gload<false>(kt + 1);
-      }
-      compute(kt & 1);
-      if (more) lstore((kt + 1) & 1);
-      __syncthreads();
-    }
+    read_frags(0, 0, 0);
+    for (int kt = 0; kt < KT; ++kt) step(kt);
   }
 
-  // Output coordinates (within the tile) owned by this lane.
+  // Output coordinates (within the tile) owned by this lane: block (i, j),
+  // 4-column run r (0..3) holds row out_row(i) and columns out_col(j, r)..+3.
   __device__ __forceinline__ int out_row(int i) const { return wm * WM + i * 32 + (lane & 31); }
   __device__ __forceinline__ int out_col(int j, int r) const {
     return wn * WN + j * 32 + 8 * r + 4 * (lane >> 5);
   }
+  // Pin accumulator block (i, j) in AGPRs at this point of the program, so
+  // its copy into VGPRs for the epilogue cannot be hoisted above the stores
+  // of earlier blocks (which would need all 256 accumulators in VGPRs).
+  __device__ __forceinline__ void pin(int i, int j) { asm volatile("" : "+a"(acc[i][j])); }
   __device__ __forceinline__ f32x4 out_vals(int i, int j, int r) const {
     return f32x4{acc[i][j][4 * r + 0], acc[i][j][4 * r + 1], acc[i][j][4 * r + 2],
                  acc[i][j][4 * r + 3]};
