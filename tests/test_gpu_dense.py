@@ -11,7 +11,8 @@ from gpu_util import (BF16, F16, Arrival, assert_close, bits16, dev16, devf32, h
 
 pytestmark = pytest.mark.gpu
 
-TILES = ["256x128", "128x128", "256x256"]
+# FM_TILE forms: BMxBN[wNW]; a bare 256x256 takes the 8-wave form.
+TILES = ["256x128", "128x128", "256x256", "256x256w4", "256x128w8"]
 
 
 @pytest.fixture(autouse=True)

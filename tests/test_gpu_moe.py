@@ -75,12 +75,14 @@ def _moe_run(inp, e0, nl, dt, H_in=None):
     return off.cpu().numpy(), sp.cpu().numpy(), H, out
 
 
+@pytest.mark.parametrize("tile", ["256x256", "256x256w4", "256x128w8", "128x128"])
 @pytest.mark.parametrize("dt", [F16, BF16])
 @pytest.mark.parametrize("T,hidden,ffn,E,nl,e0", [(256, 256, 128, 16, 4, 4),
                                                   (300, 136, 264, 8, 8, 0),
                                                   (64, 512, 512, 64, 8, 0)])
-def test_moe_small(oracle, dt, T, hidden, ffn, E, nl, e0):
-    say(f"moe T={T} hidden={hidden} ffn={ffn} E={E} nl={nl} e0={e0} dt={dt}")
+def test_moe_small(oracle, monkeypatch, tile, dt, T, hidden, ffn, E, nl, e0):
+    monkeypatch.setenv("FM_MOE_TILE", tile)
+    say(f"moe T={T} hidden={hidden} ffn={ffn} E={E} nl={nl} e0={e0} dt={dt} tile={tile}")
     inp = wl.moe_inputs(T, hidden, ffn, E, nl, 2, dt, seed=T + hidden, zipf_s=1.2)
     roff, rsp = oracle.moe_route(inp["topk_ids"], e0, nl)
     Href = oracle.moe_layer0(dt, inp["X"], inp["W1"], rsp, roff, 2)

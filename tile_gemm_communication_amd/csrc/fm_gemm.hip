@@ -55,9 +55,9 @@ __device__ __forceinline__ void store_run(char* C, int64_t idx, const f32x4& v) 
   }
 }
 
-template <class E, int BM, int BN, Mode MODE, bool OUT32, bool KTAIL>
-__global__ __launch_bounds__(kThreads, 1) void dense_kernel(const DenseArgs args) {
-  using Eng = Engine<E, BM, BN, KTAIL>;
+template <class E, int BM, int BN, int NW, Mode MODE, bool OUT32, bool KTAIL>
+__global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args) {
+  using Eng = Engine<E, BM, BN, KTAIL, NW>;
   __shared__ __attribute__((aligned(16))) char smem[Eng::LDS_BYTES];
   __shared__ int s_abort;
 
@@ -197,19 +197,21 @@ __global__ __launch_bounds__(kThreads, 1) void dense_kernel(const DenseArgs args
 namespace {
 
 struct TileCfg {
-  int bm, bn;
+  int bm, bn, nw;
 };
 
 // Tile shape for an M x N output on G CUs: the fewest full-machine waves of
 // work, weighting smaller tiles by their lower MFMA:load ratio.
 TileCfg choose_tile(int64_t M, int64_t N, int G) {
   if (const char* env = std::getenv("FM_TILE")) {
-    int bm = 0, bn = 0;
-    if (std::sscanf(env, "%dx%d", &bm, &bn) == 2 && (bm == 128 || bm == 256) &&
-        (bn == 128 || bn == 256))
-      return {bm, bn};
+    int bm = 0, bn = 0, nw = 0;
+    const int got = std::sscanf(env, "%dx%dw%d", &bm, &bn, &nw);
+    if (got >= 2 && (bm == 128 || bm == 256) && (bn == 128 || bn == 256)) {
+      if (got < 3 || (nw != 4 && nw != 8)) nw = (bm == 256 && bn == 256) ? 8 : 4;
+      if (!(bm == 128 && bn == 128 && nw == 8)) return {bm, bn, nw};
+    }
   }
-  const TileCfg cands[3] = {{256, 256}, {256, 128}, {128, 128}};
+  const TileCfg cands[3] = {{256, 256, 8}, {256, 128, 4}, {128, 128, 4}};
   const double eff[3] = {1.0, 0.85, 0.7};
   TileCfg best = cands[0];
   double best_cost = 1e300;
@@ -258,25 +260,28 @@ template <Mode MODE, bool OUT32>
 fm_status_t launch_dense(fm_dtype_t dt, TileCfg cfg, const DenseArgs& args, hipStream_t stream) {
   const int G = std::min(args.order.total, device_cu_count());
   if (G <= 0) return FM_OK;
-  const dim3 grid(G), block(kThreads);
-#define FM_LAUNCH(E, BM, BN)                                                                   \
-  do {                                                                                         \
-    if (args.K % kBK)                                                                          \
-      hipLaunchKernelGGL((dense_kernel<E, BM, BN, MODE, OUT32, true>), grid, block, 0, stream, \
-                         args);                                                                \
-    else                                                                                       \
-      hipLaunchKernelGGL((dense_kernel<E, BM, BN, MODE, OUT32, false>), grid, block, 0,        \
-                         stream, args);                                                        \
+  const dim3 grid(G);
+#define FM_LAUNCH(E, BM, BN, NW)                                                              \
+  do {                                                                                        \
+    if (args.K % kBK) /* ragged K: the 4-wave form keeps the tail path spill-free */          \
+      hipLaunchKernelGGL((dense_kernel<E, BM, BN, 4, MODE, OUT32, true>), grid, dim3(256), 0, \
+                         stream, args);                                                       \
+    else                                                                                      \
+      hipLaunchKernelGGL((dense_kernel<E, BM, BN, NW, MODE, OUT32, false>), grid,             \
+                         dim3(64 * NW), 0, stream, args);                                     \
   } while (0)
-  if (dt == FM_F16) {
-    if (cfg.bm == 256 && cfg.bn == 256) FM_LAUNCH(F16, 256, 256);
-    else if (cfg.bm == 256) FM_LAUNCH(F16, 256, 128);
-    else FM_LAUNCH(F16, 128, 128);
-  } else {
-    if (cfg.bm == 256 && cfg.bn == 256) FM_LAUNCH(BF16, 256, 256);
-    else if (cfg.bm == 256) FM_LAUNCH(BF16, 256, 128);
-    else FM_LAUNCH(BF16, 128, 128);
-  }
+#define FM_LAUNCH_E(E)                                                                        \
+  do {                                                                                        \
+    if (cfg.bm == 256 && cfg.bn == 256) {                                                     \
+      if (cfg.nw == 8) FM_LAUNCH(E, 256, 256, 8); else FM_LAUNCH(E, 256, 256, 4);             \
+    } else if (cfg.bm == 256) {                                                               \
+      if (cfg.nw == 8) FM_LAUNCH(E, 256, 128, 8); else FM_LAUNCH(E, 256, 128, 4);             \
+    } else {                                                                                  \
+      FM_LAUNCH(E, 128, 128, 4);                                                              \
+    }                                                                                         \
+  } while (0)
+  if (dt == FM_F16) FM_LAUNCH_E(F16); else FM_LAUNCH_E(BF16);
+#undef FM_LAUNCH_E
 #undef FM_LAUNCH
   return launch_status();
 }

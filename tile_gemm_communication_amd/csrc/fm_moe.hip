@@ -117,9 +117,9 @@ struct MoeArgs {
   int topk, n_local, tiles_n, group_m;
 };
 
-template <class E, int BM, int BN, bool SCATTER, bool KTAIL>
-__global__ __launch_bounds__(kThreads, 1) void moe_kernel(const MoeArgs a) {
-  using Eng = Engine<E, BM, BN, KTAIL>;
+template <class E, int BM, int BN, int NW, bool SCATTER, bool KTAIL>
+__global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
+  using Eng = Engine<E, BM, BN, KTAIL, NW>;
   __shared__ __attribute__((aligned(16))) char smem[Eng::LDS_BYTES];
   __shared__ int s_off[kMaxLocalExperts + 1];
   __shared__ int s_tile0[kMaxLocalExperts + 1];
@@ -238,40 +238,47 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(const MoeArgs a) {
 namespace {
 
 struct MoeTile {
-  int bm, bn;
+  int bm, bn, nw;
 };
 
 MoeTile moe_tile() {
   if (const char* env = std::getenv("FM_MOE_TILE")) {
-    int bm = 0, bn = 0;
-    if (std::sscanf(env, "%dx%d", &bm, &bn) == 2 && (bm == 128 || bm == 256) &&
-        (bn == 128 || bn == 256))
-      return {bm, bn};
+    int bm = 0, bn = 0, nw = 0;
+    const int got = std::sscanf(env, "%dx%dw%d", &bm, &bn, &nw);
+    if (got >= 2 && (bm == 128 || bm == 256) && (bn == 128 || bn == 256)) {
+      if (got < 3 || (nw != 4 && nw != 8)) nw = (bm == 256 && bn == 256) ? 8 : 4;
+      if (!(bm == 128 && bn == 128 && nw == 8)) return {bm, bn, nw};
+    }
   }
-  return {256, 256};
+  return {256, 256, 8};
 }
 
 template <bool SCATTER>
 fm_status_t launch_moe(fm_dtype_t dt, MoeTile cfg, MoeArgs& a, hipStream_t stream) {
   a.tiles_n = (int)cdiv(a.N, cfg.bn);
   a.group_m = 8;
-  const dim3 grid(device_cu_count()), block(kThreads);
-#define FM_LAUNCH(E, BM, BN)                                                                  \
-  do {                                                                                        \
-    if (a.K % kBK)                                                                            \
-      hipLaunchKernelGGL((moe_kernel<E, BM, BN, SCATTER, true>), grid, block, 0, stream, a);  \
-    else                                                                                      \
-      hipLaunchKernelGGL((moe_kernel<E, BM, BN, SCATTER, false>), grid, block, 0, stream, a); \
+  const dim3 grid(device_cu_count());
+#define FM_LAUNCH(E, BM, BN, NW)                                                             \
+  do {                                                                                       \
+    if (a.K % kBK) /* ragged K: the 4-wave form keeps the tail path spill-free */            \
+      hipLaunchKernelGGL((moe_kernel<E, BM, BN, 4, SCATTER, true>), grid, dim3(256), 0,       \
+                         stream, a);                                                         \
+    else                                                                                     \
+      hipLaunchKernelGGL((moe_kernel<E, BM, BN, NW, SCATTER, false>), grid, dim3(64 * NW), 0, \
+                         stream, a);                                                         \
   } while (0)
-  if (dt == FM_F16) {
-    if (cfg.bm == 256 && cfg.bn == 256) FM_LAUNCH(F16, 256, 256);
-    else if (cfg.bm == 256) FM_LAUNCH(F16, 256, 128);
-    else FM_LAUNCH(F16, 128, 128);
-  } else {
-    if (cfg.bm == 256 && cfg.bn == 256) FM_LAUNCH(BF16, 256, 256);
-    else if (cfg.bm == 256) FM_LAUNCH(BF16, 256, 128);
-    else FM_LAUNCH(BF16, 128, 128);
-  }
+#define FM_LAUNCH_E(E)                                                                       \
+  do {                                                                                       \
+    if (cfg.bm == 256 && cfg.bn == 256) {                                                    \
+      if (cfg.nw == 8) FM_LAUNCH(E, 256, 256, 8); else FM_LAUNCH(E, 256, 256, 4);            \
+    } else if (cfg.bm == 256) {                                                              \
+      if (cfg.nw == 8) FM_LAUNCH(E, 256, 128, 8); else FM_LAUNCH(E, 256, 128, 4);            \
+    } else {                                                                                 \
+      FM_LAUNCH(E, 128, 128, 4);                                                             \
+    }                                                                                        \
+  } while (0)
+  if (dt == FM_F16) FM_LAUNCH_E(F16); else FM_LAUNCH_E(BF16);
+#undef FM_LAUNCH_E
 #undef FM_LAUNCH
   return launch_status();
 }

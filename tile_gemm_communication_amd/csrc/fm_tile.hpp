@@ -1,9 +1,12 @@
 // fm_tile.hpp -- the MFMA macro-tile engine shared by every GEMM-shaped
 // kernel in libfluxmi (dense, AllGather, ReduceScatter, grouped MoE).
 //
-// One workgroup = 4 wave64 (one per SIMD) arranged 2x2 over a BM x BN output
-// tile; each wave owns a (BM/2) x (BN/2) sub-tile of 32x32 blocks computed
-// with v_mfma_f32_32x32x16_{f16,bf16} into fp32 accumulators (AGPRs).
+// One workgroup = NW wave64 (4: one per SIMD, 8: two per SIMD) arranged
+// 2 x NW/2 over a BM x BN output tile; each wave owns a (BM/2) x (BN/(NW/2))
+// sub-tile of 32x32 blocks computed with v_mfma_f32_32x32x16_{f16,bf16} into
+// fp32 accumulators (AGPRs).  With two waves per SIMD the matrix core takes
+// MFMAs from whichever wave is ready, which covers issue gaps, LDS latency
+// and barrier skew of the other.
 //
 // Data path, one LDS stage = one K step of 64, two stages in flight:
 //   HBM/L2 --global_load_lds_dwordx4 (direct to LDS, no VGPR staging)--> LDS
@@ -16,7 +19,7 @@
 //
 // Bank-conflict-free placement: rows are cut into 16-byte chunks; chunk c of
 // A row m is stored at c ^ ((m ^ m>>3) & 7) and chunk c of B row k at
-// c ^ BSWZ*(k & 3).  A direct-to-LDS load writes its 64 lanes' 16 bytes
+// c ^ BSWZ*(k & 3) (BSWZ = 4 for the 64-bank LDS of gfx950).  A direct-to-LDS load writes its 64 lanes' 16 bytes
 // contiguously, so the placement is realised by choosing which global chunk
 // each lane fetches.
 //
@@ -25,12 +28,15 @@
 // pipeline needs is explicit (s_waitcnt + barrier below).
 //
 // Pipeline per K step kt (buffer cur = kt & 1), fragments double-buffered:
-//   sub-steps 0..2: 16 MFMAs each, interleaved with the LDS reads of the next
+//   sub-steps 0..2: MFMAs interleaved with the LDS reads of the next
 //                   sub-step's fragments;
-//   sub-step 3:     half the MFMAs; wait for this wave's DMA and reads;
-//                   barrier (stage kt+1 is complete and stage kt drained);
-//                   issue the DMA of stage kt+2 into buffer cur; read
-//                   sub-step 0 of stage kt+1 interleaved with the other half.
+//   barrier:        after this wave's DMA of stage kt+1 and its reads of
+//                   stage kt are done (stage kt+1 complete, stage kt drained);
+//   sub-step 3:     MFMAs interleaved with the reads of sub-step 0 of stage
+//                   kt+1 and the DMA of stage kt+2 into buffer cur.
+// Every instruction group is fenced with sched_barrier, so the issue order is
+// the source order: one LDS read or DMA per MFMA, never a burst of loads
+// that would leave the matrix cores idle.
 //
 // The MFMA takes B^T as its first operand and A as its second, so a 32x32
 // result block is C^T in the instruction's layout: lane l holds row
@@ -79,27 +85,30 @@ __device__ __forceinline__ void interleave() {
   if constexpr (MFMAS > READS) __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - READS, 0);
 }
 
-template <class E, int BM, int BN, bool KTAIL, int BSWZ = 2>
+template <class E, int BM, int BN, bool KTAIL, int NW = 4, int BSWZ = 4>
 struct Engine {
-  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int NWM = 2, NWN = NW / 2;          // wave grid over the tile
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int WM = BM / NWM, WN = BN / NWN;
   static constexpr int FM = WM / 32, FN = WN / 32;     // 32x32 blocks per wave
   static constexpr int A_STAGE = BM * 128;
   static constexpr int B_ROW = BN * 2;
   static constexpr int B_STAGE = 64 * B_ROW;
   static constexpr int LDS_B = 2 * A_STAGE;             // B stages follow both A stages
   static constexpr int LDS_BYTES = 2 * (A_STAGE + B_STAGE);
-  static constexpr int A_DMA = BM / 32;                 // DMA instructions per wave per stage
+  static constexpr int A_ROWS = BM / NW;                // A rows each wave stages
+  static constexpr int A_DMA = A_ROWS / 8;              // DMA instructions per wave per stage
   static constexpr int B_CPR = BN / 8;                  // 16-byte chunks per B row
   static constexpr int B_RPI = 64 / B_CPR;              // B rows per 1 KB DMA instruction
-  static constexpr int B_DMA = BN / 32;
+  static constexpr int B_DMA = BN / (8 * NW);
   static constexpr int DMA = A_DMA + B_DMA;
   static constexpr int READS = FM + 2 * FN;             // LDS reads per sub-step
   static constexpr int MFMAS = FM * FN;                 // MFMAs per sub-step
   static_assert(BM == 128 || BM == 256, "BM must be 128 or 256");
   static_assert(BN == 128 || BN == 256, "BN must be 128 or 256");
   static_assert(BSWZ == 2 || BSWZ == 4, "B swizzle step");
-  static_assert((WN / 8) % (4 * ((BSWZ == 2) ? 2 : 4)) == 0,
-                "the B swizzle must not reach the wave's column offset");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert(A_DMA >= 1 && B_DMA >= 1 && WN >= 32, "tile too small for the wave grid");
 
   char* smem;
   uint32_t lds0;   // LDS byte address of smem (wave-uniform)
@@ -128,8 +137,8 @@ struct Engine {
     const int t = threadIdx.x;
     lane = t & 63;
     w = __builtin_amdgcn_readfirstlane(t >> 6);
-    wm = w >> 1;
-    wn = w & 1;
+    wm = w / NWN;
+    wn = w % NWN;
     lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)s);
     KT = (int)cdiv(K, kBK);
     // A fragment of block i, sub-step ks: row m = wm*WM + 32i + r32, chunk
@@ -159,7 +168,7 @@ struct Engine {
   // -- DMA placement --------------------------------------------------------
   // A instruction i of this wave fills tile rows w*BM/4 + 8i .. +7; lane L
   // writes physical chunk L&7 of row +L/8, i.e. logical chunk (L&7)^swz.
-  __device__ __forceinline__ int a_dma_row(int i) const { return w * (BM / 4) + 8 * i + (lane >> 3); }
+  __device__ __forceinline__ int a_dma_row(int i) const { return w * A_ROWS + 8 * i + (lane >> 3); }
   __device__ __forceinline__ int a_dma_chunk(int i) const { return (lane & 7) ^ swz_a(a_dma_row(i)); }
   // B instruction i of this wave fills K rows (w*B_DMA + i)*B_RPI .. +B_RPI-1.
   __device__ __forceinline__ int b_dma_row(int i) const { return (w * B_DMA + i) * B_RPI + lane / B_CPR; }
@@ -197,7 +206,7 @@ struct Engine {
     const int64_t ka = (int64_t)kt * kBK;
     const char* sa = a_base + ka * 2;
     const char* sb = b_base + (int64_t)kt * b_step;
-    const uint32_t la = lds0 + buf * A_STAGE + (w * (BM / 4)) * 128;
+    const uint32_t la = lds0 + buf * A_STAGE + (w * A_ROWS) * 128;
     const uint32_t lb = lds0 + LDS_B + buf * B_STAGE + (w * B_DMA) * 1024;
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i) {
@@ -216,23 +225,87 @@ struct Engine {
   }
 
   // -- fragments ------------------------------------------------------------
-  // Sub-step ks (K 16ks .. 16ks+15 of the stage in buffer buf) into slot.
-  __device__ __forceinline__ void read_frags(int buf, int ks, int slot) {
+  // LDS read items of one sub-step, in issue order: for k = 0, 1, ...: A
+  // fragment k (if k < FM), then the two halves of B fragment k (if k < FN),
+  // so the fragments the first MFMAs need arrive first.  item_code(q) packs
+  // (kind, index): kind 0 = A, 1 = B half 0, 2 = B half 1.
+  static constexpr int RITEMS = READS;
+  static constexpr int item_code(int q) {
+    int n = 0;
+    for (int k = 0; k < (FM > FN ? FM : FN); ++k) {
+      if (k < FM) { if (n == q) return k * 4 + 0; ++n; }
+      if (k < FN) {
+        if (n == q) return k * 4 + 1;
+        ++n;
+        if (n == q) return k * 4 + 2;
+        ++n;
+      }
+    }
+    return -1;
+  }
+
+  __device__ __forceinline__ void read_item(int q, int buf, int ks, int slot) {
     const char* sa = smem + buf * A_STAGE;
     const char* sb = smem + buf * B_STAGE;
+    const int code = item_code(q);
+    const int j = code >> 2, kind = code & 3;
+    if (kind == 0) {
+      fa[slot][j] = *reinterpret_cast<const u32x4*>(sa + ra_off[ks][j & 1] + j * 32 * 128);
+    } else {
+      const int hh = kind - 1;
+      const char* p = sb + rb_off[j % BV] + (16 * ks + 4 * hh) * B_ROW + (j / BV) * (64 * BV);
+      const s16x4 h = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FM_LDS4(p));
+      const u32x2 hv = __builtin_bit_cast(u32x2, h);
+      if (hh == 0) { fb[slot][j][0] = hv[0]; fb[slot][j][1] = hv[1]; }
+      else { fb[slot][j][2] = hv[0]; fb[slot][j][3] = hv[1]; }
+    }
+  }
+
+  __device__ __forceinline__ void read_frags(int buf, int ks, int slot) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      fa[slot][i] = *reinterpret_cast<const u32x4*>(sa + ra_off[ks][i & 1] + i * 32 * 128);
+    for (int q = 0; q < RITEMS; ++q) read_item(q, buf, ks, slot);
+  }
+
+  // DMA item d (0 .. DMA-1) of K step kt into buffer buf (full stage).
+  __device__ __forceinline__ void dma_item(int d, int kt, int buf) {
+    if (d < A_DMA) {
+      const uint32_t la = lds0 + buf * A_STAGE + (w * A_ROWS) * 128;
+      dma16(a_off[d], a_base + (int64_t)kt * kBK * 2, la + d * 1024);
+    } else {
+      const int i = d - A_DMA;
+      const uint32_t lb = lds0 + LDS_B + buf * B_STAGE + (w * B_DMA) * 1024;
+      dma16(b_off[i], b_base + (int64_t)kt * b_step, lb + i * 1024);
+    }
+  }
+
+  // One sub-step: the FM x FN MFMAs on fragment slot `cur`, with the reads of
+  // the next sub-step (buffer nbuf, sub-step nks, into slot cur^1) and, if
+  // DMA_KT >= 0, the DMA of K step DMA_KT into buffer dbuf woven between
+  // them.  The source order is the issue order (sched_barrier fences), one
+  // memory operation per MFMA where possible.
+  __device__ __forceinline__ void substep(int cur, int nbuf, int nks, bool do_read,
+                                          int dma_kt, int dbuf) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      s16x4 h[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const char* p = sb + rb_off[j % BV] + (16 * ks + 4 * hh) * B_ROW + (j / BV) * (64 * BV);
-        h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FM_LDS4(p));
+    for (int q = 0; q < MFMAS; ++q) {
+      const int i = q / FN, j = q % FN;
+      acc[i][j] = E::mfma32(fb[cur][j], fa[cur][i], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (do_read && q < RITEMS) {
+        read_item(q, nbuf, nks, cur ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      fb[slot][j] =
-          __builtin_bit_cast(u32x4, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      if (dma_kt >= 0 && q < DMA) {
+        dma_item(q, dma_kt, dbuf);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (do_read) {       // more read items than MFMAs (small tiles)
+#pragma unroll
+      for (int q = MFMAS; q < RITEMS; ++q) read_item(q, nbuf, nks, cur ^ 1);
+    }
+    if (dma_kt >= 0) {   // more DMA items than MFMAs
+#pragma unroll
+      for (int d = MFMAS; d < DMA; ++d) dma_item(d, dma_kt, dbuf);
     }
   }
 
@@ -245,28 +318,30 @@ struct Engine {
     }
   }
 
-  // One K step kt.  The MFMAs and fragment reads are unconditional (at the
-  // last step the next-stage read fetches stale data that is never used), so
-  // the accumulators live in one place throughout; only the DMA of stage kt+2
-  // is conditional.
+  // One K step kt (buffer cur = kt & 1):
+  //   sub-steps 0..2: MFMAs on the fragments in registers while the next
+  //                   sub-step's fragments are read;
+  //   wait for this wave's DMA (stage kt+1) and reads, barrier: stage kt+1 is
+  //                   complete and buffer cur is drained;
+  //   sub-step 3:     MFMAs while sub-step 0 of stage kt+1 is read and the
+  //                   DMA of stage kt+2 is issued into buffer cur.
+  // Without a K tail the DMA is unconditional: past the end it re-loads the
+  // last stage into a buffer nobody reads again (each wave only ever writes
+  // its own LDS rows, and its loads complete in order, so a later tile's
+  // data is never overwritten).  The accumulators thus stay in one place.
   __device__ __forceinline__ void step(int kt) {
     const int cur = kt & 1;
-    read_frags(cur, 1, 1);
-    mma(0, 0, FM);
-    interleave<MFMAS, READS>();
-    read_frags(cur, 2, 0);
-    mma(1, 0, FM);
-    interleave<MFMAS, READS>();
-    read_frags(cur, 3, 1);
-    mma(0, 0, FM);
-    interleave<MFMAS, READS>();
-    mma(1, 0, FM / 2);
-    wait_all0();          // own DMA of stage kt+1 and every read of stage kt are done
-    __syncthreads();      // ... for all waves: stage kt+1 complete, buffer cur drained
-    if (kt + 2 < KT) dma(kt + 2, cur, KTAIL && kt + 3 == KT);
-    read_frags(cur ^ 1, 0, 0);
-    mma(1, FM / 2, FM);
-    interleave<MFMAS / 2, (READS < MFMAS / 2 ? READS : MFMAS / 2)>();
+    substep(0, cur, 1, true, -1, 0);
+    substep(1, cur, 2, true, -1, 0);
+    substep(0, cur, 3, true, -1, 0);
+    wait_all0();
+    __syncthreads();
+    if constexpr (!KTAIL) {
+      substep(1, cur ^ 1, 0, true, min(kt + 2, KT - 1), cur);
+    } else {
+      if (kt + 2 < KT) dma(kt + 2, cur, kt + 3 == KT);
+      substep(1, cur ^ 1, 0, true, -1, 0);
+    }
   }
 
   // Full K loop; accumulators start at zero.  When it returns every wave has
