@@ -52,8 +52,14 @@ def parse():
     ap.add_argument("--ect-iters", type=int, default=20)
     ap.add_argument("--no-ect", action="store_true", help="skip the ECT comparisons")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256,
+    ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="rows of the AllGather-GEMM the CPU oracle computes as its sample")
+    ap.add_argument("--serial-arrival", action="store_true",
+                    help="let every chunk land before fm_ag_gemm starts (for profilers that "
+                         "serialise kernel dispatches, where a concurrent arrival cannot happen)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run fm_chunk_push over MIB MiB three times and exit: the "
+                         "known-size copy that calibrates the HBM byte counters")
     return ap.parse_args()
 
 
@@ -114,6 +120,7 @@ class Workload:
         self.off = torch.zeros(self.n_local + 1, dtype=torch.int32, device=dev)
 
         self.side = torch.cuda.Stream(device=dev)
+        self.serial_arrival = False
         self.order = list(range(self.n))                  # local chunk first, then ring order
         self.flop_ag = 2.0 * self.M * self.N1 * self.K1
         self.flop_rs = 2.0 * self.M * self.N2 * self.K2
@@ -158,6 +165,8 @@ class Workload:
         cs = torch.cuda.current_stream()
         self.epoch += 1
         self.push_all(self.epoch)
+        if self.serial_arrival:
+            cs.wait_stream(self.side)
         if evs: evs[0].record(cs)
         self.ag(self.epoch)
         if evs: evs[1].record(cs)
@@ -207,6 +216,8 @@ def ect_block(w, iters):
     def fused():
         w.epoch += 1
         w.push_all(w.epoch)
+        if w.serial_arrival:
+            cs.wait_stream(w.side)
         w.ag(w.epoch)
         cs.wait_stream(w.side)
 
@@ -297,6 +308,25 @@ def cpu_baseline(w, rows):
                       f"({rows}x{w.N1}x{w.K1}, fp64 accumulation)"}
 
 
+def copy_probe(mib):
+    """Three fm_chunk_push copies of `mib` MiB: a kernel whose HBM traffic is
+    known (read mib, write mib), to scale the profiler's byte counters."""
+    import torch
+
+    import tile_gemm_communication_amd as fm
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    for e in range(1, 4):
+        fm.fm_chunk_push(src, dst, flag, cnt, e)
+    torch.cuda.synchronize()
+    assert bool((dst == 1).all())
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n,
+                      "dispatches": 3}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -309,7 +339,11 @@ def main():
     import tile_gemm_communication_amd as fm
     fm.lib()                                   # fail loudly if the library is missing
     log(f"libfluxmi {fm.version()} on {torch.cuda.get_device_name(0)}")
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     w = Workload()
+    w.serial_arrival = args.serial_arrival
     cs = torch.cuda.current_stream()
 
     log(f"warmup {args.warmup} steps")

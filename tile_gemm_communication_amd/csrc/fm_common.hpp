@@ -55,6 +55,13 @@ template <class E> struct Out16 {
 // Device properties cached once per device (compute-unit count).
 int device_cu_count();
 
+// Per-device tile counters for ordered epilogues: kTileCounters zeroed
+// uint32 words, allocated on first use and kept until the process ends.
+// Every launch that uses them leaves them at zero again.  NULL if the
+// allocation fails.
+constexpr int kTileCounters = 32768;
+uint32_t* device_tile_counters();
+
 // Translate the last HIP launch error into a status.
 inline fm_status_t launch_status() {
   return hipGetLastError() == hipSuccess ? FM_OK : FM_ERR_HIP;

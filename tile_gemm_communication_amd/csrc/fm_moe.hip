@@ -113,7 +113,9 @@ struct MoeArgs {
   const int32_t* sorted_pairs;
   const int32_t* offsets;
   const float* weights;       // [T * topk] (layer 1)
+  uint32_t* col_done;         // layer 1: finished tiles per N-tile column (self-resetting)
   int64_t K, N;
+  int64_t spin_limit;
   int topk, n_local, tiles_n, group_m;
 };
 
@@ -169,69 +171,75 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
     eng.set_b(a.W + (int64_t)e * K * N * 2, N * 2, n0, N);
     eng.run();
 
-    const bool interior = (m0 + BM <= rows_e) && (n0 + BN <= N);
+    // Epilogue through the LDS staging regions (whole-line global accesses).
+    eng.ep_begin();
     if constexpr (SCATTER) {
-      // out[token] += weight * row, as fp32 atomics (a token may receive up to
-      // topk local contributions, in any order).
+      // out[token] += weight * row.  A token's top-k pairs sit in different
+      // experts, never twice in one; the tiles of one N column therefore only
+      // collide across experts, and expert e's tiles of column tn apply their
+      // read-modify-write after every earlier expert's tiles of that column
+      // (count per column, in expert order).  The adds are plain fp32 loads
+      // and stores, in a fixed order: the combine is deterministic.
+      if (e > 0 && t == 0)
+        wait_count(a.col_done + tn, (uint32_t)(s_tile0[e] / a.tiles_n), a.spin_limit);
+      __syncthreads();
+      const int col = eng.ep_col();
+      const bool col_ok = n0 + col < N;
 #pragma unroll
       for (int i = 0; i < Eng::FM; ++i) {
-        const int lr = m0 + eng.out_row(i);
-        if (lr >= rows_e) continue;
-        const int p = a.sorted_pairs[row_base + lr];
-        const float w = a.weights[p];
-        float* orow = reinterpret_cast<float*>(a.out) + (int64_t)(p / a.topk) * N + n0;
+        eng.ep_stage(i);
+        float* dst[Eng::EP_READS];
+        float wt[Eng::EP_READS];
 #pragma unroll
-        for (int j = 0; j < Eng::FN; ++j) {
-          eng.pin(i, j);
+        for (int q = 0; q < Eng::EP_READS; ++q) {
+          const int lr = m0 + eng.ep_row(i, q);
+          dst[q] = nullptr;
+          wt[q] = 0.f;
+          if (lr < rows_e && col_ok) {
+            const int p = a.sorted_pairs[row_base + lr];
+            wt[q] = a.weights[p];
+            dst[q] = reinterpret_cast<float*>(a.out) + (int64_t)(p / a.topk) * N + n0 + col;
+          }
+        }
+        f32x4 old[Eng::EP_READS];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int c = eng.out_col(j, r);
-            if (!interior && n0 + c >= N) continue;
-            const f32x4 v = eng.out_vals(i, j, r);
-            unsafeAtomicAdd(orow + c + 0, w * v[0]);
-            unsafeAtomicAdd(orow + c + 1, w * v[1]);
-            unsafeAtomicAdd(orow + c + 2, w * v[2]);
-            unsafeAtomicAdd(orow + c + 3, w * v[3]);
+        for (int q = 0; q < Eng::EP_READS; ++q)
+          if (dst[q]) old[q] = *reinterpret_cast<const f32x4*>(dst[q]);
+#pragma unroll
+        for (int q = 0; q < Eng::EP_READS; ++q) {
+          const f32x4 v = eng.ep_read(q);
+          if (dst[q]) {
+            f32x4 o = old[q];
+            o[0] += wt[q] * v[0];
+            o[1] += wt[q] * v[1];
+            o[2] += wt[q] * v[2];
+            o[3] += wt[q] * v[3];
+            *reinterpret_cast<f32x4*>(dst[q]) = o;
           }
         }
       }
-    } else if (interior) {
-      char* base = a.out + ((int64_t)(row_base + m0) * N + n0) * 2;
-      const uint32_t lane_off = (uint32_t)(eng.out_row(0) * N + eng.out_col(0, 0)) * 2;
-#pragma unroll
-      for (int i = 0; i < Eng::FM; ++i) {
-        char* rb = base + (uint32_t)(i * 32 * N * 2) + lane_off;
-#pragma unroll
-        for (int j = 0; j < Eng::FN; ++j) {
-          eng.pin(i, j);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const f32x4 v = eng.out_vals(i, j, r);
-            const u32x2 pk = {E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
-            *reinterpret_cast<u32x2*>(rb + (j * 32 + 8 * r) * 2) = pk;
-          }
-        }
-      }
+      wait_vmcnt<0>();   // this wave's stores are complete
+      __syncthreads();
+      if (t == 0) signal_count(a.col_done + tn, (uint32_t)(total / a.tiles_n));
     } else {
+      // H rows in expert-sorted order, 16-bit.
+      const int col = eng.ep_col();
+      const bool col_ok = n0 + col < N;
 #pragma unroll
       for (int i = 0; i < Eng::FM; ++i) {
-        const int lr = m0 + eng.out_row(i);
-        if (lr >= rows_e) continue;
-        char* hrow = a.out + (int64_t)(row_base + lr) * N * 2;
+        eng.ep_stage(i);
 #pragma unroll
-        for (int j = 0; j < Eng::FN; ++j) {
-          eng.pin(i, j);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int64_t col = n0 + eng.out_col(j, r);
-            if (col >= N) continue;
-            const f32x4 v = eng.out_vals(i, j, r);
+        for (int q = 0; q < Eng::EP_READS; ++q) {
+          const int lr = m0 + eng.ep_row(i, q);
+          const f32x4 v = eng.ep_read(q);
+          if (lr < rows_e && col_ok) {
             const u32x2 pk = {E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
-            *reinterpret_cast<u32x2*>(hrow + col * 2) = pk;
+            *reinterpret_cast<u32x2*>(a.out + ((int64_t)(row_base + lr) * N + n0 + col) * 2) = pk;
           }
         }
       }
     }
+    eng.ep_end();
   }
 }
 
@@ -257,6 +265,12 @@ template <bool SCATTER>
 fm_status_t launch_moe(fm_dtype_t dt, MoeTile cfg, MoeArgs& a, hipStream_t stream) {
   a.tiles_n = (int)cdiv(a.N, cfg.bn);
   a.group_m = 8;
+  a.spin_limit = 1ll << 26;
+  if (SCATTER) {
+    if (a.tiles_n > kTileCounters) return FM_ERR_UNSUPPORTED;
+    a.col_done = device_tile_counters();
+    if (!a.col_done) return FM_ERR_HIP;
+  }
   const dim3 grid(device_cu_count());
 #define FM_LAUNCH(E, BM, BN, NW)                                                             \
   do {                                                                                       \

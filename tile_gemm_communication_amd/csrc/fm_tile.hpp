@@ -376,6 +376,50 @@ struct Engine {
     return f32x4{acc[i][j][4 * r + 0], acc[i][j][4 * r + 1], acc[i][j][4 * r + 2],
                  acc[i][j][4 * r + 3]};
   }
+
+  // -- LDS-staged epilogue ----------------------------------------------------
+  // In the MFMA layout a lane holds 4 columns of one row and a wave's 64 lanes
+  // span 32 rows, so a direct global access touches 32 rows x 32 bytes.  The
+  // staged epilogue turns each 32-row block of the wave's sub-tile around
+  // through a wave-private LDS region: after ep_stage(i) and ep_read(q), lane
+  // l holds 4 consecutive fp32 columns of one row and the wave covers EP_RPI
+  // whole rows of WN columns, so global loads and stores move full lines.
+  // Rows are padded by 16 bytes, which makes both the 16-byte writes (32 rows
+  // apart) and the 16-byte reads (row-contiguous) conflict-free.
+  static constexpr int EP_STRIDE = WN * 4 + 16;   // bytes per staged row
+  static constexpr int EP_LPR = WN / 4;           // lanes per staged row
+  static constexpr int EP_RPI = 64 / EP_LPR;      // rows per read instruction
+  static constexpr int EP_READS = 32 / EP_RPI;    // reads per 32-row block
+  static_assert(NW * 32 * EP_STRIDE <= LDS_BYTES, "staging regions exceed LDS");
+
+  // Before the first ep_stage of a tile: this wave's DMAs have landed and no
+  // wave reads K-loop data any more.  After the last ep_read: ep_end() before
+  // the next tile's DMA may overwrite the regions.
+  __device__ __forceinline__ void ep_begin() {
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+  __device__ __forceinline__ void ep_end() { __syncthreads(); }
+  __device__ __forceinline__ void ep_stage(int i) {
+    char* reg = smem + w * (32 * EP_STRIDE) + (lane & 31) * EP_STRIDE + 16 * (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      pin(i, j);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<f32x4*>(reg + (32 * j + 8 * r) * 4) = out_vals(i, j, r);
+    }
+  }
+  // Tile row and column of the 4 values ep_read(q) returns (block i).
+  __device__ __forceinline__ int ep_row(int i, int q) const {
+    return wm * WM + i * 32 + q * EP_RPI + lane / EP_LPR;
+  }
+  __device__ __forceinline__ int ep_col() const { return wn * WN + 4 * (lane % EP_LPR); }
+  __device__ __forceinline__ f32x4 ep_read(int q) const {
+    return *reinterpret_cast<const f32x4*>(smem + w * (32 * EP_STRIDE) +
+                                           (q * EP_RPI + lane / EP_LPR) * EP_STRIDE +
+                                           16 * (lane % EP_LPR));
+  }
 };
 
 }  // namespace fm
