@@ -185,9 +185,14 @@ fm_status_t fm_moe_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t
  * where row(p) is p's position in sorted_pairs (from fm_moe_gather_gemm /
  * fm_moe_route with the same arguments).
  *   H [rows, ffn] with rows = expert_offsets[n_local]; W2 [n_local, ffn, hidden];
- *   topk_weights device fp32 [T, topk]; out device fp32 [T, hidden] (accumulated
- *   with fp32 atomic adds, so the order of the <= topk additions per element is
- *   unspecified).
+ *   topk_weights device fp32 [T, topk]; out device fp32 [T, hidden].
+ * The additions into a token row are applied in local-expert order with plain
+ * fp32 loads and stores (no atomics), so the result is deterministic.  The
+ * ordering uses per-device tile counters that the library allocates on the
+ * first call (128 KiB, kept until the process ends; FM_ERR_HIP if that
+ * allocation fails) and every call leaves at zero: calls of this function on
+ * one device must not overlap in time (issue them on one stream, or order
+ * the streams).  Requires ceil(hidden / 128) <= 32768.
  */
 fm_status_t fm_moe_gemm_scatter(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn,
                                 int32_t topk, int32_t n_local, const void* H, const void* W2,

@@ -145,3 +145,36 @@ def test_full_moe_rank0(oracle):
     tidx = torch.from_numpy(toks).to("cuda:0")
     assert_close(host64(out[tidx]) - inp["out_seed"][toks], ref - inp["out_seed"][toks],
                  "full combine tokens")
+
+
+@pytest.mark.parametrize("T,hidden,ffn,E,nl,topk", [(4096, 1024, 512, 16, 8, 2),
+                                                    (1500, 392, 200, 8, 8, 4)])
+def test_moe_combine_deterministic(oracle, T, hidden, ffn, E, nl, topk):
+    """The combine applies a token's local contributions in expert order
+    without atomics: repeated calls give identical bits, also when every
+    token has up to four local pairs, and the result meets the parity bar."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    say(f"moe combine determinism T={T} hidden={hidden} ffn={ffn} topk={topk}")
+    inp = wl.moe_inputs(T, hidden, ffn, E, nl, topk, BF16, seed=T + topk, zipf_s=1.2)
+    roff, rsp = oracle.moe_route(inp["topk_ids"], 0, nl)
+    Hb = oracle.round_bf16(oracle.moe_layer0(BF16, inp["X"], inp["W1"], rsp, roff, topk))
+    rows = int(roff[-1])
+    Hd = torch.zeros((T * topk, ffn), dtype=torch.bfloat16, device="cuda:0")
+    Hd[:rows] = dev16(Hb, BF16)
+    sp = torch.full((T * topk,), -1, dtype=torch.int32, device="cuda:0")
+    sp[:rows] = _i32(rsp)
+    off = _i32(roff)
+    W2 = dev16(inp["W2"], BF16)
+    wts = devf32(inp["topk_weights"])
+    outs = []
+    for _ in range(3):
+        out = devf32(inp["out_seed"])
+        fm.fm_moe_gemm_scatter(Hd, W2, sp, off, wts, out)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    assert all(np.array_equal(outs[0].view(np.uint32), o.view(np.uint32)) for o in outs[1:])
+    ref = oracle.moe_layer1(BF16, Hb, inp["W2"], inp["topk_ids"], inp["topk_weights"], rsp, roff,
+                            inp["out_seed"], 0)
+    assert_close(outs[0].astype(np.float64) - inp["out_seed"], ref - inp["out_seed"],
+                 "deterministic combine")

@@ -18,7 +18,9 @@
 
 namespace fm {
 
-enum class Mode : int { Gemm = 0, AG = 1, RS = 2 };
+// RS: ReduceScatter epilogue for tiles that never straddle a slice (slice
+// rows a multiple of BM) with plain adds; RSG: any slice size, or atomic adds.
+enum class Mode : int { Gemm = 0, AG = 1, RS = 2, RSG = 3 };
 
 constexpr int kMaxRanks = 16;
 // In-tile byte offsets are 32-bit (tile rows x row pitch), which bounds each
@@ -98,95 +100,95 @@ __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args)
     eng.set_b(args.B, N * 2, n0, N);
     eng.run();
 
-    const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
-    if constexpr (MODE == Mode::RS) {
-      // Epilogue: add the fp32 partial into the owning rank's row slice.
+    // Epilogue through the LDS staging regions: each global access of a wave
+    // covers Eng::EP_RPI whole rows of its sub-tile.
+    eng.ep_begin();
+    const int col = eng.ep_col();
+    const bool col_ok = n0 + col < N;
+    if constexpr (MODE == Mode::RS || MODE == Mode::RSG) {
+      // Add the fp32 partial into the owning rank's row slice.
       const int64_t Ms = args.slice_rows;
       const int s_lo = (int)(m0 / Ms), s_hi = (int)((m_end - 1) / Ms);
-      if (interior && s_lo == s_hi && !args.atomic) {
+      if constexpr (MODE == Mode::RS) {
+        // Common case: the tile lies in one slice.  Uniform base, 32-bit lane
+        // offsets (row < BM, N < 2^22), all loads of a block in flight first.
         float* base = args.dst[s_lo] + (m0 - (int64_t)s_lo * Ms) * N + n0;
-        const uint32_t lane_off = (uint32_t)(eng.out_row(0) * N + eng.out_col(0, 0));
+        // rows of block i, run q are valid while i*32 + q*EP_RPI < lim
+        const int lim = col_ok ? (int)(m_end - m0) - eng.ep_row(0, 0) : 0;
 #pragma unroll
-        for (int i = 0; i < Eng::FM; ++i)
+        for (int i = 0; i < Eng::FM; ++i) {
+          eng.ep_stage(i);
+          float* p0 = base + (uint32_t)(eng.ep_row(i, 0) * (int)N + col);
+          // batches of RB runs: RB loads in flight, then RB stores
+          constexpr int RB = Eng::EP_READS < 4 ? Eng::EP_READS : 4;
 #pragma unroll
-          for (int j = 0; j < Eng::FN; ++j) {
-            // one 32x32 block at a time: 4 loads in flight, then 4 stores
-            eng.pin(i, j);
-            float* p = base + (uint32_t)(i * 32 * N) + lane_off + j * 32;
-            f32x4 old[4];
+          for (int q0 = 0; q0 < Eng::EP_READS; q0 += RB) {
+            f32x4 old[RB];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) old[r] = *reinterpret_cast<const f32x4*>(p + 8 * r);
+            for (int u = 0; u < RB; ++u)
+              if (i * 32 + (q0 + u) * Eng::EP_RPI < lim)
+                old[u] = *reinterpret_cast<const f32x4*>(
+                    p0 + (uint32_t)((q0 + u) * Eng::EP_RPI * (int)N));
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              *reinterpret_cast<f32x4*>(p + 8 * r) = old[r] + eng.out_vals(i, j, r);
+            for (int u = 0; u < RB; ++u) {
+              const f32x4 v = eng.ep_read(q0 + u);
+              if (i * 32 + (q0 + u) * Eng::EP_RPI < lim)
+                *reinterpret_cast<f32x4*>(p0 + (uint32_t)((q0 + u) * Eng::EP_RPI * (int)N)) =
+                    old[u] + v;
+            }
           }
+        }
       } else {
-        for (int s = s_lo; s <= s_hi; ++s) {
-          float* base = args.dst[s];
-          const int64_t r0 = (int64_t)s * Ms, r1 = min(r0 + Ms, M);
+        (void)s_hi;
+        // A tile across slices, or atomic accumulation: slice by slice (a
+        // uniform loop, so each destination base stays scalar), one run at a
+        // time.
+        const int row_l = eng.ep_row(0, 0);
 #pragma unroll
-          for (int i = 0; i < Eng::FM; ++i) {
-            const int64_t row = m0 + eng.out_row(i);
-            const bool rok = row >= r0 && row < r1;
-            float* prow = base + (row - r0) * N;
-#pragma unroll
-            for (int j = 0; j < Eng::FN; ++j) {
-              eng.pin(i, j);
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int64_t col = n0 + eng.out_col(j, r);
-                if (!rok || col >= N) continue;
-                const f32x4 v = eng.out_vals(i, j, r);
-                if (args.atomic) {
-                  unsafeAtomicAdd(prow + col + 0, v[0]);
-                  unsafeAtomicAdd(prow + col + 1, v[1]);
-                  unsafeAtomicAdd(prow + col + 2, v[2]);
-                  unsafeAtomicAdd(prow + col + 3, v[3]);
-                } else {
-                  f32x4* q = reinterpret_cast<f32x4*>(prow + col);
-                  *q = *q + v;
-                }
+        for (int i = 0; i < Eng::FM; ++i) {
+          eng.ep_stage(i);
+          for (int s = s_lo; s <= s_hi; ++s) {
+            const int64_t r0 = (int64_t)s * Ms;
+            // tile-relative row range of slice s, shifted to this lane's rows
+            const int lo = (int)(max(r0, m0) - m0) - row_l - i * 32;
+            const int hi = (int)(min(r0 + Ms, m_end) - m0) - row_l - i * 32;
+            const int64_t off = (m0 - r0 + row_l + i * 32) * N + n0 + col;
+#pragma unroll 1
+            for (int q = 0; q < Eng::EP_READS; ++q) {
+              const int rq = q * Eng::EP_RPI;
+              if (!col_ok || rq < lo || rq >= hi) continue;
+              float* d = args.dst[s] + off + (int64_t)rq * N;
+              const f32x4 v = eng.ep_read(q);
+              if (args.atomic) {
+                unsafeAtomicAdd(d + 0, v[0]);
+                unsafeAtomicAdd(d + 1, v[1]);
+                unsafeAtomicAdd(d + 2, v[2]);
+                unsafeAtomicAdd(d + 3, v[3]);
+              } else {
+                *reinterpret_cast<f32x4*>(d) = *reinterpret_cast<const f32x4*>(d) + v;
               }
             }
           }
         }
       }
     } else {
-      // Epilogue: round (16-bit) or keep (fp32) and store runs of 4 columns.
-      if (interior) {
-        // tile base (uniform) + 32-bit lane offset + per-block constants
-        constexpr int EB = OUT32 ? 4 : 2;
-        char* base = args.C + (m0 * N + n0) * EB;
-        const uint32_t lane_off = (uint32_t)(eng.out_row(0) * N + eng.out_col(0, 0)) * EB;
+      // Round (16-bit) or keep (fp32) and store runs of 4 columns.
+      constexpr int EB = OUT32 ? 4 : 2;
+      char* base = args.C + (m0 * N + n0) * EB;
+      const int lim = col_ok ? (int)(m_end - m0) - eng.ep_row(0, 0) : 0;
 #pragma unroll
-        for (int i = 0; i < Eng::FM; ++i) {
-          char* row_base = base + (uint32_t)(i * 32 * N * EB) + lane_off;
+      for (int i = 0; i < Eng::FM; ++i) {
+        eng.ep_stage(i);
+        char* p0 = base + (uint32_t)(eng.ep_row(i, 0) * (int)N + col) * EB;
 #pragma unroll
-          for (int j = 0; j < Eng::FN; ++j) {
-            eng.pin(i, j);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              store_run<E, OUT32>(row_base, j * 32 + 8 * r, eng.out_vals(i, j, r));
-          }
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < Eng::FM; ++i) {
-          const int64_t row = m0 + eng.out_row(i);
-          if (row >= M) continue;
-#pragma unroll
-          for (int j = 0; j < Eng::FN; ++j) {
-            eng.pin(i, j);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int64_t col = n0 + eng.out_col(j, r);
-              if (col >= N) continue;
-              store_run<E, OUT32>(args.C, row * N + col, eng.out_vals(i, j, r));
-            }
-          }
+        for (int q = 0; q < Eng::EP_READS; ++q) {
+          const f32x4 v = eng.ep_read(q);
+          if (i * 32 + q * Eng::EP_RPI < lim)
+            store_run<E, OUT32>(p0 + (uint32_t)(q * Eng::EP_RPI * (int)N * EB), 0, v);
         }
       }
     }
+    eng.ep_end();
   }
 }
 
@@ -391,5 +393,7 @@ extern "C" fm_status_t fm_gemm_rs(fm_dtype_t dt, int64_t M, int64_t N, int64_t K
     key[tm] = ((s - (rank + 1)) % n_ranks + n_ranks) % n_ranks;
   }
   set_morder(args.order, key);
-  return launch_dense<Mode::RS, false>(dt, cfg, args, stream);
+  if (!atomic && args.slice_rows % cfg.bm == 0)
+    return launch_dense<Mode::RS, false>(dt, cfg, args, stream);
+  return launch_dense<Mode::RSG, false>(dt, cfg, args, stream);
 }

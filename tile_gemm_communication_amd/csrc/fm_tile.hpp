@@ -401,6 +401,10 @@ struct Engine {
   }
   __device__ __forceinline__ void ep_end() { __syncthreads(); }
   __device__ __forceinline__ void ep_stage(int i) {
+    // Keep each block's global traffic after its own staging: without this
+    // fence the compiler hoists the loads of later blocks and spills.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     char* reg = smem + w * (32 * EP_STRIDE) + (lane & 31) * EP_STRIDE + 16 * (lane >> 5);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
