@@ -5,7 +5,9 @@ one MI355X, for one rank's share of a TP=8 / EP=8 layer step.
 One step (all on one GPU, inputs resident in HBM):
   1. AllGather-GEMM, dense MLP layer 0 at TP=8: the rank's own 512 x 12288
      chunk is in place; the other seven chunks are pushed into the gathered
-     buffer by a side stream (fm_chunk_push, per-chunk flags) while
+     buffer by three side streams, peers round-robin, so that arrivals
+     overlap as they do over a full mesh of links (fm_chunk_push, per-chunk
+     flags) while
      fm_ag_gemm computes Output1 = X[4096 x 12288] * W1[12288 x 6144] (fp16).
   2. GEMM-ReduceScatter, dense MLP layer 1: Output1 * W2[6144 x 12288] added
      into eight fp32 [512 x 12288] rank slices (fm_gemm_rs).
@@ -119,7 +121,9 @@ class Workload:
         self.sp = torch.empty(self.T * self.topk, dtype=torch.int32, device=dev)
         self.off = torch.zeros(self.n_local + 1, dtype=torch.int32, device=dev)
 
-        self.side = torch.cuda.Stream(device=dev)
+        # three side streams: with the compute stream that is the four hardware
+        # queues a process gets by default
+        self.sides = [torch.cuda.Stream(device=dev) for _ in range(3)]
         self.serial_arrival = False
         self.order = list(range(self.n))                  # local chunk first, then ring order
         self.flop_ag = 2.0 * self.M * self.N1 * self.K1
@@ -128,18 +132,29 @@ class Workload:
         torch.cuda.synchronize()
 
     # -- pieces of a step ----------------------------------------------------
-    def push_all(self, epoch):
+    def push_all(self, epoch, events=None):
+        """Publish the local chunk and push the seven peer chunks, peer i on
+        side stream i % 3.  events: optional per-chunk events recorded after
+        each push."""
         import tile_gemm_communication_amd as fm
         import torch
         cs = torch.cuda.current_stream()
-        self.side.wait_stream(cs)
-        with torch.cuda.stream(self.side):
-            fm.fm_chunk_push(None, None, self.flags[0:1], self.counters[0:1], epoch,
-                             stream=self.side)
-            for c in self.order[1:]:
-                fm.fm_chunk_push(self.peers[c], self.X[c * self.Mc:(c + 1) * self.Mc],
-                                 self.flags[c:c + 1], self.counters[c:c + 1], epoch,
-                                 stream=self.side)
+        for s in self.sides:
+            s.wait_stream(cs)
+        fm.fm_chunk_push(None, None, self.flags[0:1], self.counters[0:1], epoch,
+                         stream=self.sides[0])
+        for i, c in enumerate(self.order[1:]):
+            s = self.sides[i % len(self.sides)]
+            fm.fm_chunk_push(self.peers[c], self.X[c * self.Mc:(c + 1) * self.Mc],
+                             self.flags[c:c + 1], self.counters[c:c + 1], epoch, stream=s)
+            if events is not None:
+                events[c].record(s)
+
+    def join_sides(self):
+        import torch
+        cs = torch.cuda.current_stream()
+        for s in self.sides:
+            cs.wait_stream(s)
 
     def ag(self, epoch):
         import tile_gemm_communication_amd as fm
@@ -159,18 +174,18 @@ class Workload:
         fm.fm_moe_gemm_scatter(self.H, self.mW2, self.sp, self.off, self.wts, self.mout)
 
     def step(self, evs=None):
-        """One full step on the current stream (+ the side stream for arrival).
+        """One full step on the current stream (+ the side streams for arrival).
         evs: optional list of 5 events bracketing AG | RS | MoE0 | MoE1."""
         import torch
         cs = torch.cuda.current_stream()
         self.epoch += 1
         self.push_all(self.epoch)
         if self.serial_arrival:
-            cs.wait_stream(self.side)
+            self.join_sides()
         if evs: evs[0].record(cs)
         self.ag(self.epoch)
         if evs: evs[1].record(cs)
-        cs.wait_stream(self.side)
+        self.join_sides()
         self.rs()
         if evs: evs[2].record(cs)
         self.moe0()
@@ -217,27 +232,22 @@ def ect_block(w, iters):
         w.epoch += 1
         w.push_all(w.epoch)
         if w.serial_arrival:
-            cs.wait_stream(w.side)
+            w.join_sides()
         w.ag(w.epoch)
-        cs.wait_stream(w.side)
+        w.join_sides()
 
     chunk_ev = [torch.cuda.Event() for _ in range(w.n)]
 
     def naive():
         # the prior-art sequence: one GEMM launch per chunk, each after its chunk
         w.epoch += 1
-        w.side.wait_stream(cs)
-        with torch.cuda.stream(w.side):
-            for c in w.order[1:]:
-                fm.fm_chunk_push(w.peers[c], w.X[c * w.Mc:(c + 1) * w.Mc], w.flags[c:c + 1],
-                                 w.counters[c:c + 1], w.epoch, stream=w.side)
-                chunk_ev[c].record(w.side)
+        w.push_all(w.epoch, events=chunk_ev)
         for c in w.order:
             if c != w.order[0]:
                 cs.wait_event(chunk_ev[c])
             rows = slice(c * w.Mc, (c + 1) * w.Mc)
             fm.fm_gemm(w.X[rows], w.W1, w.Out1[rows])
-        cs.wait_stream(w.side)
+        w.join_sides()
 
     log("ECT: AllGather-GEMM")
     for name, fn in [("nonsplit_fm_gemm", ns_fm), ("nonsplit_hipblaslt", ns_blas),
@@ -391,7 +401,7 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,1)/sqrt(K) weights, log-Zipf router)",
         "config": {
             "workload": "one rank of a TP=8/EP=8 layer step: AllGather-GEMM 4096x6144x12288 "
-                        "(8 chunks of 512 rows, 7 pushed by a side stream) -> GEMM-ReduceScatter "
+                        "(8 chunks of 512 rows, 7 pushed by 3 side streams) -> GEMM-ReduceScatter "
                         "4096x12288x6144 into 8 fp32 slices (fp16); MoE 16384 tokens x 4096, "
                         "64 experts top-2, 8 local, ffn 2816 (bf16)",
             "moe_rows_local": w.rows_local,

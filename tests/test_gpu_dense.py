@@ -47,6 +47,7 @@ def _gemm(A_bits, B_bits, dt, out32=False):
 @pytest.mark.parametrize("dt", [F16, BF16])
 def test_gemm_small(oracle, monkeypatch, tile, shape, dt):
     monkeypatch.setenv("FM_TILE", tile)
+    monkeypatch.setenv("FM_SPLIT_TAIL", "0")
     M, N, K = shape
     say(f"fm_gemm {M}x{N}x{K} dt={dt} tile={tile}")
     A, B = wl.gemm_inputs(M, N, K, dt, seed=M + N + K)
@@ -104,6 +105,7 @@ def test_ag_tiny_random_arrival(oracle, monkeypatch, tile):
     256-row tile spans every chunk.  Equal to the oracle, and bit-identical to
     fm_gemm on the gathered buffer."""
     monkeypatch.setenv("FM_TILE", tile)
+    monkeypatch.setenv("FM_SPLIT_TAIL", "0")
     c = wl.TINY_AG
     chunks, W, order = wl.ag_inputs(c["n_chunks"], c["Mc"], c["N"], c["K"], F16, seed=c["seed"],
                                     arrival="random")
@@ -166,6 +168,7 @@ def _rs(A, W, seeds, dt, rank=0, atomic=False):
 @pytest.mark.parametrize("dt", [F16, BF16])
 def test_rs_small(oracle, monkeypatch, tile, atomic, dt):
     monkeypatch.setenv("FM_TILE", tile)
+    monkeypatch.setenv("FM_SPLIT_TAIL", "0")
     A, W, seeds = wl.rs_inputs(256, 512, 512, 4, dt, seed=401)
     say(f"fm_gemm_rs 256x512x512 P=4 tile={tile} atomic={atomic} dt={dt}")
     got = _rs(A, W, seeds, dt, rank=0, atomic=atomic)
@@ -253,3 +256,39 @@ def test_full_gemm_rs(oracle):
     delta = np.array([got[r // Ms][r % Ms, cc] - seeds[r // Ms][r % Ms, cc]
                       for r, cc in zip(rows, cols)])
     assert_close(delta, ref, "full rs samples")
+
+
+def _cus():
+    import torch
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.parametrize("extra_tiles,K", [(None, 128), (7, 200), (-1, 64)])
+def test_split_tail_bit_identical(oracle, monkeypatch, extra_tiles, K):
+    """A last wave of at most half the CUs runs as 256x128 halves in a second
+    launch.  Per output element the K sum is unchanged, so the result equals
+    the unsplit schedule bit for bit, and the oracle within the parity bar.
+    Shapes: one full wave plus half a wave; one full wave plus 7 tiles (and a
+    ragged K); fewer tiles than half the CUs (halves only)."""
+    import torch
+    G = _cus()
+    if extra_tiles is None:
+        tiles_m, tiles_n = 6, (G + G // 2) // 6
+    elif extra_tiles == -1:
+        tiles_m, tiles_n = 2, max(1, G // 8)
+    else:
+        tiles_m, tiles_n = 1, G + extra_tiles
+    # a ragged last column of tiles; with halves only, its right half lies
+    # wholly past N
+    M, N = 256 * tiles_m, 256 * tiles_n - (192 if extra_tiles == -1 else 8)
+    say(f"split tail {M}x{N}x{K} tiles={tiles_m * tiles_n} cus={G}")
+    monkeypatch.setenv("FM_TILE", "256x256")
+    A, B = wl.gemm_inputs(M, N, K, F16, seed=M + N + K)
+    monkeypatch.setenv("FM_SPLIT_TAIL", "1")
+    C1 = _gemm(A, B, F16)
+    monkeypatch.setenv("FM_SPLIT_TAIL", "0")
+    C0 = _gemm(A, B, F16)
+    assert torch.equal(C1.view(torch.int16), C0.view(torch.int16)), "split tail changed bits"
+    rows, cols = sample_coords(M, N, 2000, seed=5, tile=(256, 128))
+    assert_close(_at(C1, rows, cols), oracle.gemm_entries(F16, A, B, rows, cols),
+                 "split tail samples")

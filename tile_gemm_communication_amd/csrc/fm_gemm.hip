@@ -44,6 +44,9 @@ struct DenseArgs {
   int64_t slice_rows;
   float* dst[kMaxRanks];
   TileOrder order;
+  // This launch covers schedule positions [pos0, pos_end) of `order`, each
+  // split into sub_n tiles of BN columns (order's tiles are sub_n * BN wide).
+  int pos0, pos_end, sub_n;
 };
 
 // Store a run of 4 consecutive outputs at element index idx of C.
@@ -69,13 +72,16 @@ __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args)
   const int slot = xcd_slot(blockIdx.x, G);
   uint64_t ready = 0;
 
-  for (int L = slot; L < args.order.total; L += G) {
+  const int n_pos = (args.pos_end - args.pos0) * args.sub_n;
+  for (int L = slot; L < n_pos; L += G) {
+    const int P = args.pos0 + L / args.sub_n, sub = L % args.sub_n;
     int tm_pos, tn;
-    band_coords(L, args.order.tiles_m, args.order.tiles_n, args.order.group_m, tm_pos, tn);
+    band_coords(P, args.order.tiles_m, args.order.tiles_n, args.order.group_m, tm_pos, tn);
     const int tm = args.order.has_morder ? (int)args.order.morder[tm_pos] : tm_pos;
     const int64_t m0 = (int64_t)tm * BM;
-    const int64_t n0 = (int64_t)tn * BN;
+    const int64_t n0 = ((int64_t)tn * args.sub_n + sub) * BN;
     const int64_t m_end = min(m0 + BM, M);
+    if (n0 >= N) continue;   // a part of an edge tile that lies past N
 
     if constexpr (MODE == Mode::AG) {
       // Tile prologue: wait for every chunk overlapping rows [m0, m_end).
@@ -204,6 +210,16 @@ struct TileCfg {
 
 // Tile shape for an M x N output on G CUs: the fewest full-machine waves of
 // work, weighting smaller tiles by their lower MFMA:load ratio.
+// A last partial wave of at most G/2 256x256 tiles runs as twice as many
+// 256x128 tiles (one wave of half-size tiles instead of a half-empty wave).
+bool split_tail_ok(TileCfg cfg, int64_t tiles, int G) {
+  if (cfg.bn != 256) return false;
+  if (const char* env = std::getenv("FM_SPLIT_TAIL"))
+    if (env[0] == '0') return false;
+  const int64_t rem = tiles % G;
+  return rem > 0 && 2 * rem <= G;
+}
+
 TileCfg choose_tile(int64_t M, int64_t N, int G) {
   if (const char* env = std::getenv("FM_TILE")) {
     int bm = 0, bn = 0, nw = 0;
@@ -219,8 +235,10 @@ TileCfg choose_tile(int64_t M, int64_t N, int G) {
   double best_cost = 1e300;
   for (int c = 0; c < 3; ++c) {
     const int64_t tiles = cdiv(M, cands[c].bm) * cdiv(N, cands[c].bn);
-    const double waves = (double)cdiv(tiles, G);
-    const double cost = waves * cands[c].bm * cands[c].bn / eff[c];
+    const double area = (double)cands[c].bm * cands[c].bn / eff[c];
+    double cost = (double)cdiv(tiles, G) * area;
+    if (split_tail_ok(cands[c], tiles, G))   // last partial wave as 256x128 halves
+      cost = (double)(tiles / G) * area + 256.0 * 128.0 / eff[1];
     if (cost < best_cost * 0.999) {
       best_cost = cost;
       best = cands[c];
@@ -259,10 +277,9 @@ void set_morder(TileOrder& o, const std::vector<int>& key) {
 bool valid_ab(fm_dtype_t dt) { return dt == FM_F16 || dt == FM_BF16; }
 
 template <Mode MODE, bool OUT32>
-fm_status_t launch_dense(fm_dtype_t dt, TileCfg cfg, const DenseArgs& args, hipStream_t stream) {
-  const int G = std::min(args.order.total, device_cu_count());
-  if (G <= 0) return FM_OK;
-  const dim3 grid(G);
+void launch_one(fm_dtype_t dt, TileCfg cfg, const DenseArgs& args, hipStream_t stream) {
+  const int n_pos = (args.pos_end - args.pos0) * args.sub_n;
+  const dim3 grid(std::min(n_pos, device_cu_count()));
 #define FM_LAUNCH(E, BM, BN, NW)                                                              \
   do {                                                                                        \
     if (args.K % kBK) /* ragged K: the 4-wave form keeps the tail path spill-free */          \
@@ -285,6 +302,36 @@ fm_status_t launch_dense(fm_dtype_t dt, TileCfg cfg, const DenseArgs& args, hipS
   if (dt == FM_F16) FM_LAUNCH_E(F16); else FM_LAUNCH_E(BF16);
 #undef FM_LAUNCH_E
 #undef FM_LAUNCH
+}
+
+// One launch over the whole schedule, or -- when the last wave would be at
+// most half full -- the full waves first, then the remaining 256x256 tiles as
+// 256x128 halves in a second launch on the same stream.  Each output element
+// is still summed over K by one workgroup in the same order, so the split
+// does not change a single bit of the result.
+template <Mode MODE, bool OUT32>
+fm_status_t launch_dense(fm_dtype_t dt, TileCfg cfg, DenseArgs& args, hipStream_t stream) {
+  const int T = args.order.total;
+  if (T <= 0) return FM_OK;
+  const int G = device_cu_count();
+  if (split_tail_ok(cfg, T, G)) {
+    const int full = T - T % G;
+    if (full > 0) {
+      args.pos0 = 0;
+      args.pos_end = full;
+      args.sub_n = 1;
+      launch_one<MODE, OUT32>(dt, cfg, args, stream);
+    }
+    args.pos0 = full;
+    args.pos_end = T;
+    args.sub_n = 2;
+    launch_one<MODE, OUT32>(dt, TileCfg{cfg.bm, 128, 4}, args, stream);
+  } else {
+    args.pos0 = 0;
+    args.pos_end = T;
+    args.sub_n = 1;
+    launch_one<MODE, OUT32>(dt, cfg, args, stream);
+  }
   return launch_status();
 }
 

@@ -7,6 +7,8 @@
 // the FlagCX guide ("flagcxPutSignal": write the data, then bump the remote
 // signal) and the push mode of the FLUX review ("拉取 vs 推送数据传输"), with
 // the peer's buffer being local HBM on one GPU.
+#include <algorithm>
+
 #include "fm_common.hpp"
 
 namespace fm {
@@ -27,7 +29,10 @@ __global__ __launch_bounds__(256) void push_kernel(const u32x4* __restrict__ src
     dst[i + 768] = d;
   }
   for (; i < end; i += 256) dst[i] = src[i];
-  __threadfence();   // this thread's stores are visible device-wide
+  // Every wave waits until its stores are acknowledged by L2; after the
+  // barrier one release (a single L2 write-back per workgroup rather than one
+  // per thread) makes the workgroup's stores visible device-wide.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t prev =
@@ -56,7 +61,13 @@ extern "C" fm_status_t fm_chunk_push(const void* src, void* dst, int64_t bytes, 
     if (s < d + bytes && d < s + bytes) return FM_ERR_INVALID_ARG;   // overlap
   }
   const int64_t n16 = bytes / 16;
-  int wg = n_workgroups > 0 ? n_workgroups : 64;
+  // Default: one workgroup per 64 KiB, at most two per CU.  Each thread keeps
+  // four 16-byte loads in flight, so a grid of G workgroups has G * 16 KiB in
+  // flight; a few MiB in flight are needed to approach HBM bandwidth.
+  int wg = n_workgroups > 0
+               ? n_workgroups
+               : (int)std::min<int64_t>(std::max<int64_t>(cdiv(bytes, 65536), 1),
+                                        2 * (int64_t)device_cu_count());
   if (n16 == 0) wg = 1;
   else if (wg > cdiv(n16, 256)) wg = (int)cdiv(n16, 256);
   hipLaunchKernelGGL(push_kernel, dim3(wg), dim3(256), 0, stream, (const u32x4*)src, (u32x4*)dst,
