@@ -39,6 +39,27 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = 2516.6          # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+
+# HBM bytes per launch of each step kernel, from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE runs of `bench.py --steps 2 --warmup 1 --no-ect --no-cpu-baseline
+# --serial-arrival` (KiB per dispatch, averaged), scaled by the factors a
+# known-size copy (`bench.py --copy-probe 256`) gives: FETCH_SIZE x2.0,
+# WRITE_SIZE x1.0.  Keyed by the digest of the kernel sources they were taken
+# on: after any change to csrc/ they no longer apply and traffic is null.
+TRAFFIC_DIGEST = ""
+TRAFFIC_BYTES = {}            # op name -> (read bytes, written bytes) per launch
+
+
+def source_digest() -> str:
+    """sha256 over the library's kernel sources (names and contents)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "tile_gemm_communication_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 METRIC = "fused AG/RS-GEMM TFLOP/s & % MFMA peak; ECT vs non-split GEMM"
 
 
@@ -54,7 +75,7 @@ def parse():
     ap.add_argument("--ect-iters", type=int, default=20)
     ap.add_argument("--no-ect", action="store_true", help="skip the ECT comparisons")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2048,
+    ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of the AllGather-GEMM the CPU oracle computes as its sample")
     ap.add_argument("--serial-arrival", action="store_true",
                     help="let every chunk land before fm_ag_gemm starts (for profilers that "
@@ -299,6 +320,16 @@ def ect_block(w, iters):
     return res
 
 
+def traffic(op):
+    """Measured HBM bytes per launch of `op` (read + written); traffic is None
+    when the kernel sources changed since the counters were taken."""
+    if op not in TRAFFIC_BYTES or source_digest() != TRAFFIC_DIGEST:
+        return {"traffic": None}
+    rd, wr = TRAFFIC_BYTES[op]
+    return {"traffic": rd + wr, "traffic_read": rd, "traffic_write": wr,
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0)"}
+
+
 def cpu_baseline(w, rows):
     """The CPU oracle, untuned, on a bounded sample of the AllGather-GEMM:
     `rows` output rows of Output1 = X * W1 (fp64 accumulation)."""
@@ -410,7 +441,7 @@ def main():
         "ops": ops,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_TFLOPS, 4), **traffic(dom)},
     }
     if not args.no_ect:
         out["ect"] = ect_block(w, args.ect_iters)
