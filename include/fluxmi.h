@@ -156,7 +156,11 @@ fm_status_t fm_gemm_rs(fm_dtype_t dt, int64_t M, int64_t N, int64_t K, int32_t n
  *                 [0, expert_offsets[n_local]) hold the local pair ids stably
  *                 sorted by expert (increasing pair id within an expert); the
  *                 rest is left untouched.
- * Deterministic: identical bits on every call.
+ * Deterministic: identical bits on every call.  The per-chunk histograms of
+ * the counting sort use the library's per-device counter buffer (see
+ * fm_moe_gemm_scatter; FM_ERR_HIP if its first allocation fails): route
+ * calls (also those inside fm_moe_gather_gemm) on one device must not
+ * overlap in time.
  */
 fm_status_t fm_moe_route(int64_t T, int32_t topk, int32_t expert_begin, int32_t n_local,
                          const int32_t* topk_ids, int32_t* sorted_pairs,

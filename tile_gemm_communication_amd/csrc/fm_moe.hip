@@ -1,5 +1,5 @@
 // fm_moe.hip -- the MoE path of one expert-parallel rank:
-//   route   expert-sorted row index (counting sort, stable, deterministic)
+//   route   expert-sorted row index (chunked counting sort, stable, deterministic)
 //   layer 0 token gather fused into a grouped (per-expert, ragged-M) GEMM
 //   layer 1 grouped GEMM with the top-k weighted scatter-reduce fused into
 //           its epilogue (fp32 atomic adds into the token rows)
@@ -20,84 +20,101 @@ namespace fm {
 
 constexpr int kMaxLocalExperts = 64;
 constexpr int kRouteThreads = 256;
-constexpr int kRouteSeg = 16;                         // pairs per thread per chunk
-constexpr int kRouteChunk = kRouteThreads * kRouteSeg;
+constexpr int kRouteWaves = kRouteThreads / 64;
+// Per-chunk expert counts live in the library's tile-counter buffer, in the
+// half the combine does not use.
+constexpr int kRouteScratch0 = kTileCounters / 2;
+constexpr int kRouteScratchN = kTileCounters - kRouteScratch0;
 
 // ---------------------------------------------------------------------------
-// Route: one workgroup.  Pass 1 counts local pairs per expert; the exclusive
-// scan of the counts gives expert_offsets.  Pass 2 walks the pairs in chunks
-// of kRouteChunk; inside a chunk thread t owns the contiguous pairs
-// [t*kRouteSeg, (t+1)*kRouteSeg), so ordering slots by (expert, chunk, thread,
-// position) is ordering by (expert, pair id): a stable sort.
+// Route: a counting sort over chunks of `ch` consecutive pairs, one
+// workgroup per chunk.
+//   count: per-chunk histogram of local experts.
+//   place: every workgroup derives its chunk's first slot per expert from
+//          the histograms (totals -> expert_offsets, plus the counts of the
+//          earlier chunks), then walks its chunk in rounds of 256 pairs in
+//          pair order.  Within a round a pair's rank among same-expert pairs
+//          of its wave comes from a ballot, and earlier waves' counts come
+//          from LDS, so slots follow pair order: the sort is stable.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids,
-                                                               int64_t P, int e0, int n_local,
-                                                               int32_t* __restrict__ sorted_pairs,
-                                                               int32_t* __restrict__ offsets) {
-  __shared__ int s_cnt[kMaxLocalExperts * kRouteThreads];   // [expert][thread]
-  __shared__ int s_base[kMaxLocalExperts];
-  __shared__ int s_tot[kMaxLocalExperts];
-  __shared__ signed char s_e[kRouteChunk];
+__global__ __launch_bounds__(kRouteThreads) void route_count_kernel(
+    const int32_t* __restrict__ ids, int64_t P, int e0, int n_local, int64_t ch,
+    uint32_t* __restrict__ counts) {
+  __shared__ int s_cnt[kMaxLocalExperts];
   const int t = threadIdx.x;
-
-  // Pass 1: totals per expert.
-  if (t < n_local) s_tot[t] = 0;
+  if (t < n_local) s_cnt[t] = 0;
   __syncthreads();
-  for (int64_t p = t; p < P; p += kRouteThreads) {
+  const int64_t p0 = (int64_t)blockIdx.x * ch, p1 = min(p0 + ch, P);
+  for (int64_t p = p0 + t; p < p1; p += kRouteThreads) {
     const int e = ids[p] - e0;
-    if (e >= 0 && e < n_local) atomicAdd(&s_tot[e], 1);
+    if (e >= 0 && e < n_local) atomicAdd(&s_cnt[e], 1);
+  }
+  __syncthreads();
+  if (t < n_local) counts[(int64_t)blockIdx.x * n_local + t] = (uint32_t)s_cnt[t];
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_place_kernel(
+    const int32_t* __restrict__ ids, int64_t P, int e0, int n_local, int64_t ch, int n_chunks,
+    const uint32_t* __restrict__ counts, int32_t* __restrict__ sorted_pairs,
+    int32_t* __restrict__ offsets) {
+  __shared__ int s_base[kMaxLocalExperts];            // next slot per expert
+  __shared__ int s_tot[kMaxLocalExperts];
+  __shared__ int s_wcnt[kRouteWaves][kMaxLocalExperts];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int c = blockIdx.x;
+  if (t < n_local) {
+    int tot = 0, pre = 0;
+    for (int cc = 0; cc < n_chunks; ++cc) {
+      const int v = (int)counts[(int64_t)cc * n_local + t];
+      pre += cc < c ? v : 0;
+      tot += v;
+    }
+    s_tot[t] = tot;
+    s_base[t] = pre;
   }
   __syncthreads();
   if (t == 0) {
     int acc = 0;
     for (int e = 0; e < n_local; ++e) {
-      s_base[e] = acc;
-      offsets[e] = acc;
+      s_base[e] += acc;
+      if (c == 0) offsets[e] = acc;
       acc += s_tot[e];
     }
-    offsets[n_local] = acc;
+    if (c == 0) offsets[n_local] = acc;
   }
-  __syncthreads();
-
-  // Pass 2: stable placement, chunk by chunk.
-  for (int64_t c0 = 0; c0 < P; c0 += kRouteChunk) {
-    for (int i = t; i < kRouteChunk; i += kRouteThreads) {
-      const int64_t p = c0 + i;
-      int e = -1;
-      if (p < P) {
-        e = ids[p] - e0;
-        if (e < 0 || e >= n_local) e = -1;
-      }
-      s_e[i] = (signed char)e;
-    }
-    for (int e = 0; e < n_local; ++e) s_cnt[e * kRouteThreads + t] = 0;
+  const int64_t p0 = (int64_t)c * ch, p1 = min(p0 + ch, P);
+  for (int64_t r0 = p0; r0 < p1; r0 += kRouteThreads) {
+    if (t < kRouteWaves * kMaxLocalExperts) (&s_wcnt[0][0])[t] = 0;
     __syncthreads();
-    for (int i = 0; i < kRouteSeg; ++i) {
-      const int e = s_e[t * kRouteSeg + i];
-      if (e >= 0) s_cnt[e * kRouteThreads + t] += 1;
+    const int64_t p = r0 + t;
+    int e = -1;
+    if (p < p1) {
+      e = ids[p] - e0;
+      if (e < 0 || e >= n_local) e = -1;
     }
-    __syncthreads();
-    if (t < n_local) {   // exclusive scan over threads for expert t
-      int acc = 0;
-      for (int u = 0; u < kRouteThreads; ++u) {
-        const int v = s_cnt[t * kRouteThreads + u];
-        s_cnt[t * kRouteThreads + u] = acc;
-        acc += v;
-      }
-      s_tot[t] = acc;
+    // rank among the earlier lanes of this wave with the same expert
+    int rank = 0;
+    uint64_t todo = __ballot(e >= 0);
+    while (todo) {
+      const int le = __shfl(e, __ffsll((unsigned long long)todo) - 1);
+      const uint64_t m = __ballot(e == le);
+      if (e == le) rank = __popcll(m & ((1ull << lane) - 1));
+      if (lane == 0) s_wcnt[w][le] = __popcll(m);
+      todo &= ~m;
     }
     __syncthreads();
-    for (int i = 0; i < kRouteSeg; ++i) {
-      const int e = s_e[t * kRouteSeg + i];
-      if (e >= 0) {
-        const int slot = s_base[e] + s_cnt[e * kRouteThreads + t];
-        s_cnt[e * kRouteThreads + t] += 1;
-        sorted_pairs[slot] = (int32_t)(c0 + t * kRouteSeg + i);
-      }
+    if (e >= 0) {
+      int slot = s_base[e] + rank;
+      for (int v = 0; v < w; ++v) slot += s_wcnt[v][e];
+      sorted_pairs[slot] = (int32_t)p;
     }
     __syncthreads();
-    if (t < n_local) s_base[t] += s_tot[t];
-    __syncthreads();
+    if (t < n_local) {
+      int add = 0;
+      for (int v = 0; v < kRouteWaves; ++v) add += s_wcnt[v][t];
+      s_base[t] += add;
+    }
+    __syncthreads();   // s_wcnt is cleared for the next round
   }
 }
 
@@ -317,8 +334,18 @@ extern "C" fm_status_t fm_moe_route(int64_t T, int32_t topk, int32_t expert_begi
   const fm_status_t st =
       check_route_args(T, topk, n_local, topk_ids, sorted_pairs, expert_offsets);
   if (st != FM_OK) return st;
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, topk_ids, T * topk,
-                     (int)expert_begin, (int)n_local, sorted_pairs, expert_offsets);
+  const int64_t P = T * topk;
+  int64_t ch = 2048;   // pairs per workgroup; the chunk histograms must fit the scratch
+  while (std::max<int64_t>(1, cdiv(P, ch)) * n_local > kRouteScratchN) ch *= 2;
+  const int n_chunks = (int)std::max<int64_t>(1, cdiv(P, ch));
+  uint32_t* counts = device_tile_counters();
+  if (!counts) return FM_ERR_HIP;
+  counts += kRouteScratch0;
+  hipLaunchKernelGGL(route_count_kernel, dim3(n_chunks), dim3(kRouteThreads), 0, stream,
+                     topk_ids, P, (int)expert_begin, (int)n_local, ch, counts);
+  hipLaunchKernelGGL(route_place_kernel, dim3(n_chunks), dim3(kRouteThreads), 0, stream,
+                     topk_ids, P, (int)expert_begin, (int)n_local, ch, n_chunks,
+                     (const uint32_t*)counts, sorted_pairs, expert_offsets);
   return launch_status();
 }
 
