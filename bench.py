@@ -85,6 +85,9 @@ def parse():
     ap.add_argument("--serial-arrival", action="store_true",
                     help="let every chunk land before fm_ag_gemm starts (for profilers that "
                          "serialise kernel dispatches, where a concurrent arrival cannot happen)")
+    ap.add_argument("--arrival", choices=("kernel", "dma"), default="kernel",
+                    help="emulated peer push: fm_chunk_push (copy kernel) or "
+                         "fm_chunk_push_dma (copy engines, no compute units)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run fm_chunk_push over MIB MiB three times and exit: the "
                          "known-size copy that calibrates the HBM byte counters")
@@ -151,6 +154,8 @@ class Workload:
         # queues a process gets by default
         self.sides = [torch.cuda.Stream(device=dev) for _ in range(3)]
         self.serial_arrival = False
+        self.arrival = "kernel"
+        self.n_sides = len(self.sides)
         self.order = list(range(self.n))                  # local chunk first, then ring order
         self.flop_ag = 2.0 * self.M * self.N1 * self.K1
         self.flop_rs = 2.0 * self.M * self.N2 * self.K2
@@ -167,12 +172,16 @@ class Workload:
         cs = torch.cuda.current_stream()
         for s in self.sides:
             s.wait_stream(cs)
-        fm.fm_chunk_push(None, None, self.flags[0:1], self.counters[0:1], epoch,
-                         stream=self.sides[0])
+        def push(src, dst, c, s):
+            if self.arrival == "dma":
+                fm.fm_chunk_push_dma(src, dst, self.flags[c:c + 1], epoch, stream=s)
+            else:
+                fm.fm_chunk_push(src, dst, self.flags[c:c + 1], self.counters[c:c + 1], epoch,
+                                 stream=s)
+        push(None, None, 0, self.sides[0])
         for i, c in enumerate(self.order[1:]):
-            s = self.sides[i % len(self.sides)]
-            fm.fm_chunk_push(self.peers[c], self.X[c * self.Mc:(c + 1) * self.Mc],
-                             self.flags[c:c + 1], self.counters[c:c + 1], epoch, stream=s)
+            s = self.sides[i % self.n_sides]
+            push(self.peers[c], self.X[c * self.Mc:(c + 1) * self.Mc], c, s)
             if events is not None:
                 events[c].record(s)
 
@@ -390,6 +399,7 @@ def main():
         return
     w = Workload()
     w.serial_arrival = args.serial_arrival
+    w.arrival = args.arrival
     cs = torch.cuda.current_stream()
 
     log(f"warmup {args.warmup} steps")
@@ -441,6 +451,7 @@ def main():
                         "4096x12288x6144 into 8 fp32 slices (fp16); MoE 16384 tokens x 4096, "
                         "64 experts top-2, 8 local, ffn 2816 (bf16)",
             "moe_rows_local": w.rows_local,
+            "arrival": f"{args.arrival} pushes, 3 side streams",
             "step_flop": total_flop,
         },
         "ops": ops,

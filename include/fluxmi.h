@@ -125,6 +125,21 @@ fm_status_t fm_chunk_push(const void* src, void* dst, int64_t bytes, uint32_t* f
                           hipStream_t stream);
 
 /*
+ * fm_chunk_push_dma -- the same producer step on the copy engines: an
+ * asynchronous device-to-device copy that uses no compute units, followed on
+ * `stream` by a write of epoch into *flag made once the copy has completed.
+ * This is how a peer's DMA engine delivers a chunk over a link and then rings
+ * the signal (the review's push mode in "拉取 vs 推送数据传输"; the FlagCX
+ * guide's put-with-signal), so the consumer's compute units are not spent on
+ * the emulated transfer.
+ *   bytes  multiple of 16 (0 = write the flag only); src/dst 16-byte aligned
+ *          and non-overlapping; flag 4-byte aligned device memory.
+ * Returns FM_ERR_HIP if the runtime rejects the copy or the flag write.
+ */
+fm_status_t fm_chunk_push_dma(const void* src, void* dst, int64_t bytes, uint32_t* flag,
+                              uint32_t epoch, hipStream_t stream);
+
+/*
  * fm_gemm_rs -- Output2 = ReduceScatter(GEMM(Output1, W2)), this rank's part
  * (FLUX review, "MLP 前向传播" second GEMM and "ReduceScatter 重叠").
  *   A        [M, K] (K = this rank's shard of the reduction), W [K, N].

@@ -98,10 +98,11 @@ class Arrival:
     def poison(self):
         self.X.fill_(float("nan"))
 
-    def push(self, order, epoch, delay_cycles=0, skip=(), local=None):
+    def push(self, order, epoch, delay_cycles=0, skip=(), local=None, dma=False):
         """Enqueue pushes of chunks in `order` on the side stream (after the
         current stream's work).  `local` is published without a copy (the
-        rank's own chunk, already in place); chunks in `skip` never arrive."""
+        rank's own chunk, already in place); chunks in `skip` never arrive.
+        dma: copy on the copy engines (fm_chunk_push_dma) instead of a kernel."""
         import torch
         import tile_gemm_communication_amd as fm
         if local is not None:   # the rank's own chunk is already in place
@@ -115,12 +116,13 @@ class Arrival:
                 if c in skip:
                     continue
                 rows = slice(c * self.Mc, (c + 1) * self.Mc)
-                if local is not None and c == local:
-                    fm.fm_chunk_push(None, None, self.flags[c:c + 1], self.counters[c:c + 1],
-                                     epoch, stream=self.side)
+                src, dst = (None, None) if local is not None and c == local else \
+                    (self.peers[c], self.X[rows])
+                if dma:
+                    fm.fm_chunk_push_dma(src, dst, self.flags[c:c + 1], epoch, stream=self.side)
                 else:
-                    fm.fm_chunk_push(self.peers[c], self.X[rows], self.flags[c:c + 1],
-                                     self.counters[c:c + 1], epoch, stream=self.side)
+                    fm.fm_chunk_push(src, dst, self.flags[c:c + 1], self.counters[c:c + 1],
+                                     epoch, stream=self.side)
 
     def join(self):
         import torch

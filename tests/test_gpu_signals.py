@@ -56,6 +56,36 @@ def test_push_copies_and_publishes():
         assert flag.item() == 10 + wg and counter.item() == 0
 
 
+def test_push_dma_copies_and_publishes():
+    import torch
+    import tile_gemm_communication_amd as fm
+    src = torch.randint(-30000, 30000, (3 << 20,), dtype=torch.int16, device="cuda:0")
+    dst = torch.zeros_like(src)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    for e in (5, 6):
+        dst.zero_()
+        fm.fm_chunk_push_dma(src, dst, flag, epoch=e)
+        torch.cuda.synchronize()
+        assert torch.equal(src, dst) and flag.item() == e
+    fm.fm_chunk_push_dma(None, None, flag, epoch=9)
+    torch.cuda.synchronize()
+    assert flag.item() == 9
+
+
+@pytest.mark.parametrize("delay", [0, 5_000_000])
+def test_dma_arrival_bit_identical(delay):
+    """Chunks delivered by the copy engines with a flag write behind each: the
+    fused kernel waits for them and reproduces the non-split GEMM's bits."""
+    chunks, W, order = wl.ag_inputs(8, 256, 768, 1024, F16, seed=905, arrival="random")
+    arr = Arrival(chunks, F16, 1024)
+    Wd = dev16(W, F16)
+    arr.poison()
+    say(f"dma arrival delay={delay}")
+    C = _ag(arr, Wd, 768, order, arr.next_epoch(), delay_cycles=delay, dma=True)
+    assert arr.err.item() == 0
+    assert np.array_equal(bits16(C), _reference(arr, Wd, 768))
+
+
 def test_late_arrival_is_waited_for():
     """Chunks are pushed only after a ~ms spin on the side stream while the
     gathered buffer holds NaN: the fused kernel must wait and still produce

@@ -118,6 +118,16 @@ def test_chunk_push_validation():
     assert L.fm_chunk_push(P, P2, 64, P3, None, 1, 0, None) == fm.FM_ERR_INVALID_ARG
 
 
+def test_chunk_push_dma_validation():
+    L = fm.lib()
+    assert L.fm_chunk_push_dma(P, P2, 100, P3, 1, None) == fm.FM_ERR_INVALID_ARG   # 16 B
+    assert L.fm_chunk_push_dma(P, P, 4096, P3, 1, None) == fm.FM_ERR_INVALID_ARG   # overlap
+    assert L.fm_chunk_push_dma(P, P2, 64, None, 1, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_chunk_push_dma(P, P2, 64, ctypes.c_void_p(0x30002), 1, None) == \
+        fm.FM_ERR_INVALID_ARG   # flag alignment
+    assert L.fm_chunk_push_dma(None, P2, 64, P3, 1, None) == fm.FM_ERR_INVALID_ARG
+
+
 def test_oracle_is_not_reachable_from_the_product():
     pkg = os.path.join(ROOT, "tile_gemm_communication_amd")
     for dirpath, _, files in os.walk(pkg):

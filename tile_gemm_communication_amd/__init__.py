@@ -21,6 +21,7 @@ FM_OK, FM_ERR_INVALID_ARG, FM_ERR_UNSUPPORTED, FM_ERR_HIP, FM_ERR_TIMEOUT = rang
 FM_F16, FM_BF16, FM_F32 = 0, 1, 2
 
 EXPORTS = ("fm_version", "fm_status_str", "fm_gemm", "fm_ag_gemm", "fm_chunk_push",
+           "fm_chunk_push_dma",
            "fm_gemm_rs", "fm_moe_route", "fm_moe_gather_gemm", "fm_moe_gemm_scatter")
 
 
@@ -54,6 +55,8 @@ def lib() -> ctypes.CDLL:
     L.fm_ag_gemm.argtypes = [ctypes.c_int, i64, i64, i64, i32, p, p, p, p, u32, p, p, i64, p]
     L.fm_chunk_push.restype = ctypes.c_int
     L.fm_chunk_push.argtypes = [p, p, i64, p, p, u32, i32, p]
+    L.fm_chunk_push_dma.restype = ctypes.c_int
+    L.fm_chunk_push_dma.argtypes = [p, p, i64, p, u32, p]
     L.fm_gemm_rs.restype = ctypes.c_int
     L.fm_gemm_rs.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, p, p, p, i32, p]
     L.fm_moe_route.restype = ctypes.c_int
@@ -155,6 +158,16 @@ def fm_chunk_push(src, dst, flag, counter, epoch: int, n_workgroups: int = 0,
         _ptr(src) if nbytes else None, _ptr(dst) if nbytes else None, nbytes, _ptr(flag),
         _ptr(counter), ctypes.c_uint32(epoch & 0xFFFFFFFF), int(n_workgroups),
         _stream(stream)))
+
+
+def fm_chunk_push_dma(src, dst, flag, epoch: int, stream=None) -> None:
+    """Copy src into dst on the copy engines, then write flag = epoch."""
+    nbytes = src.numel() * src.element_size() if src is not None else 0
+    if src is not None and dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("fm_chunk_push_dma: dst smaller than src")
+    _check("fm_chunk_push_dma", lib().fm_chunk_push_dma(
+        _ptr(src) if nbytes else None, _ptr(dst) if nbytes else None, nbytes, _ptr(flag),
+        ctypes.c_uint32(epoch & 0xFFFFFFFF), _stream(stream)))
 
 
 def fm_gemm_rs(A, W, dst, rank: int, atomic: bool = False, stream=None) -> None:

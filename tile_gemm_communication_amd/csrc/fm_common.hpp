@@ -61,6 +61,11 @@ int device_cu_count();
 // allocation fails.
 constexpr int kTileCounters = 32768;
 uint32_t* device_tile_counters();
+// Layout of the counter buffer, one region per user so that different
+// operators may overlap in time (calls of one operator on one device may not):
+constexpr int kColDone0 = 0, kColDoneN = 16384;            // MoE combine, per N column
+constexpr int kRoute0 = kColDoneN;                          // route chunk histograms
+constexpr int kRouteN = kTileCounters - kRoute0;
 
 // Translate the last HIP launch error into a status.
 inline fm_status_t launch_status() {

@@ -60,6 +60,46 @@ __device__ __forceinline__ void store_run(char* C, int64_t idx, const f32x4& v) 
   }
 }
 
+// Point the engine's DMA at the A rows [m0, m0+BM) (clamped to M) and the B
+// columns [n0, n0+BN) of one tile.
+template <class Eng>
+__device__ __forceinline__ void setup_operands(Eng& eng, const DenseArgs& args, int64_t m0,
+                                               int64_t n0) {
+  const int64_t M = args.M, N = args.N, K = args.K;
+  eng.set_a_base(args.A + m0 * K * 2);
+#pragma unroll
+  for (int i = 0; i < Eng::A_DMA; ++i) {
+    const int64_t row = min(m0 + eng.a_dma_row(i), M - 1);
+    eng.set_a(i, (uint32_t)((row - m0) * K * 2));
+  }
+  eng.set_b(args.B, N * 2, n0, N);
+}
+
+// Store epilogue (between ep_begin and ep_end): round to 16 bits (or keep
+// fp32) and store runs of 4 columns, a wave covering whole rows per access.
+template <class E, bool OUT32, class Eng>
+__device__ __forceinline__ void store_tile(Eng& eng, const DenseArgs& args, int64_t m0,
+                                           int64_t n0) {
+  const int64_t M = args.M, N = args.N;
+  const int64_t m_end = min(m0 + Eng::BM_, M);
+  const int col = eng.ep_col();
+  const bool col_ok = n0 + col < N;
+  constexpr int EB = OUT32 ? 4 : 2;
+  char* base = args.C + (m0 * N + n0) * EB;
+  const int lim = col_ok ? (int)(m_end - m0) - eng.ep_row(0, 0) : 0;
+#pragma unroll
+  for (int i = 0; i < Eng::FM; ++i) {
+    eng.ep_stage(i);
+    char* p0 = base + (uint32_t)(eng.ep_row(i, 0) * (int)N + col) * EB;
+#pragma unroll
+    for (int q = 0; q < Eng::EP_READS; ++q) {
+      const f32x4 v = eng.ep_read(q);
+      if (i * 32 + q * Eng::EP_RPI < lim)
+        store_run<E, OUT32>(p0 + (uint32_t)(q * Eng::EP_RPI * (int)N * EB), 0, v);
+    }
+  }
+}
+
 template <class E, int BM, int BN, int NW, Mode MODE, bool OUT32, bool KTAIL>
 __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args) {
   using Eng = Engine<E, BM, BN, KTAIL, NW>;
@@ -97,13 +137,7 @@ __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args)
       if (abort_now) return;
     }
 
-    eng.set_a_base(args.A + m0 * K * 2);
-#pragma unroll
-    for (int i = 0; i < Eng::A_DMA; ++i) {
-      const int64_t row = min(m0 + eng.a_dma_row(i), M - 1);
-      eng.set_a(i, (uint32_t)((row - m0) * K * 2));
-    }
-    eng.set_b(args.B, N * 2, n0, N);
+    setup_operands(eng, args, m0, n0);
     eng.run();
 
     // Epilogue through the LDS staging regions: each global access of a wave
@@ -178,21 +212,7 @@ __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args)
         }
       }
     } else {
-      // Round (16-bit) or keep (fp32) and store runs of 4 columns.
-      constexpr int EB = OUT32 ? 4 : 2;
-      char* base = args.C + (m0 * N + n0) * EB;
-      const int lim = col_ok ? (int)(m_end - m0) - eng.ep_row(0, 0) : 0;
-#pragma unroll
-      for (int i = 0; i < Eng::FM; ++i) {
-        eng.ep_stage(i);
-        char* p0 = base + (uint32_t)(eng.ep_row(i, 0) * (int)N + col) * EB;
-#pragma unroll
-        for (int q = 0; q < Eng::EP_READS; ++q) {
-          const f32x4 v = eng.ep_read(q);
-          if (i * 32 + q * Eng::EP_RPI < lim)
-            store_run<E, OUT32>(p0 + (uint32_t)(q * Eng::EP_RPI * (int)N * EB), 0, v);
-        }
-      }
+      store_tile<E, OUT32>(eng, args, m0, n0);
     }
     eng.ep_end();
   }

@@ -21,10 +21,10 @@ namespace fm {
 constexpr int kMaxLocalExperts = 64;
 constexpr int kRouteThreads = 256;
 constexpr int kRouteWaves = kRouteThreads / 64;
-// Per-chunk expert counts live in the library's tile-counter buffer, in the
-// half the combine does not use.
-constexpr int kRouteScratch0 = kTileCounters / 2;
-constexpr int kRouteScratchN = kTileCounters - kRouteScratch0;
+// Per-chunk expert counts live in the route region of the library's
+// tile-counter buffer.
+constexpr int kRouteScratch0 = kRoute0;
+constexpr int kRouteScratchN = kRouteN;
 
 // ---------------------------------------------------------------------------
 // Route: a counting sort over chunks of `ch` consecutive pairs, one
@@ -284,9 +284,10 @@ fm_status_t launch_moe(fm_dtype_t dt, MoeTile cfg, MoeArgs& a, hipStream_t strea
   a.group_m = 8;
   a.spin_limit = 1ll << 26;
   if (SCATTER) {
-    if (a.tiles_n > kTileCounters) return FM_ERR_UNSUPPORTED;
+    if (a.tiles_n > kColDoneN) return FM_ERR_UNSUPPORTED;
     a.col_done = device_tile_counters();
     if (!a.col_done) return FM_ERR_HIP;
+    a.col_done += kColDone0;
   }
   const dim3 grid(device_cu_count());
 #define FM_LAUNCH(E, BM, BN, NW)                                                             \

@@ -74,3 +74,20 @@ extern "C" fm_status_t fm_chunk_push(const void* src, void* dst, int64_t bytes, 
                      n16, flag, counter, epoch);
   return launch_status();
 }
+
+extern "C" fm_status_t fm_chunk_push_dma(const void* src, void* dst, int64_t bytes,
+                                         uint32_t* flag, uint32_t epoch, hipStream_t stream) {
+  if (!flag || bytes < 0 || bytes % 16 || (reinterpret_cast<uintptr_t>(flag) & 3u))
+    return FM_ERR_INVALID_ARG;
+  if (bytes > 0 && (!src || !dst || !aligned16(src) || !aligned16(dst))) return FM_ERR_INVALID_ARG;
+  if (bytes > 0) {
+    const char* s = (const char*)src;
+    const char* d = (const char*)dst;
+    if (s < d + bytes && d < s + bytes) return FM_ERR_INVALID_ARG;   // overlap
+    if (hipMemcpyAsync(dst, src, (size_t)bytes, hipMemcpyDeviceToDeviceNoCU, stream) !=
+        hipSuccess)
+      return FM_ERR_HIP;
+  }
+  if (hipStreamWriteValue32(stream, flag, epoch, 0) != hipSuccess) return FM_ERR_HIP;
+  return FM_OK;
+}

@@ -89,6 +89,7 @@ template <class E, int BM, int BN, bool KTAIL, int NW = 4, int BSWZ = 4>
 struct Engine {
   static constexpr int NWM = 2, NWN = NW / 2;          // wave grid over the tile
   static constexpr int THREADS = 64 * NW;
+  static constexpr int BM_ = BM, BN_ = BN;
   static constexpr int WM = BM / NWM, WN = BN / NWN;
   static constexpr int FM = WM / 32, FN = WN / 32;     // 32x32 blocks per wave
   static constexpr int A_STAGE = BM * 128;
