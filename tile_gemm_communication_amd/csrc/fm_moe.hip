@@ -231,11 +231,11 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
             o[1] += wt[q] * v[1];
             o[2] += wt[q] * v[2];
             o[3] += wt[q] * v[3];
-            *reinterpret_cast<f32x4*>(dst[q]) = o;
+            store_through(dst[q], o);
           }
         }
       }
-      wait_vmcnt<0>();   // this wave's stores are complete
+      wait_vmcnt<0>();   // this wave's write-through stores are complete
       __syncthreads();
       if (t == 0) signal_count(a.col_done + tn, (uint32_t)(total / a.tiles_n));
     } else {
