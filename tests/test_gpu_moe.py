@@ -82,6 +82,7 @@ def _moe_run(inp, e0, nl, dt, H_in=None):
                                                   (64, 512, 512, 64, 8, 0)])
 def test_moe_small(oracle, monkeypatch, tile, dt, T, hidden, ffn, E, nl, e0):
     monkeypatch.setenv("FM_MOE_TILE", tile)
+    monkeypatch.setenv("FM_SPLIT_TAIL", "0")
     say(f"moe T={T} hidden={hidden} ffn={ffn} E={E} nl={nl} e0={e0} dt={dt} tile={tile}")
     inp = wl.moe_inputs(T, hidden, ffn, E, nl, 2, dt, seed=T + hidden, zipf_s=1.2)
     roff, rsp = oracle.moe_route(inp["topk_ids"], e0, nl)
@@ -178,3 +179,37 @@ def test_moe_combine_deterministic(oracle, T, hidden, ffn, E, nl, topk):
                             inp["out_seed"], 0)
     assert_close(outs[0].astype(np.float64) - inp["out_seed"], ref - inp["out_seed"],
                  "deterministic combine")
+
+
+@pytest.mark.parametrize("T,ffn", [(20000, 504), (600, 264)])
+def test_moe_gather_split_tail_bit_identical(oracle, monkeypatch, T, ffn):
+    """Layer 0 runs a half-empty last wave of 256x256 tiles as 256x128 halves
+    (a second launch).  Each H element is still summed over K by one
+    workgroup in the same order, so H is bit-identical to the unsplit run,
+    and meets the parity bar on sampled rows.  Shapes: about 330 tiles (one
+    full wave plus a tail) with a ragged last column, and a few tiles only
+    (halves alone)."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    hidden, E, nl = 64, 8, 8
+    say(f"moe split tail T={T} ffn={ffn}")
+    inp = wl.moe_inputs(T, hidden, ffn, E, nl, 2, BF16, seed=T + ffn, zipf_s=1.2)
+    roff, rsp = oracle.moe_route(inp["topk_ids"], 0, nl)
+    rows = int(roff[-1])
+    X, W1, ids = dev16(inp["X"], BF16), dev16(inp["W1"], BF16), _i32(inp["topk_ids"])
+    outs = []
+    for split in ("1", "0"):
+        monkeypatch.setenv("FM_SPLIT_TAIL", split)
+        H = torch.zeros((T * 2, ffn), dtype=torch.bfloat16, device="cuda:0")
+        sp = torch.full((T * 2,), -1, dtype=torch.int32, device="cuda:0")
+        off = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
+        fm.fm_moe_gather_gemm(X, ids, W1, H, sp, off, 0)
+        torch.cuda.synchronize()
+        outs.append(H)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), "split changed H"
+    rng = np.random.default_rng(3)
+    srows = np.unique(np.concatenate([rng.integers(0, rows, 64), roff[:-1], roff[1:] - 1]))
+    srows = srows[(srows >= 0) & (srows < rows)]
+    Hs = oracle.moe_layer0_rows(BF16, inp["X"], inp["W1"], rsp, roff, 2, srows)
+    idx = torch.from_numpy(srows).to("cuda:0")
+    assert_close(host64(outs[0][idx]), Hs, "split-tail layer0 rows")

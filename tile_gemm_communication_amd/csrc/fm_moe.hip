@@ -134,6 +134,10 @@ struct MoeArgs {
   int64_t K, N;
   int64_t spin_limit;
   int topk, n_local, tiles_n, group_m;
+  // Tail split (layer 0): when the last wave of 256x256 tiles would fill at
+  // most half of g_ref CUs, part 0 runs the full waves and part 1 the
+  // remaining tiles as 256x128 halves.  tiles_n always counts 256-wide tiles.
+  int split, part, g_ref;
 };
 
 template <class E, int BM, int BN, int NW, bool SCATTER, bool KTAIL>
@@ -161,8 +165,17 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   const int total = s_tile0[a.n_local];
   const int G = gridDim.x;
   const int slot = xcd_slot(blockIdx.x, G);
+  int full = total;
+  if (a.split) {
+    const int rem = total % a.g_ref;
+    if (rem > 0 && 2 * rem <= a.g_ref) full = total - rem;
+  }
+  const int sub_n = a.part ? 2 : 1;                  // BN = 256 / sub_n
+  const int pos0 = a.part ? full : 0;
+  const int n_items = a.part ? 2 * (total - full) : full;
 
-  for (int L = slot; L < total; L += G) {
+  for (int L2 = slot; L2 < n_items; L2 += G) {
+    const int L = pos0 + L2 / sub_n, sub = L2 % sub_n;
     int e = 0;
     while (e + 1 < a.n_local && s_tile0[e + 1] <= L) ++e;
     const int row_base = s_off[e];
@@ -171,7 +184,8 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
     int tm, tn;
     band_coords(L - s_tile0[e], tiles_me, a.tiles_n, min(a.group_m, tiles_me), tm, tn);
     const int m0 = tm * BM;
-    const int64_t n0 = (int64_t)tn * BN;
+    const int64_t n0 = ((int64_t)tn * sub_n + sub) * BN;
+    if (n0 >= N) continue;   // the right half of an edge tile that lies past N
 
     eng.set_a_base(a.A);
 #pragma unroll
@@ -279,16 +293,37 @@ MoeTile moe_tile() {
 }
 
 template <bool SCATTER>
+void launch_moe_part(fm_dtype_t dt, MoeTile cfg, const MoeArgs& a, hipStream_t stream);
+
+// Layer 0 splits a half-empty last wave into 256x128 halves (part 1, a second
+// launch; it finds no work when the device-side tile count needs no split).
+// The combine (layer 1) keeps whole tiles: its per-column ordering counts
+// one tile per column and M-tile.
+template <bool SCATTER>
 fm_status_t launch_moe(fm_dtype_t dt, MoeTile cfg, MoeArgs& a, hipStream_t stream) {
   a.tiles_n = (int)cdiv(a.N, cfg.bn);
   a.group_m = 8;
   a.spin_limit = 1ll << 26;
+  a.g_ref = device_cu_count();
+  const char* env = std::getenv("FM_SPLIT_TAIL");
+  a.split = (!SCATTER && cfg.bm == 256 && cfg.bn == 256 && !(env && env[0] == '0')) ? 1 : 0;
+  a.part = 0;
   if (SCATTER) {
     if (a.tiles_n > kColDoneN) return FM_ERR_UNSUPPORTED;
     a.col_done = device_tile_counters();
     if (!a.col_done) return FM_ERR_HIP;
     a.col_done += kColDone0;
   }
+  launch_moe_part<SCATTER>(dt, cfg, a, stream);
+  if (a.split) {
+    a.part = 1;
+    launch_moe_part<SCATTER>(dt, MoeTile{256, 128, 4}, a, stream);
+  }
+  return launch_status();
+}
+
+template <bool SCATTER>
+void launch_moe_part(fm_dtype_t dt, MoeTile cfg, const MoeArgs& a, hipStream_t stream) {
   const dim3 grid(device_cu_count());
 #define FM_LAUNCH(E, BM, BN, NW)                                                             \
   do {                                                                                       \
@@ -312,7 +347,6 @@ fm_status_t launch_moe(fm_dtype_t dt, MoeTile cfg, MoeArgs& a, hipStream_t strea
   if (dt == FM_F16) FM_LAUNCH_E(F16); else FM_LAUNCH_E(BF16);
 #undef FM_LAUNCH_E
 #undef FM_LAUNCH
-  return launch_status();
 }
 
 fm_status_t check_route_args(int64_t T, int32_t topk, int32_t n_local, const int32_t* topk_ids,
