@@ -146,6 +146,8 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[Eng::LDS_BYTES];
   __shared__ int s_off[kMaxLocalExperts + 1];
   __shared__ int s_tile0[kMaxLocalExperts + 1];
+  __shared__ int s_tok[SCATTER ? BM : 1];      // combine: token and gate weight per tile row
+  __shared__ float s_wt[SCATTER ? BM : 1];
 
   const int t = threadIdx.x;
   if (t <= a.n_local) s_off[t] = a.offsets[t];
@@ -200,6 +202,12 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       eng.set_a(i, (uint32_t)(src_row * K * 2));
     }
     eng.set_b(a.W + (int64_t)e * K * N * 2, N * 2, n0, N);
+    // Combine: fetch each tile row's pair id now, so that the load overlaps
+    // the K loop (the K loop's first wait drains it with the stage-0 DMA).
+    int my_p = -1;
+    if constexpr (SCATTER) {
+      if (t < BM && m0 + t < rows_e) my_p = a.sorted_pairs[row_base + m0 + t];
+    }
     eng.run();
 
     // Epilogue through the LDS staging regions (whole-line global accesses).
@@ -211,6 +219,11 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       // read-modify-write after every earlier expert's tiles of that column
       // (count per column, in expert order).  The adds are plain fp32 loads
       // and stores, in a fixed order: the combine is deterministic.
+      // Row metadata into LDS (token, gate weight; token -1 past the rows).
+      if (t < BM) {
+        s_tok[t] = my_p >= 0 ? my_p / a.topk : -1;
+        s_wt[t] = my_p >= 0 ? a.weights[my_p] : 0.f;
+      }
       if (e > 0 && t == 0)
         wait_count(a.col_done + tn, (uint32_t)(s_tile0[e] / a.tiles_n), a.spin_limit);
       __syncthreads();
@@ -218,24 +231,23 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       const bool col_ok = n0 + col < N;
 #pragma unroll
       for (int i = 0; i < Eng::FM; ++i) {
-        eng.ep_stage(i);
         float* dst[Eng::EP_READS];
         float wt[Eng::EP_READS];
 #pragma unroll
         for (int q = 0; q < Eng::EP_READS; ++q) {
-          const int lr = m0 + eng.ep_row(i, q);
-          dst[q] = nullptr;
-          wt[q] = 0.f;
-          if (lr < rows_e && col_ok) {
-            const int p = a.sorted_pairs[row_base + lr];
-            wt[q] = a.weights[p];
-            dst[q] = reinterpret_cast<float*>(a.out) + (int64_t)(p / a.topk) * N + n0 + col;
-          }
+          const int r = eng.ep_row(i, q);
+          const int tok = s_tok[r];
+          wt[q] = s_wt[r];
+          dst[q] = (tok >= 0 && col_ok)
+                       ? reinterpret_cast<float*>(a.out) + (int64_t)tok * N + n0 + col
+                       : nullptr;
         }
+        // out loads go first; the accumulators are staged while they fly
         f32x4 old[Eng::EP_READS];
 #pragma unroll
         for (int q = 0; q < Eng::EP_READS; ++q)
           if (dst[q]) old[q] = *reinterpret_cast<const f32x4*>(dst[q]);
+        eng.ep_stage(i);
 #pragma unroll
         for (int q = 0; q < Eng::EP_READS; ++q) {
           const f32x4 v = eng.ep_read(q);
