@@ -157,25 +157,20 @@ __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args)
         const int lim = col_ok ? (int)(m_end - m0) - eng.ep_row(0, 0) : 0;
 #pragma unroll
         for (int i = 0; i < Eng::FM; ++i) {
-          eng.ep_stage(i);
           float* p0 = base + (uint32_t)(eng.ep_row(i, 0) * (int)N + col);
-          // batches of RB runs: RB loads in flight, then RB stores
-          constexpr int RB = Eng::EP_READS < 4 ? Eng::EP_READS : 4;
+          // the slice rows are requested first; the accumulators are staged
+          // while the loads fly
+          f32x4 old[Eng::EP_READS];
 #pragma unroll
-          for (int q0 = 0; q0 < Eng::EP_READS; q0 += RB) {
-            f32x4 old[RB];
+          for (int q = 0; q < Eng::EP_READS; ++q)
+            if (i * 32 + q * Eng::EP_RPI < lim)
+              old[q] = *reinterpret_cast<const f32x4*>(p0 + (uint32_t)(q * Eng::EP_RPI * (int)N));
+          eng.ep_stage(i);
 #pragma unroll
-            for (int u = 0; u < RB; ++u)
-              if (i * 32 + (q0 + u) * Eng::EP_RPI < lim)
-                old[u] = *reinterpret_cast<const f32x4*>(
-                    p0 + (uint32_t)((q0 + u) * Eng::EP_RPI * (int)N));
-#pragma unroll
-            for (int u = 0; u < RB; ++u) {
-              const f32x4 v = eng.ep_read(q0 + u);
-              if (i * 32 + (q0 + u) * Eng::EP_RPI < lim)
-                *reinterpret_cast<f32x4*>(p0 + (uint32_t)((q0 + u) * Eng::EP_RPI * (int)N)) =
-                    old[u] + v;
-            }
+          for (int q = 0; q < Eng::EP_READS; ++q) {
+            const f32x4 v = eng.ep_read(q);
+            if (i * 32 + q * Eng::EP_RPI < lim)
+              *reinterpret_cast<f32x4*>(p0 + (uint32_t)(q * Eng::EP_RPI * (int)N)) = old[q] + v;
           }
         }
       } else {
