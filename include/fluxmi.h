@@ -117,8 +117,8 @@ fm_status_t fm_ag_gemm(fm_dtype_t dt, int64_t M, int64_t N, int64_t K, int32_t n
  *            and non-overlapping.
  *   counter  device uint32 scratch owned by the caller, zero before the
  *            first call and left zero after every call; one per flag in use.
- *   n_workgroups  copy workgroups, 0 = default (one per 64 KiB, at most two
- *                 per compute unit).
+ *   n_workgroups  copy workgroups, 0 = default (one per 192 KiB, at most
+ *                 two per compute unit).
  */
 fm_status_t fm_chunk_push(const void* src, void* dst, int64_t bytes, uint32_t* flag,
                           uint32_t* counter, uint32_t epoch, int32_t n_workgroups,

@@ -330,7 +330,24 @@ fm_status_t launch_dense(fm_dtype_t dt, TileCfg cfg, DenseArgs& args, hipStream_
   if (T <= 0) return FM_OK;
   const int G = device_cu_count();
   if (split_tail_ok(cfg, T, G)) {
-    const int full = T - T % G;
+    const int rem = T % G, full = T - rem;
+    const TileCfg half{cfg.bm, 128, 4};
+    if (MODE == Mode::AG) {
+      // AllGather: the halves take the first positions (the chunks that
+      // arrive first), so the wave that may wait on arrivals is made of the
+      // shorter tiles, and the full tiles run once every chunk is likely in.
+      args.pos0 = 0;
+      args.pos_end = rem;
+      args.sub_n = 2;
+      launch_one<MODE, OUT32>(dt, half, args, stream);
+      if (full > 0) {
+        args.pos0 = rem;
+        args.pos_end = T;
+        args.sub_n = 1;
+        launch_one<MODE, OUT32>(dt, cfg, args, stream);
+      }
+      return launch_status();
+    }
     if (full > 0) {
       args.pos0 = 0;
       args.pos_end = full;
@@ -340,7 +357,7 @@ fm_status_t launch_dense(fm_dtype_t dt, TileCfg cfg, DenseArgs& args, hipStream_
     args.pos0 = full;
     args.pos_end = T;
     args.sub_n = 2;
-    launch_one<MODE, OUT32>(dt, TileCfg{cfg.bm, 128, 4}, args, stream);
+    launch_one<MODE, OUT32>(dt, half, args, stream);
   } else {
     args.pos0 = 0;
     args.pos_end = T;

@@ -61,12 +61,13 @@ extern "C" fm_status_t fm_chunk_push(const void* src, void* dst, int64_t bytes, 
     if (s < d + bytes && d < s + bytes) return FM_ERR_INVALID_ARG;   // overlap
   }
   const int64_t n16 = bytes / 16;
-  // Default: one workgroup per 64 KiB, at most two per CU.  Each thread keeps
-  // four 16-byte loads in flight, so a grid of G workgroups has G * 16 KiB in
-  // flight; a few MiB in flight are needed to approach HBM bandwidth.
+  // Default: one workgroup per 192 KiB, at most two per CU.  Each thread
+  // keeps four 16-byte loads in flight (16 KiB per workgroup).  A 12.6 MB
+  // chunk gets 64 workgroups: as fast as a wider grid on an idle GPU, and it
+  // takes fewer compute units from a GEMM running beside it.
   int wg = n_workgroups > 0
                ? n_workgroups
-               : (int)std::min<int64_t>(std::max<int64_t>(cdiv(bytes, 65536), 1),
+               : (int)std::min<int64_t>(std::max<int64_t>(cdiv(bytes, 196608), 1),
                                         2 * (int64_t)device_cu_count());
   if (n16 == 0) wg = 1;
   else if (wg > cdiv(n16, 256)) wg = (int)cdiv(n16, 256);
