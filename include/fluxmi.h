@@ -208,11 +208,13 @@ fm_status_t fm_moe_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t
  *   topk_weights device fp32 [T, topk]; out device fp32 [T, hidden].
  * The additions into a token row are applied in local-expert order with plain
  * fp32 loads and stores (no atomics), so the result is deterministic.  The
- * ordering uses per-device tile counters that the library allocates on the
- * first call (128 KiB, kept until the process ends; FM_ERR_HIP if that
- * allocation fails) and every call leaves at zero: calls of this function on
- * one device must not overlap in time (issue them on one stream, or order
- * the streams).  Requires ceil(hidden / 128) <= 32768.
+ * ordering uses per-(row tile, column tile) completion flags in a per-device
+ * buffer that the library allocates on the first call (128 KiB, kept until
+ * the process ends; FM_ERR_HIP if that allocation fails), stamped with a
+ * per-call epoch: calls of this function on one device must not overlap in
+ * time (issue them on one stream, or order the streams).  Requires
+ * (ceil(T*topk/256) + n_local) * ceil(hidden/256) <= 16384, else
+ * FM_ERR_UNSUPPORTED.
  */
 fm_status_t fm_moe_gemm_scatter(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn,
                                 int32_t topk, int32_t n_local, const void* H, const void* W2,

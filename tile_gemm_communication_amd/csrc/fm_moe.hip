@@ -9,6 +9,7 @@
 // computation units line up; local data blocks are computed first.  Here the
 // unit is a row tile of one expert's gathered tokens.
 #include <algorithm>
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -19,6 +20,7 @@
 namespace fm {
 
 constexpr int kMaxLocalExperts = 64;
+constexpr int kMaxMTiles = 1024;                      // token ranges cached in LDS
 constexpr int kRouteThreads = 256;
 constexpr int kRouteWaves = kRouteThreads / 64;
 // Per-chunk expert counts live in the route region of the library's
@@ -130,7 +132,8 @@ struct MoeArgs {
   const int32_t* sorted_pairs;
   const int32_t* offsets;
   const float* weights;       // [T * topk] (layer 1)
-  uint32_t* col_done;         // layer 1: finished tiles per N-tile column (self-resetting)
+  uint32_t* tile_done;        // layer 1: per (M-tile, N-tile) completion epoch
+  uint32_t epoch;             // this call's epoch (flags >= epoch: done in this call)
   int64_t K, N;
   int64_t spin_limit;
   int topk, n_local, tiles_n, group_m;
@@ -138,7 +141,51 @@ struct MoeArgs {
   // most half of g_ref CUs, part 0 runs the full waves and part 1 the
   // remaining tiles as 256x128 halves.  tiles_n always counts 256-wide tiles.
   int split, part, g_ref;
+  int64_t rows_cap;           // T * topk: an upper bound on the local rows
 };
+
+// Epochs of the combine's tile flags: one per call, process-wide, never 0
+// (the flags start at 0).
+uint32_t next_combine_epoch() {
+  static std::atomic<uint32_t> epoch{0};
+  uint32_t e = epoch.fetch_add(1) + 1;
+  if (e == 0) e = epoch.fetch_add(1) + 1;
+  return e;
+}
+
+// Called by one thread: wait until every tile of an expert before e in
+// column tn whose token range overlaps that of global M-tile gm has published
+// this call's epoch, then acquire.  Beyond kMaxMTiles tiles the ranges are not
+// cached and every earlier tile of the column is waited for.
+__device__ __forceinline__ void wait_token_range(const MoeArgs& a, const int* s_tile0,
+                                                 const int* s_ftok, const int* s_ltok,
+                                                 int total_m, int e, int gm, int tn) {
+  const bool cached = total_m <= kMaxMTiles;
+  const int lo_tok = cached ? s_ftok[gm] : 0;
+  const int hi_tok = cached ? s_ltok[gm] : 0x7FFFFFFF;
+  for (int ep = 0; ep < e; ++ep) {
+    const int g0 = s_tile0[ep] / a.tiles_n, g1 = s_tile0[ep + 1] / a.tiles_n;
+    int m = g0;
+    if (cached) {   // first tile of expert ep whose last token is >= lo_tok
+      int lo = g0, hi = g1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_ltok[mid] < lo_tok) lo = mid + 1; else hi = mid;
+      }
+      m = lo;
+    }
+    for (; m < g1 && (!cached || s_ftok[m] <= hi_tok); ++m) {
+      const uint32_t* f = a.tile_done + (int64_t)m * a.tiles_n + tn;
+      int64_t polls = 0;
+      while (!flag_reached(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                           a.epoch)) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++polls > a.spin_limit) break;   // safeguard only: see the deadlock note
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
 
 template <class E, int BM, int BN, int NW, bool SCATTER, bool KTAIL>
 __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
@@ -148,6 +195,9 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   __shared__ int s_tile0[kMaxLocalExperts + 1];
   __shared__ int s_tok[SCATTER ? BM : 1];      // combine: token and gate weight per tile row
   __shared__ float s_wt[SCATTER ? BM : 1];
+  // combine: first and last token of every M-tile (all experts, in order)
+  __shared__ int s_ftok[SCATTER ? kMaxMTiles : 1];
+  __shared__ int s_ltok[SCATTER ? kMaxMTiles : 1];
 
   const int t = threadIdx.x;
   if (t <= a.n_local) s_off[t] = a.offsets[t];
@@ -161,6 +211,23 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
     s_tile0[a.n_local] = acc;
   }
   __syncthreads();
+
+  // Combine: token range of every M-tile.  Rows of an expert are sorted by
+  // pair id, hence by token, and hold each token at most once, so the tiles
+  // of one expert cover disjoint, increasing token ranges.
+  const int total_m = s_tile0[a.n_local] / a.tiles_n;
+  if constexpr (SCATTER) {
+    for (int m = t; m < total_m && m < kMaxMTiles; m += 64 * NW) {
+      int e = 0;
+      while (e + 1 < a.n_local && s_tile0[e + 1] / a.tiles_n <= m) ++e;
+      const int tm = m - s_tile0[e] / a.tiles_n;
+      const int rows_e = s_off[e + 1] - s_off[e];
+      const int r0 = s_off[e] + tm * BM, r1 = s_off[e] + min((tm + 1) * BM, rows_e) - 1;
+      s_ftok[m] = a.sorted_pairs[r0] / a.topk;
+      s_ltok[m] = a.sorted_pairs[r1] / a.topk;
+    }
+    __syncthreads();
+  }
 
   Eng eng(smem, a.K);
   const int64_t N = a.N, K = a.K;
@@ -224,8 +291,13 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
         s_tok[t] = my_p >= 0 ? my_p / a.topk : -1;
         s_wt[t] = my_p >= 0 ? a.weights[my_p] : 0.f;
       }
+      // Wait for the tiles of earlier experts in this N column whose token
+      // ranges overlap this tile's: they hold every earlier contribution to
+      // this tile's tokens, and are usually long finished (each expert walks
+      // its tokens in order, about one expert's worth of tiles earlier).
+      const int gm = s_tile0[e] / a.tiles_n + tm;   // this tile's global M-tile
       if (e > 0 && t == 0)
-        wait_count(a.col_done + tn, (uint32_t)(s_tile0[e] / a.tiles_n), a.spin_limit);
+        wait_token_range(a, s_tile0, s_ftok, s_ltok, total_m, e, gm, tn);
       __syncthreads();
       const int col = eng.ep_col();
       const bool col_ok = n0 + col < N;
@@ -263,7 +335,9 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       }
       wait_vmcnt<0>();   // this wave's write-through stores are complete
       __syncthreads();
-      if (t == 0) signal_count(a.col_done + tn, (uint32_t)(total / a.tiles_n));
+      if (t == 0)
+        __hip_atomic_store(a.tile_done + (int64_t)gm * a.tiles_n + tn, a.epoch, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     } else {
       // H rows in expert-sorted order, 16-bit.
       const int col = eng.ep_col();
@@ -321,10 +395,13 @@ fm_status_t launch_moe(fm_dtype_t dt, MoeTile cfg, MoeArgs& a, hipStream_t strea
   a.split = (!SCATTER && cfg.bm == 256 && cfg.bn == 256 && !(env && env[0] == '0')) ? 1 : 0;
   a.part = 0;
   if (SCATTER) {
-    if (a.tiles_n > kColDoneN) return FM_ERR_UNSUPPORTED;
-    a.col_done = device_tile_counters();
-    if (!a.col_done) return FM_ERR_HIP;
-    a.col_done += kColDone0;
+    // one completion flag per (M-tile, N-tile); M-tiles <= pairs/BM + experts
+    const int64_t m_tiles = cdiv(a.rows_cap, (int64_t)cfg.bm) + a.n_local;
+    if (m_tiles * a.tiles_n > kColDoneN) return FM_ERR_UNSUPPORTED;
+    a.tile_done = device_tile_counters();
+    if (!a.tile_done) return FM_ERR_HIP;
+    a.tile_done += kColDone0;
+    a.epoch = next_combine_epoch();
   }
   launch_moe_part<SCATTER>(dt, cfg, a, stream);
   if (a.split) {
@@ -425,6 +502,7 @@ extern "C" fm_status_t fm_moe_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidd
   a.K = hidden;
   a.N = ffn;
   a.topk = topk;
+  a.rows_cap = T * topk;
   a.n_local = n_local;
   return launch_moe<false>(dt, moe_tile(), a, stream);
 }
@@ -457,6 +535,7 @@ extern "C" fm_status_t fm_moe_gemm_scatter(fm_dtype_t dt, int64_t T, int64_t hid
   a.K = ffn;
   a.N = hidden;
   a.topk = topk;
+  a.rows_cap = T * topk;
   a.n_local = n_local;
   return launch_moe<true>(dt, moe_tile(), a, stream);
 }

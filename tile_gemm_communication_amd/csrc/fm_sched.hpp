@@ -76,40 +76,12 @@ __device__ __forceinline__ bool wait_chunks(const uint32_t* flags, uint32_t epoc
   return true;
 }
 
-// Ordered epilogues (tile counters).  Called by one thread: wait until
-// *ctr >= target, then acquire, so that what the counted tiles stored before
-// their release is visible.  Returns false once `limit` polls pass.
-__device__ __forceinline__ bool wait_count(const uint32_t* ctr, uint32_t target, int64_t limit) {
-  int64_t polls = 0;
-  bool ok = true;
-  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-    __builtin_amdgcn_s_sleep(2);
-    if (++polls > limit) {
-      ok = false;
-      break;
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return ok;
-}
-
 // Store 16 bytes written through every cache level (system-scope store):
 // once the wave's vmcnt drains, the data is visible device-wide without an
 // L2 write-back.  Used for data that a counted tile hands to a tile that may
 // run on another XCD (each XCD has its own, non-coherent L2).
 __device__ __forceinline__ void store_through(float* p, const f32x4& v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" ::"v"(p), "v"(v) : "memory");
-}
-
-// Called by one thread after the workgroup's handed-over data is complete:
-// every wave wrote it with store_through and waited for vmcnt(0), then a
-// barrier.  That data is already visible device-wide, so the count needs no
-// release fence (which would write back the whole L2 of this XCD on every
-// tile).  The tile that brings the count to `total` (the last one; nobody
-// waits on the counter any more) resets it for the next launch.
-__device__ __forceinline__ void signal_count(uint32_t* ctr, uint32_t total) {
-  const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (old + 1 == total) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace fm
