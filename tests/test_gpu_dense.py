@@ -137,7 +137,7 @@ def test_ag_arrival_order_invariance():
         assert np.array_equal(b, first), perm
 
 
-@pytest.mark.parametrize("n_chunks,Mc", [(1, 300), (8, 64), (3, 512), (16, 32)])
+@pytest.mark.parametrize("n_chunks,Mc", [(1, 300), (8, 64), (3, 512), (16, 32), (64, 16)])
 def test_ag_chunk_layouts(oracle, n_chunks, Mc):
     """Chunks smaller, equal and larger than a tile; ragged M."""
     K, N = 136, 264
@@ -177,7 +177,8 @@ def test_rs_small(oracle, monkeypatch, tile, atomic, dt):
         assert_close(got[r] - seeds[r], ref[r] - seeds[r], f"rs slice {r}")
 
 
-@pytest.mark.parametrize("M,P,rank", [(128, 4, 3), (520, 8, 5), (96, 1, 0), (264, 2, 1)])
+@pytest.mark.parametrize("M,P,rank", [(128, 4, 3), (520, 8, 5), (96, 1, 0), (264, 2, 1),
+                                      (1024, 16, 15)])
 def test_rs_slices_vs_tiles(oracle, M, P, rank):
     """Slices smaller than a tile (tiles straddle slices), ragged M, P = 1."""
     A, W, seeds = wl.rs_inputs(M, 200, 136, P, F16, seed=M + P)

@@ -213,3 +213,43 @@ def test_moe_gather_split_tail_bit_identical(oracle, monkeypatch, T, ffn):
     Hs = oracle.moe_layer0_rows(BF16, inp["X"], inp["W1"], rsp, roff, 2, srows)
     idx = torch.from_numpy(srows).to("cuda:0")
     assert_close(host64(outs[0][idx]), Hs, "split-tail layer0 rows")
+
+
+def test_moe_nothing_local_leaves_buffers():
+    """No pair routed to this rank's experts: every local expert is empty, H
+    keeps its contents and the combine adds nothing."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    T, hidden, ffn, nl = 300, 128, 64, 4
+    inp = wl.moe_inputs(T, hidden, ffn, 16, nl, 2, BF16, seed=11)
+    ids = np.full((T, 2), 12, dtype=np.int32)            # experts 12, never local (0..3)
+    H = torch.full((T * 2, ffn), 7.0, dtype=torch.bfloat16, device="cuda:0")
+    sp = torch.full((T * 2,), -1, dtype=torch.int32, device="cuda:0")
+    off = torch.full((nl + 1,), 99, dtype=torch.int32, device="cuda:0")
+    out = devf32(inp["out_seed"])
+    fm.fm_moe_gather_gemm(dev16(inp["X"], BF16), _i32(ids), dev16(inp["W1"], BF16), H, sp, off, 0)
+    fm.fm_moe_gemm_scatter(H, dev16(inp["W2"], BF16), sp, off, devf32(inp["topk_weights"]), out)
+    torch.cuda.synchronize()
+    assert off.cpu().numpy().tolist() == [0] * (nl + 1)
+    assert bool((H.float() == 7.0).all()) and bool((sp == -1).all())
+    assert np.array_equal(out.cpu().numpy(), inp["out_seed"])
+
+
+@pytest.mark.parametrize("topk,nl,e0", [(1, 1, 3), (4, 64, 0)])
+def test_moe_extreme_expert_counts(oracle, topk, nl, e0):
+    """One local expert with top-1 routing, and 64 local experts with top-4
+    (up to four ordered contributions per token)."""
+    T, hidden, ffn = 700, 192, 136
+    E = max(nl + e0, 8)
+    say(f"moe topk={topk} n_local={nl} e0={e0}")
+    inp = wl.moe_inputs(T, hidden, ffn, E, nl, topk, BF16, seed=T + topk, zipf_s=0.6)
+    roff, rsp = oracle.moe_route(inp["topk_ids"], e0, nl)
+    Href = oracle.moe_layer0(BF16, inp["X"], inp["W1"], rsp, roff, topk)
+    Hb = oracle.round_bf16(Href)
+    off, sp, H, out = _moe_run(inp, e0, nl, BF16, H_in=Hb)
+    rows = int(roff[-1])
+    assert np.array_equal(off, roff) and np.array_equal(sp[:rows], rsp)
+    assert_close(host64(H[:rows]), Href, "layer0 H")
+    ref = oracle.moe_layer1(BF16, Hb, inp["W2"], inp["topk_ids"], inp["topk_weights"], rsp, roff,
+                            inp["out_seed"], e0)
+    assert_close(host64(out) - inp["out_seed"], ref - inp["out_seed"], "combine")
