@@ -11,8 +11,8 @@ from gpu_util import (BF16, F16, Arrival, assert_close, bits16, dev16, devf32, h
 
 pytestmark = pytest.mark.gpu
 
-# FM_TILE forms: BMxBN[wNW]; a bare 256x256 takes the 8-wave form.
-TILES = ["256x128", "128x128", "256x256", "256x256w4", "256x128w8"]
+# FM_TILE forms: BMxBN[wNW] (4 or 8 waves; 4 when omitted).
+TILES = ["256x128", "128x128", "256x256", "256x256w8", "256x128w8"]
 
 
 @pytest.fixture(autouse=True)

@@ -75,7 +75,7 @@ def _moe_run(inp, e0, nl, dt, H_in=None):
     return off.cpu().numpy(), sp.cpu().numpy(), H, out
 
 
-@pytest.mark.parametrize("tile", ["256x256", "256x256w4", "256x128w8", "128x128"])
+@pytest.mark.parametrize("tile", ["256x256", "256x256w4", "256x256w8", "256x128w8", "128x128"])
 @pytest.mark.parametrize("dt", [F16, BF16])
 @pytest.mark.parametrize("T,hidden,ffn,E,nl,e0", [(256, 256, 128, 16, 4, 4),
                                                   (300, 136, 264, 8, 8, 0),

@@ -102,7 +102,8 @@ __device__ __forceinline__ void store_tile(Eng& eng, const DenseArgs& args, int6
 
 template <class E, int BM, int BN, int NW, Mode MODE, bool OUT32, bool KTAIL>
 __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args) {
-  using Eng = Engine<E, BM, BN, KTAIL, NW>;
+  // One wave per SIMD has the register room for a two-sub-step read-ahead.
+  using Eng = Engine<E, BM, BN, KTAIL, NW, 4, NW == 4 ? 2 : 1>;
   __shared__ __attribute__((aligned(16))) char smem[Eng::LDS_BYTES];
   __shared__ int s_abort;
 
@@ -240,11 +241,11 @@ TileCfg choose_tile(int64_t M, int64_t N, int G) {
     int bm = 0, bn = 0, nw = 0;
     const int got = std::sscanf(env, "%dx%dw%d", &bm, &bn, &nw);
     if (got >= 2 && (bm == 128 || bm == 256) && (bn == 128 || bn == 256)) {
-      if (got < 3 || (nw != 4 && nw != 8)) nw = (bm == 256 && bn == 256) ? 8 : 4;
+      if (got < 3 || (nw != 4 && nw != 8)) nw = 4;
       if (!(bm == 128 && bn == 128 && nw == 8)) return {bm, bn, nw};
     }
   }
-  const TileCfg cands[3] = {{256, 256, 8}, {256, 128, 4}, {128, 128, 4}};
+  const TileCfg cands[3] = {{256, 256, 4}, {256, 128, 4}, {128, 128, 4}};
   const double eff[3] = {1.0, 0.85, 0.7};
   TileCfg best = cands[0];
   double best_cost = 1e300;

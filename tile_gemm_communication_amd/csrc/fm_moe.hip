@@ -189,7 +189,9 @@ __device__ __forceinline__ void wait_token_range(const MoeArgs& a, const int* s_
 
 template <class E, int BM, int BN, int NW, bool SCATTER, bool KTAIL>
 __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
-  using Eng = Engine<E, BM, BN, KTAIL, NW>;
+  // One wave per SIMD has the register room for a two-sub-step read-ahead
+  // (not next to the combine's epilogue state).
+  using Eng = Engine<E, BM, BN, KTAIL, NW, 4, (NW == 4 && !SCATTER) ? 2 : 1>;
   __shared__ __attribute__((aligned(16))) char smem[Eng::LDS_BYTES];
   __shared__ int s_off[kMaxLocalExperts + 1];
   __shared__ int s_tile0[kMaxLocalExperts + 1];
@@ -366,16 +368,20 @@ struct MoeTile {
   int bm, bn, nw;
 };
 
-MoeTile moe_tile() {
+// 256x256 tiles.  Layer 0 runs one wave per SIMD (with the deeper fragment
+// read-ahead); the combine runs two, which hide its read-modify-write
+// epilogue better.
+MoeTile moe_tile(bool scatter) {
+  const int nw_default = scatter ? 8 : 4;
   if (const char* env = std::getenv("FM_MOE_TILE")) {
     int bm = 0, bn = 0, nw = 0;
     const int got = std::sscanf(env, "%dx%dw%d", &bm, &bn, &nw);
     if (got >= 2 && (bm == 128 || bm == 256) && (bn == 128 || bn == 256)) {
-      if (got < 3 || (nw != 4 && nw != 8)) nw = (bm == 256 && bn == 256) ? 8 : 4;
+      if (got < 3 || (nw != 4 && nw != 8)) nw = (bm == 256 && bn == 256) ? nw_default : 4;
       if (!(bm == 128 && bn == 128 && nw == 8)) return {bm, bn, nw};
     }
   }
-  return {256, 256, 8};
+  return {256, 256, nw_default};
 }
 
 template <bool SCATTER>
@@ -504,7 +510,7 @@ extern "C" fm_status_t fm_moe_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidd
   a.topk = topk;
   a.rows_cap = T * topk;
   a.n_local = n_local;
-  return launch_moe<false>(dt, moe_tile(), a, stream);
+  return launch_moe<false>(dt, moe_tile(false), a, stream);
 }
 
 extern "C" fm_status_t fm_moe_gemm_scatter(fm_dtype_t dt, int64_t T, int64_t hidden,
@@ -537,5 +543,5 @@ extern "C" fm_status_t fm_moe_gemm_scatter(fm_dtype_t dt, int64_t T, int64_t hid
   a.topk = topk;
   a.rows_cap = T * topk;
   a.n_local = n_local;
-  return launch_moe<true>(dt, moe_tile(), a, stream);
+  return launch_moe<true>(dt, moe_tile(true), a, stream);
 }

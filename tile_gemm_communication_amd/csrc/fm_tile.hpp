@@ -85,8 +85,13 @@ __device__ __forceinline__ void interleave() {
   if constexpr (MFMAS > READS) __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - READS, 0);
 }
 
-template <class E, int BM, int BN, bool KTAIL, int NW = 4, int BSWZ = 4>
+template <class E, int BM, int BN, bool KTAIL, int NW = 4, int BSWZ = 4, int DEPTH_ = 1>
 struct Engine {
+  // Fragment read-ahead in sub-steps: 1 = the next sub-step (two register
+  // slots), 2 = two sub-steps ahead (four slots, one per sub-step; needs the
+  // register room of one wave per SIMD).  A K tail always uses 1.
+  static constexpr int DEPTH = KTAIL ? 1 : DEPTH_;
+  static constexpr int NSLOT = DEPTH == 2 ? 4 : 2;
   static constexpr int NWM = 2, NWN = NW / 2;          // wave grid over the tile
   static constexpr int THREADS = 64 * NW;
   static constexpr int BM_ = BM, BN_ = BN;
@@ -118,8 +123,8 @@ struct Engine {
   int KT;
 
   f32x16 acc[FM][FN];
-  u32x4 fa[2][FM];
-  u32x4 fb[2][FN];
+  u32x4 fa[NSLOT][FM];
+  u32x4 fb[NSLOT][FN];
 
   // DMA sources: wave-uniform bases (K offset 0) plus per-lane 32-bit offsets.
   const char* a_base;
@@ -286,28 +291,49 @@ struct Engine {
   // memory operation per MFMA where possible.
   __device__ __forceinline__ void substep(int cur, int nbuf, int nks, bool do_read,
                                           int dma_kt, int dbuf) {
+    substep_g(cur, nbuf, nks, cur ^ 1, do_read, dma_kt, dbuf, 0, DMA);
+  }
+  // General form: MFMAs on slot mslot, reads into slot rslot, DMA items
+  // [d0, d1) of K step dma_kt.
+  __device__ __forceinline__ void substep_g(int mslot, int nbuf, int nks, int rslot,
+                                            bool do_read, int dma_kt, int dbuf, int d0, int d1) {
 #pragma unroll
     for (int q = 0; q < MFMAS; ++q) {
       const int i = q / FN, j = q % FN;
-      acc[i][j] = E::mfma32(fb[cur][j], fa[cur][i], acc[i][j]);
+      acc[i][j] = E::mfma32(fb[mslot][j], fa[mslot][i], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
       if (do_read && q < RITEMS) {
-        read_item(q, nbuf, nks, cur ^ 1);
+        read_item(q, nbuf, nks, rslot);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (dma_kt >= 0 && q < DMA) {
-        dma_item(q, dma_kt, dbuf);
+      if (dma_kt >= 0 && d0 + q < d1) {
+        dma_item(d0 + q, dma_kt, dbuf);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (do_read) {       // more read items than MFMAs (small tiles)
 #pragma unroll
-      for (int q = MFMAS; q < RITEMS; ++q) read_item(q, nbuf, nks, cur ^ 1);
+      for (int q = MFMAS; q < RITEMS; ++q) read_item(q, nbuf, nks, rslot);
     }
     if (dma_kt >= 0) {   // more DMA items than MFMAs
 #pragma unroll
-      for (int d = MFMAS; d < DMA; ++d) dma_item(d, dma_kt, dbuf);
+      for (int d = d0 + MFMAS; d < d1; ++d) dma_item(d, dma_kt, dbuf);
     }
+  }
+
+  // Read-ahead 2: sub-steps 0 and 1 read the fragments of sub-steps 2 and 3
+  // of this stage; after the wait and barrier, sub-steps 2 and 3 read
+  // sub-steps 0 and 1 of stage kt+1 and issue the DMA of stage kt+2 into
+  // buffer cur in two halves.  Every read has a whole sub-step more slack.
+  __device__ __forceinline__ void step2(int kt) {
+    const int cur = kt & 1;
+    substep_g(0, cur, 2, 2, true, -1, 0, 0, 0);
+    substep_g(1, cur, 3, 3, true, -1, 0, 0, 0);
+    wait_all0();
+    __syncthreads();
+    const int dk = min(kt + 2, KT - 1);
+    substep_g(2, cur ^ 1, 0, 0, true, dk, cur, 0, DMA / 2);
+    substep_g(3, cur ^ 1, 1, 1, true, dk, cur, DMA / 2, DMA);
   }
 
   __device__ __forceinline__ void mma(int slot, int i0, int i1) {
@@ -360,7 +386,12 @@ struct Engine {
       wait_vmcnt<0>();     // a masked stage issues fewer loads: wait for all
     __syncthreads();
     read_frags(0, 0, 0);
-    for (int kt = 0; kt < KT; ++kt) step(kt);
+    if constexpr (DEPTH == 2) {
+      read_frags(0, 1, 1);
+      for (int kt = 0; kt < KT; ++kt) step2(kt);
+    } else {
+      for (int kt = 0; kt < KT; ++kt) step(kt);
+    }
   }
 
   // Output coordinates (within the tile) owned by this lane: block (i, j),
