@@ -368,11 +368,12 @@ struct MoeTile {
   int bm, bn, nw;
 };
 
-// 256x256 tiles.  Layer 0 runs one wave per SIMD (with the deeper fragment
-// read-ahead); the combine runs two, which hide its read-modify-write
-// epilogue better.
+// 256x256 tiles with two waves per SIMD: measured on N(0,1) data, 2% faster
+// than one wave per SIMD for layer 0, and 10% for the combine, whose
+// read-modify-write epilogue the second wave hides.
 MoeTile moe_tile(bool scatter) {
-  const int nw_default = scatter ? 8 : 4;
+  const int nw_default = 8;
+  (void)scatter;
   if (const char* env = std::getenv("FM_MOE_TILE")) {
     int bm = 0, bn = 0, nw = 0;
     const int got = std::sscanf(env, "%dx%dw%d", &bm, &bn, &nw);
