@@ -16,7 +16,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;   // 4 wave64 per workgroup, one per SIMD
 constexpr int kBK = 64;         // K extent of one LDS stage (128 bytes per row)
 
 __host__ __device__ constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -47,10 +46,6 @@ struct BF16 {
   }
 };
 
-// Output element traits for the plain-store epilogue.
-template <class E> struct Out16 {
-  static constexpr int bytes = 2;
-};
 
 // Device properties cached once per device (compute-unit count).
 int device_cu_count();

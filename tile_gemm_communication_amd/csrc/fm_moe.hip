@@ -2,7 +2,7 @@
 //   route   expert-sorted row index (chunked counting sort, stable, deterministic)
 //   layer 0 token gather fused into a grouped (per-expert, ragged-M) GEMM
 //   layer 1 grouped GEMM with the top-k weighted scatter-reduce fused into
-//           its epilogue (fp32 atomic adds into the token rows)
+//           its epilogue (ordered fp32 read-modify-write into the token rows)
 //
 // COMET article, "COMET 的技术原理": the tensor shared by the MoE layers is
 // decomposed along the token dimension so that the smallest communication and

@@ -19,21 +19,25 @@
 //
 // Bank-conflict-free placement: rows are cut into 16-byte chunks; chunk c of
 // A row m is stored at c ^ ((m ^ m>>3) & 7) and chunk c of B row k at
-// c ^ BSWZ*(k & 3) (BSWZ = 4 for the 64-bank LDS of gfx950).  A direct-to-LDS load writes its 64 lanes' 16 bytes
-// contiguously, so the placement is realised by choosing which global chunk
-// each lane fetches.
+// c ^ BSWZ*(k & 3) (BSWZ = 4 for the 64-bank LDS of gfx950).  A
+// direct-to-LDS load writes its 64 lanes' 16 bytes contiguously, so the
+// placement is realised by choosing which global chunk each lane fetches.
 //
 // The loads are issued with inline assembly: the compiler then sees no LDS
 // DMA and does not order every later LDS read behind it; the ordering the
 // pipeline needs is explicit (s_waitcnt + barrier below).
 //
-// Pipeline per K step kt (buffer cur = kt & 1), fragments double-buffered:
+// Pipeline per K step kt (buffer cur = kt & 1).  With a read-ahead of one
+// sub-step (two fragment register slots):
 //   sub-steps 0..2: MFMAs interleaved with the LDS reads of the next
 //                   sub-step's fragments;
 //   barrier:        after this wave's DMA of stage kt+1 and its reads of
 //                   stage kt are done (stage kt+1 complete, stage kt drained);
 //   sub-step 3:     MFMAs interleaved with the reads of sub-step 0 of stage
 //                   kt+1 and the DMA of stage kt+2 into buffer cur.
+// With a read-ahead of two (four slots, one wave per SIMD) sub-steps 0 and 1
+// read sub-steps 2 and 3, the barrier follows sub-step 1, and sub-steps 2
+// and 3 read sub-steps 0 and 1 of stage kt+1 while issuing the DMA.
 // Every instruction group is fenced with sched_barrier, so the issue order is
 // the source order: one LDS read or DMA per MFMA, never a burst of loads
 // that would leave the matrix cores idle.
