@@ -75,6 +75,8 @@ class Oracle:
         L.or_moe_route.restype = _i64
         L.or_moe_route.argtypes = [_i64, _i64, _i64, _i64, _p, _p, _p]
         L.or_moe_layer0.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p]
+        L.or_moe_ag_layer0.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _i64, _p, _p,
+                                       _p, _p, _p, _p]
         L.or_moe_layer0_rows.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _p, _p, _p, _p,
                                          _i64, _p, _p]
         L.or_moe_layer1.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _i64, _p, _p, _p,
@@ -186,6 +188,27 @@ class Oracle:
         H = np.empty((int(off[-1]), ffn), dtype=np.float64)
         self._L.or_moe_layer0(dt, T, hidden, ffn, topk, n_local, X.ctypes.data, W1.ctypes.data,
                               sp.ctypes.data, off.ctypes.data, H.ctypes.data)
+        return H
+
+    def moe_ag_layer0(self, dt, chunks, W1, sorted_pairs, offsets, topk, arrival=None):
+        """Layer 0 on the token chunks gathered in `arrival` order (by index)."""
+        chunks = [_u16(c) for c in chunks]
+        n = len(chunks)
+        Tc, hidden = chunks[0].shape
+        W1 = _u16(W1)
+        n_local, h2, ffn = W1.shape
+        assert h2 == hidden
+        ptrs = (ctypes.c_void_p * n)(*[c.ctypes.data for c in chunks])
+        arr = None
+        if arrival is not None:
+            arr = np.ascontiguousarray(arrival, dtype=np.int32)
+            assert sorted(arr.tolist()) == list(range(n))
+        sp = np.ascontiguousarray(sorted_pairs, dtype=np.int32)
+        off = np.ascontiguousarray(offsets, dtype=np.int32)
+        H = np.empty((int(off[-1]), ffn), dtype=np.float64)
+        self._L.or_moe_ag_layer0(dt, n, Tc, hidden, ffn, topk, n_local, ptrs,
+                                 None if arr is None else arr.ctypes.data, W1.ctypes.data,
+                                 sp.ctypes.data, off.ctypes.data, H.ctypes.data)
         return H
 
     def moe_layer0_rows(self, dt, X, W1, sorted_pairs, offsets, topk, rows) -> np.ndarray:

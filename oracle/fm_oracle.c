@@ -197,17 +197,24 @@ void or_gemm_entries(int dt, int64_t M, int64_t N, int64_t K,
 /* order of arrival must not change the result.                               */
 /* ------------------------------------------------------------------------- */
 
-void or_ag_gemm(int dt, int64_t n_chunks, int64_t Mc, int64_t N, int64_t K,
-                const uint16_t* const* chunks, const int32_t* arrival,
-                const uint16_t* W, double* C) {
-    int64_t M = n_chunks * Mc;
-    uint16_t* X = (uint16_t*)malloc((size_t)(M * K) * sizeof(uint16_t));
+/* The AllGather itself: chunks land in arrival order and each is copied to */
+/* its place by chunk index.  Returns a malloc'ed [n_chunks*Mc, K] buffer.    */
+static uint16_t* gather_chunks(int64_t n_chunks, int64_t Mc, int64_t K,
+                               const uint16_t* const* chunks, const int32_t* arrival) {
+    uint16_t* X = (uint16_t*)malloc((size_t)(n_chunks * Mc * K) * sizeof(uint16_t));
     for (int64_t a = 0; a < n_chunks; ++a) {
         int64_t c = arrival ? arrival[a] : a;           /* which chunk lands now */
         int64_t dst_chunk = MUTANT(2) ? a : c;           /* placed by arrival slot */
         memcpy(X + dst_chunk * Mc * K, chunks[c], (size_t)(Mc * K) * sizeof(uint16_t));
     }
-    or_gemm(dt, M, N, K, X, W, C);
+    return X;
+}
+
+void or_ag_gemm(int dt, int64_t n_chunks, int64_t Mc, int64_t N, int64_t K,
+                const uint16_t* const* chunks, const int32_t* arrival,
+                const uint16_t* W, double* C) {
+    uint16_t* X = gather_chunks(n_chunks, Mc, K, chunks, arrival);
+    or_gemm(dt, n_chunks * Mc, N, K, X, W, C);
     free(X);
 }
 
@@ -299,6 +306,22 @@ void or_moe_layer0(int dt, int64_t T, int64_t hidden, int64_t ffn, int64_t topk,
             }
         }
     }
+}
+
+/* ------------------------------------------------------------------------- */
+/* O5' MoE layer 0 behind a token AllGather (Flux README: all-gather fused    */
+/* with the grouped GEMM of MoE MLP layer 0).  The expert-parallel ranks'     */
+/* token chunks are gathered (arrival order, placed by chunk index: chunk c   */
+/* holds tokens [c*Tc, (c+1)*Tc)), then layer 0 runs on the gathered tokens.  */
+/* ------------------------------------------------------------------------- */
+
+void or_moe_ag_layer0(int dt, int64_t n_chunks, int64_t Tc, int64_t hidden, int64_t ffn,
+                      int64_t topk, int64_t n_local, const uint16_t* const* chunks,
+                      const int32_t* arrival, const uint16_t* W1,
+                      const int32_t* sorted_pairs, const int32_t* offsets, double* H) {
+    uint16_t* X = gather_chunks(n_chunks, Tc, hidden, chunks, arrival);
+    or_moe_layer0(dt, n_chunks * Tc, hidden, ffn, topk, n_local, X, W1, sorted_pairs, offsets, H);
+    free(X);
 }
 
 /* ------------------------------------------------------------------------- */

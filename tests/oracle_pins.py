@@ -267,6 +267,27 @@ def pin_moe_layer0_bruteforce(o):
     assert np.array_equal(part, H[rows])
 
 
+def pin_moe_ag_layer0_gather(o):
+    """Layer 0 behind a token AllGather: 4 chunks of 6 tokens arriving in
+    every order.  Brute force on the concatenated tokens (numpy decode and
+    fp64 dot products) fixes the placement by chunk index and the gather."""
+    inp, e0, nl, topk, dt = _tiny_moe(seed=71)
+    T = inp["X"].shape[0]
+    n = 4
+    assert T % n == 0
+    chunks = [inp["X"][c * (T // n):(c + 1) * (T // n)] for c in range(n)]
+    off, sp = o.moe_route(inp["topk_ids"], e0, nl)
+    x = np_decode(inp["X"], dt)
+    w1 = np_decode(inp["W1"], dt)
+    ref = np.zeros((int(off[-1]), w1.shape[2]))
+    for e in range(nl):
+        for r in range(off[e], off[e + 1]):
+            ref[r] = x[sp[r] // topk] @ w1[e]
+    for perm in itertools.permutations(range(n)):
+        H = o.moe_ag_layer0(dt, chunks, inp["W1"], sp, off, topk, arrival=list(perm))
+        assert np.abs(H - ref).max() <= 1e-12, perm
+
+
 def pin_moe_layer0_onehot_is_gemm(o):
     T, hidden, ffn = 24, 16, 8
     X = wl.normal_bits((T, hidden), 62, BF16)
@@ -378,7 +399,8 @@ ALL_PINS = [
     pin_ag_concat, pin_ag_arrival_invariance,
     pin_rs_sum_of_slices, pin_rs_split_k_bruteforce, pin_rs_single_rank_is_gemm,
     pin_route_numpy, pin_route_edges, pin_route_routing_workload,
-    pin_moe_layer0_bruteforce, pin_moe_layer0_onehot_is_gemm, pin_moe_layer1_token_loop,
+    pin_moe_layer0_bruteforce, pin_moe_ag_layer0_gather, pin_moe_layer0_onehot_is_gemm,
+    pin_moe_layer1_token_loop,
     pin_moe_identical_experts_chain, pin_moe_ep_ranks_sum,
     pin_golden_mlp, pin_golden_moe,
 ]
