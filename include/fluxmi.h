@@ -197,6 +197,29 @@ fm_status_t fm_moe_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t
                                hipStream_t stream);
 
 /*
+ * fm_moe_ag_gather_gemm -- fm_moe_gather_gemm behind a token AllGather (Flux
+ * README: all-gather fused with the grouped GEMM of MoE MLP layer 0): X is
+ * the gathered token buffer of n_chunks expert-parallel ranks, chunk c
+ * holding tokens [c*T/n_chunks, (c+1)*T/n_chunks), and a tile reads its token
+ * rows only after every chunk they come from has flags[c] >= epoch (the
+ * protocol of fm_ag_gemm; producers as fm_chunk_push / fm_chunk_push_dma).
+ * Rows of an expert are sorted by token, so a tile needs the chunks between
+ * its first and last token, and tiles run in token order within an expert:
+ * the local chunk's rows can start before the others land.  topk_ids covers
+ * all T tokens and must be complete before the call.
+ *   n_chunks  1..64, T % n_chunks == 0; flags device uint32 [n_chunks].
+ *   err_word, spin_limit  as fm_ag_gemm (a wait past the limit writes
+ *             FM_ERR_TIMEOUT there; H is then undefined).
+ * The result equals fm_moe_gather_gemm on the fully gathered X, bit for bit.
+ */
+fm_status_t fm_moe_ag_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn,
+                                  int32_t topk, int32_t expert_begin, int32_t n_local,
+                                  const void* X, const int32_t* topk_ids, const void* W1,
+                                  void* H, int32_t* sorted_pairs, int32_t* expert_offsets,
+                                  int32_t n_chunks, const uint32_t* flags, uint32_t epoch,
+                                  int32_t* err_word, int64_t spin_limit, hipStream_t stream);
+
+/*
  * fm_moe_gemm_scatter -- MoE layer 1 on this rank with the top-k weighted
  * combine fused into the GEMM epilogue (Flux README: grouped GEMM fused with
  * the reduce-scatter of MoE MLP layer 1):

@@ -253,3 +253,102 @@ def test_moe_extreme_expert_counts(oracle, topk, nl, e0):
     ref = oracle.moe_layer1(BF16, Hb, inp["W2"], inp["topk_ids"], inp["topk_weights"], rsp, roff,
                             inp["out_seed"], e0)
     assert_close(host64(out) - inp["out_seed"], ref - inp["out_seed"], "combine")
+
+
+def _moe_ag_run(arr, inp, e0, nl, order, epoch, dt=BF16, spin=0, **push_kw):
+    """Token chunks pushed by the side stream (Arrival) while the fused
+    AllGather + gather-GEMM runs; returns (off, sp, H)."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    ids = inp["topk_ids"]
+    T, topk = ids.shape
+    ffn = inp["W1"].shape[2]
+    H = torch.zeros((T * topk, ffn), dtype=torch.bfloat16, device="cuda:0")
+    sp = torch.full((T * topk,), -1, dtype=torch.int32, device="cuda:0")
+    off = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
+    arr.err.zero_()
+    arr.push(order, epoch, **push_kw)
+    fm.fm_moe_ag_gather_gemm(arr.X, _i32(ids), dev16(inp["W1"], dt), H, sp, off, e0, arr.flags,
+                             epoch, arr.n, err_word=arr.err, spin_limit=spin)
+    arr.join()
+    torch.cuda.synchronize()
+    return off.cpu().numpy(), sp.cpu().numpy(), H
+
+
+@pytest.mark.parametrize("T,n,delay", [(1024, 4, 0), (3000, 8, 3_000_000)])
+def test_moe_ag_gather_random_arrival(oracle, T, n, delay):
+    """Token chunks arriving in a seeded random order (optionally late): the
+    fused layer 0 equals the oracle on the gathered tokens and reproduces
+    fm_moe_gather_gemm on the gathered buffer bit for bit."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    from gpu_util import Arrival
+    hidden, ffn, E, nl, e0 = 256, 264, 16, 8, 0
+    inp = wl.moe_inputs(T, hidden, ffn, E, nl, 2, BF16, seed=T + n, zipf_s=1.2)
+    chunks = inp["X"].reshape(n, T // n, hidden)
+    order = wl.permutation(n, seed=T)
+    say(f"moe ag T={T} chunks={n} order={order.tolist()} delay={delay}")
+    arr = Arrival(chunks, BF16, hidden)
+    arr.poison()
+    off, sp, H = _moe_ag_run(arr, inp, e0, nl, order, arr.next_epoch(), delay_cycles=delay)
+    assert arr.err.item() == 0
+    roff, rsp = oracle.moe_route(inp["topk_ids"], e0, nl)
+    rows = int(roff[-1])
+    assert np.array_equal(off, roff) and np.array_equal(sp[:rows], rsp)
+    ref = oracle.moe_ag_layer0(BF16, list(chunks), inp["W1"], rsp, roff, 2, arrival=order)
+    assert_close(host64(H[:rows]), ref, "moe ag layer0")
+    H2 = torch.zeros_like(H)
+    sp2 = torch.full_like(torch.from_numpy(sp).to("cuda:0"), -1)
+    off2 = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
+    fm.fm_moe_gather_gemm(arr.X, _i32(inp["topk_ids"]), dev16(inp["W1"], BF16), H2, sp2, off2,
+                          e0)
+    torch.cuda.synchronize()
+    assert torch.equal(H[:rows].view(torch.int16), H2[:rows].view(torch.int16))
+
+
+def test_moe_ag_withheld_chunk_times_out():
+    """A token chunk that never arrives: the bounded wait writes
+    FM_ERR_TIMEOUT to err_word and the kernel exits (no hang)."""
+    import tile_gemm_communication_amd as fm
+    from gpu_util import Arrival
+    T, hidden, ffn, n = 512, 128, 64, 4
+    inp = wl.moe_inputs(T, hidden, ffn, 8, 8, 2, BF16, seed=5)
+    arr = Arrival(inp["X"].reshape(n, T // n, hidden), BF16, hidden)
+    _moe_ag_run(arr, inp, 0, 8, [0, 1, 2, 3], arr.next_epoch(), spin=2000, skip=(2,))
+    assert arr.err.item() == fm.FM_ERR_TIMEOUT
+
+
+def test_full_moe_ag_rank0(oracle):
+    """EP=8 rank 0 with the 16384 tokens gathered from 8 ranks (2048 each,
+    the local chunk first, then ring order): routing bit-exact, sampled rows
+    against the oracle, and bit-identical to the non-fused layer 0."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    from gpu_util import Arrival
+    c = wl.MOE_EP8
+    say("full moe ag EP=8 rank 0")
+    inp = wl.moe_inputs(c["T"], c["hidden"], c["ffn"], c["n_experts"], c["n_local"], c["topk"],
+                        BF16, seed=c["seed"], zipf_s=c["zipf_s"])
+    e0, n = c["rank"] * c["n_local"], 8
+    chunks = inp["X"].reshape(n, c["T"] // n, c["hidden"])
+    arr = Arrival(chunks, BF16, c["hidden"])
+    arr.poison()
+    order = list(range(n))
+    off, sp, H = _moe_ag_run(arr, inp, e0, c["n_local"], order, arr.next_epoch(), local=0)
+    assert arr.err.item() == 0
+    roff, rsp = oracle.moe_route(inp["topk_ids"], e0, c["n_local"])
+    rows = int(roff[-1])
+    assert np.array_equal(off, roff) and np.array_equal(sp[:rows], rsp)
+    rng = np.random.default_rng(9)
+    srows = np.unique(np.concatenate([rng.integers(0, rows, 48), roff[:-1], roff[1:] - 1]))
+    srows = srows[(srows >= 0) & (srows < rows)]
+    Hs = oracle.moe_layer0_rows(BF16, inp["X"], inp["W1"], rsp, roff, 2, srows)
+    idx = torch.from_numpy(srows).to("cuda:0")
+    assert_close(host64(H[idx]), Hs, "full moe ag rows")
+    H2 = torch.zeros_like(H)
+    sp2 = torch.full((c["T"] * 2,), -1, dtype=torch.int32, device="cuda:0")
+    off2 = torch.zeros(c["n_local"] + 1, dtype=torch.int32, device="cuda:0")
+    fm.fm_moe_gather_gemm(arr.X, _i32(inp["topk_ids"]), dev16(inp["W1"], BF16), H2, sp2, off2,
+                          e0)
+    torch.cuda.synchronize()
+    assert torch.equal(H[:rows].view(torch.int16), H2[:rows].view(torch.int16))

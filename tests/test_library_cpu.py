@@ -128,6 +128,16 @@ def test_chunk_push_dma_validation():
     assert L.fm_chunk_push_dma(None, P2, 64, P3, 1, None) == fm.FM_ERR_INVALID_ARG
 
 
+def test_moe_ag_gather_validation():
+    L = fm.lib()
+    args = (1, 64, 64, 64, 2, 0, 8, P, P, P, P, P, P)
+    assert L.fm_moe_ag_gather_gemm(*args, 4, None, 1, None, 0, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_moe_ag_gather_gemm(*args, 0, P3, 1, None, 0, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_moe_ag_gather_gemm(*args, 3, P3, 1, None, 0, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_moe_ag_gather_gemm(*args, 65, P3, 1, None, 0, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_moe_ag_gather_gemm(*args, 4, P3, 1, None, -1, None) == fm.FM_ERR_INVALID_ARG
+
+
 def test_oracle_is_not_reachable_from_the_product():
     pkg = os.path.join(ROOT, "tile_gemm_communication_amd")
     for dirpath, _, files in os.walk(pkg):

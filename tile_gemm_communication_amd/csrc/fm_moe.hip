@@ -142,6 +142,13 @@ struct MoeArgs {
   // remaining tiles as 256x128 halves.  tiles_n always counts 256-wide tiles.
   int split, part, g_ref;
   int64_t rows_cap;           // T * topk: an upper bound on the local rows
+  // Layer 0 behind a token AllGather (flags != null): chunk c holds tokens
+  // [c*chunk_tokens, (c+1)*chunk_tokens) and is read after flags[c] >= epoch.
+  const uint32_t* flags;
+  uint32_t chunk_epoch;
+  int64_t chunk_tokens;
+  int32_t* err_word;
+  int64_t chunk_spin;
 };
 
 // Epochs of the combine's tile flags: one per call, process-wide, never 0
@@ -200,6 +207,8 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   // combine: first and last token of every M-tile (all experts, in order)
   __shared__ int s_ftok[SCATTER ? kMaxMTiles : 1];
   __shared__ int s_ltok[SCATTER ? kMaxMTiles : 1];
+  __shared__ int s_abort;
+  uint64_t ready = 0;   // token chunks this workgroup has already acquired
 
   const int t = threadIdx.x;
   if (t <= a.n_local) s_off[t] = a.offsets[t];
@@ -257,6 +266,26 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
     const int m0 = tm * BM;
     const int64_t n0 = ((int64_t)tn * sub_n + sub) * BN;
     if (n0 >= N) continue;   // the right half of an edge tile that lies past N
+
+    if constexpr (!SCATTER) {
+      if (a.flags) {
+        // Token AllGather: rows of an expert are sorted by token, so the tile
+        // needs the chunks from its first row's token to its last row's.
+        if (t == 0) {
+          const int r_last = row_base + min(m0 + BM, rows_e) - 1;
+          const int64_t tok_lo = a.sorted_pairs[row_base + m0] / a.topk;
+          const int64_t tok_hi = a.sorted_pairs[r_last] / a.topk;
+          const bool ok = wait_chunks(a.flags, a.chunk_epoch, (int)(tok_lo / a.chunk_tokens),
+                                      (int)(tok_hi / a.chunk_tokens), ready, a.chunk_spin,
+                                      a.err_word);
+          s_abort = ok ? 0 : 1;
+        }
+        __syncthreads();
+        const int abort_now = s_abort;
+        __syncthreads();
+        if (abort_now) return;   // timed out: err_word is set, H is undefined
+      }
+    }
 
     eng.set_a_base(a.A);
 #pragma unroll
@@ -480,12 +509,15 @@ extern "C" fm_status_t fm_moe_route(int64_t T, int32_t topk, int32_t expert_begi
   return launch_status();
 }
 
-extern "C" fm_status_t fm_moe_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidden,
-                                          int64_t ffn, int32_t topk, int32_t expert_begin,
-                                          int32_t n_local, const void* X,
-                                          const int32_t* topk_ids, const void* W1, void* H,
-                                          int32_t* sorted_pairs, int32_t* expert_offsets,
-                                          hipStream_t stream) {
+namespace fm {
+namespace {
+
+fm_status_t moe_gather_impl(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn, int32_t topk,
+                            int32_t expert_begin, int32_t n_local, const void* X,
+                            const int32_t* topk_ids, const void* W1, void* H,
+                            int32_t* sorted_pairs, int32_t* expert_offsets, int32_t n_chunks,
+                            const uint32_t* flags, uint32_t epoch, int32_t* err_word,
+                            int64_t spin_limit, hipStream_t stream) {
   if (dt != FM_F16 && dt != FM_BF16) return FM_ERR_UNSUPPORTED;
   fm_status_t st = check_route_args(T, topk, n_local, topk_ids, sorted_pairs, expert_offsets);
   if (st != FM_OK) return st;
@@ -493,6 +525,11 @@ extern "C" fm_status_t fm_moe_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidd
   if (T > 0 && ffn > 0 &&
       (!X || !W1 || !H || !aligned16(X) || !aligned16(W1) || !aligned16(H)))
     return FM_ERR_INVALID_ARG;
+  if (flags) {
+    if (n_chunks < 1 || n_chunks > 64 || T % n_chunks || spin_limit < 0 ||
+        (reinterpret_cast<uintptr_t>(flags) & 3u))
+      return FM_ERR_INVALID_ARG;
+  }
   // gathered-row byte offsets are 32-bit
   if (hidden >= (1ll << 22) || ffn >= (1ll << 22) || T * hidden >= (1ll << 31))
     return FM_ERR_UNSUPPORTED;
@@ -511,7 +548,41 @@ extern "C" fm_status_t fm_moe_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidd
   a.topk = topk;
   a.rows_cap = T * topk;
   a.n_local = n_local;
+  if (flags) {
+    a.flags = flags;
+    a.chunk_epoch = epoch;
+    a.chunk_tokens = T / n_chunks;
+    a.err_word = err_word;
+    a.chunk_spin = spin_limit ? spin_limit : (1ll << 24);
+  }
   return launch_moe<false>(dt, moe_tile(false), a, stream);
+}
+
+}  // namespace
+}  // namespace fm
+
+extern "C" fm_status_t fm_moe_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidden,
+                                          int64_t ffn, int32_t topk, int32_t expert_begin,
+                                          int32_t n_local, const void* X,
+                                          const int32_t* topk_ids, const void* W1, void* H,
+                                          int32_t* sorted_pairs, int32_t* expert_offsets,
+                                          hipStream_t stream) {
+  return moe_gather_impl(dt, T, hidden, ffn, topk, expert_begin, n_local, X, topk_ids, W1, H,
+                         sorted_pairs, expert_offsets, 0, nullptr, 0, nullptr, 0, stream);
+}
+
+extern "C" fm_status_t fm_moe_ag_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidden,
+                                             int64_t ffn, int32_t topk, int32_t expert_begin,
+                                             int32_t n_local, const void* X,
+                                             const int32_t* topk_ids, const void* W1, void* H,
+                                             int32_t* sorted_pairs, int32_t* expert_offsets,
+                                             int32_t n_chunks, const uint32_t* flags,
+                                             uint32_t epoch, int32_t* err_word,
+                                             int64_t spin_limit, hipStream_t stream) {
+  if (!flags) return FM_ERR_INVALID_ARG;
+  return moe_gather_impl(dt, T, hidden, ffn, topk, expert_begin, n_local, X, topk_ids, W1, H,
+                         sorted_pairs, expert_offsets, n_chunks, flags, epoch, err_word,
+                         spin_limit, stream);
 }
 
 extern "C" fm_status_t fm_moe_gemm_scatter(fm_dtype_t dt, int64_t T, int64_t hidden,
