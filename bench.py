@@ -146,6 +146,14 @@ class Workload:
         self.ids = torch.from_numpy(ids).to(dev)
         self.wts = torch.from_numpy(inp["topk_weights"]).to(dev)
         self.mout = torch.from_numpy(inp["out_seed"]).to(dev)
+        # token AllGather in front of MoE layer 0: 8 chunks of T/8 tokens, chunk
+        # c from peer c (the local chunk 0 already in place)
+        self.mTc = self.T // self.n
+        self.mpeers = [up(inp["X"][c * self.mTc:(c + 1) * self.mTc], bf16) for c in range(self.n)]
+        self.mXg = torch.empty_like(self.mX)
+        self.mXg[: self.mTc].copy_(self.mpeers[0])
+        self.mflags = torch.zeros(self.n, dtype=torch.int32, device=dev)
+        self.mcounters = torch.zeros(self.n, dtype=torch.int32, device=dev)
         self.H = torch.empty((self.T * self.topk, self.ffn), dtype=bf16, device=dev)
         self.sp = torch.empty(self.T * self.topk, dtype=torch.int32, device=dev)
         self.off = torch.zeros(self.n_local + 1, dtype=torch.int32, device=dev)
@@ -163,25 +171,27 @@ class Workload:
         torch.cuda.synchronize()
 
     # -- pieces of a step ----------------------------------------------------
-    def push_all(self, epoch, events=None):
+    def push_all(self, epoch, events=None, moe=False):
         """Publish the local chunk and push the seven peer chunks, peer i on
         side stream i % 3.  events: optional per-chunk events recorded after
-        each push."""
+        each push.  moe: the token chunks of MoE layer 0 instead of the dense
+        AllGather's row chunks."""
         import tile_gemm_communication_amd as fm
         import torch
+        peers, X, Mc = (self.mpeers, self.mXg, self.mTc) if moe else (self.peers, self.X, self.Mc)
+        flags, counters = (self.mflags, self.mcounters) if moe else (self.flags, self.counters)
         cs = torch.cuda.current_stream()
         for s in self.sides:
             s.wait_stream(cs)
         def push(src, dst, c, s):
             if self.arrival == "dma":
-                fm.fm_chunk_push_dma(src, dst, self.flags[c:c + 1], epoch, stream=s)
+                fm.fm_chunk_push_dma(src, dst, flags[c:c + 1], epoch, stream=s)
             else:
-                fm.fm_chunk_push(src, dst, self.flags[c:c + 1], self.counters[c:c + 1], epoch,
-                                 stream=s)
+                fm.fm_chunk_push(src, dst, flags[c:c + 1], counters[c:c + 1], epoch, stream=s)
         push(None, None, 0, self.sides[0])
         for i, c in enumerate(self.order[1:]):
             s = self.sides[i % self.n_sides]
-            push(self.peers[c], self.X[c * self.Mc:(c + 1) * self.Mc], c, s)
+            push(peers[c], X[c * Mc:(c + 1) * Mc], c, s)
             if events is not None:
                 events[c].record(s)
 
@@ -203,6 +213,12 @@ class Workload:
     def moe0(self):
         import tile_gemm_communication_amd as fm
         fm.fm_moe_gather_gemm(self.mX, self.ids, self.mW1, self.H, self.sp, self.off, self.e0)
+
+    def moe0_ag(self, epoch):
+        import tile_gemm_communication_amd as fm
+        fm.fm_moe_ag_gather_gemm(self.mXg, self.ids, self.mW1, self.H, self.sp, self.off, self.e0,
+                                 self.mflags, epoch, self.n, order=self.order,
+                                 err_word=self.err)
 
     def moe1(self):
         import tile_gemm_communication_amd as fm
@@ -327,6 +343,35 @@ def ect_block(w, iters):
     res["rs_ect_vs_fm_gemm_ms"] = round(res["rs_fused_ms"] - res["rs_nonsplit_fm_gemm_ms"], 4)
     res["rs_ect_naive_ms"] = round(res["rs_naive_chunked_ms"] - nonsplit, 4)
     res["rs_ect_frac_of_nonsplit"] = round(res["rs_ect_ms"] / nonsplit, 4)
+
+    # --- token AllGather + MoE layer 0 --------------------------------------
+    def moe_ns():
+        w.moe0()
+
+    def moe_fused():
+        w.epoch += 1
+        w.push_all(w.epoch, moe=True)
+        if w.serial_arrival:
+            w.join_sides()
+        w.moe0_ag(w.epoch)
+        w.join_sides()
+
+    def moe_naive():
+        # the whole AllGather first, then the layer
+        w.epoch += 1
+        w.push_all(w.epoch, moe=True)
+        w.join_sides()
+        fm.fm_moe_gather_gemm(w.mXg, w.ids, w.mW1, w.H, w.sp, w.off, w.e0)
+
+    log("ECT: token AllGather + MoE layer 0")
+    for name, fn in [("nonsplit", moe_ns), ("fused", moe_fused), ("gather_then_gemm", moe_naive)]:
+        med, best = time_loop(fn, iters, 3)
+        res[f"moe_ag_{name}_ms"] = round(med, 4)
+    res["moe_ag_ect_ms"] = round(res["moe_ag_fused_ms"] - res["moe_ag_nonsplit_ms"], 4)
+    res["moe_ag_ect_naive_ms"] = round(res["moe_ag_gather_then_gemm_ms"]
+                                       - res["moe_ag_nonsplit_ms"], 4)
+    res["moe_ag_ect_frac_of_nonsplit"] = round(res["moe_ag_ect_ms"] / res["moe_ag_nonsplit_ms"], 4)
+    assert int(w.err.item()) == 0, "fm_moe_ag_gather_gemm reported a timeout"
     res["nonsplit_fm_gemm_tflops_4096x12288x6144"] = round(
         w.flop_rs / (res["rs_nonsplit_fm_gemm_ms"] * 1e-3) / 1e12, 1)
     res["nonsplit_hipblaslt_tflops_4096x12288x6144"] = round(

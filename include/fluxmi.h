@@ -204,10 +204,14 @@ fm_status_t fm_moe_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t
  * rows only after every chunk they come from has flags[c] >= epoch (the
  * protocol of fm_ag_gemm; producers as fm_chunk_push / fm_chunk_push_dma).
  * Rows of an expert are sorted by token, so a tile needs the chunks between
- * its first and last token, and tiles run in token order within an expert:
- * the local chunk's rows can start before the others land.  topk_ids covers
- * all T tokens and must be complete before the call.
+ * its first and last token.  Tiles run in bands of a few M-tiles of one
+ * expert, ordered by the expected arrival of the last chunk a band needs, so
+ * the rows of the local and earliest chunks start before the others land.
+ * topk_ids covers all T tokens and must be complete before the call.
  *   n_chunks  1..64, T % n_chunks == 0; flags device uint32 [n_chunks].
+ *   order     host array of n_chunks chunk indices, the expected arrival
+ *             order, or NULL for index order (as fm_ag_gemm; it only orders
+ *             the tiles).
  *   err_word, spin_limit  as fm_ag_gemm (a wait past the limit writes
  *             FM_ERR_TIMEOUT there; H is then undefined).
  * The result equals fm_moe_gather_gemm on the fully gathered X, bit for bit.
@@ -217,7 +221,8 @@ fm_status_t fm_moe_ag_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidden, int6
                                   const void* X, const int32_t* topk_ids, const void* W1,
                                   void* H, int32_t* sorted_pairs, int32_t* expert_offsets,
                                   int32_t n_chunks, const uint32_t* flags, uint32_t epoch,
-                                  int32_t* err_word, int64_t spin_limit, hipStream_t stream);
+                                  const int32_t* order, int32_t* err_word, int64_t spin_limit,
+                                  hipStream_t stream);
 
 /*
  * fm_moe_gemm_scatter -- MoE layer 1 on this rank with the top-k weighted

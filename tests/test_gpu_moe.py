@@ -255,7 +255,7 @@ def test_moe_extreme_expert_counts(oracle, topk, nl, e0):
     assert_close(host64(out) - inp["out_seed"], ref - inp["out_seed"], "combine")
 
 
-def _moe_ag_run(arr, inp, e0, nl, order, epoch, dt=BF16, spin=0, **push_kw):
+def _moe_ag_run(arr, inp, e0, nl, order, epoch, dt=BF16, spin=0, hint=None, **push_kw):
     """Token chunks pushed by the side stream (Arrival) while the fused
     AllGather + gather-GEMM runs; returns (off, sp, H)."""
     import torch
@@ -269,17 +269,20 @@ def _moe_ag_run(arr, inp, e0, nl, order, epoch, dt=BF16, spin=0, **push_kw):
     arr.err.zero_()
     arr.push(order, epoch, **push_kw)
     fm.fm_moe_ag_gather_gemm(arr.X, _i32(ids), dev16(inp["W1"], dt), H, sp, off, e0, arr.flags,
-                             epoch, arr.n, err_word=arr.err, spin_limit=spin)
+                             epoch, arr.n, order=hint, err_word=arr.err, spin_limit=spin)
     arr.join()
     torch.cuda.synchronize()
     return off.cpu().numpy(), sp.cpu().numpy(), H
 
 
-@pytest.mark.parametrize("T,n,delay", [(1024, 4, 0), (3000, 8, 3_000_000)])
-def test_moe_ag_gather_random_arrival(oracle, T, n, delay):
-    """Token chunks arriving in a seeded random order (optionally late): the
-    fused layer 0 equals the oracle on the gathered tokens and reproduces
-    fm_moe_gather_gemm on the gathered buffer bit for bit."""
+@pytest.mark.parametrize("T,n,delay,hint", [(1024, 4, 0, "none"), (3000, 8, 3_000_000, "same"),
+                                            (4096, 8, 1_000_000, "reversed"),
+                                            (2048, 2, 0, "same")])
+def test_moe_ag_gather_random_arrival(oracle, monkeypatch, T, n, delay, hint):
+    """Token chunks arriving in a seeded random order (optionally late), with
+    the arrival hint absent, right or wrong: the fused layer 0 equals the
+    oracle on the gathered tokens and reproduces fm_moe_gather_gemm on the
+    gathered buffer bit for bit."""
     import torch
     import tile_gemm_communication_amd as fm
     from gpu_util import Arrival
@@ -287,10 +290,14 @@ def test_moe_ag_gather_random_arrival(oracle, T, n, delay):
     inp = wl.moe_inputs(T, hidden, ffn, E, nl, 2, BF16, seed=T + n, zipf_s=1.2)
     chunks = inp["X"].reshape(n, T // n, hidden)
     order = wl.permutation(n, seed=T)
-    say(f"moe ag T={T} chunks={n} order={order.tolist()} delay={delay}")
+    hint_order = {"none": None, "same": order.tolist(), "reversed": order.tolist()[::-1]}[hint]
+    if T == 2048:
+        monkeypatch.setenv("FM_MOE_AG_GROUP", "1")   # one band per M-tile
+    say(f"moe ag T={T} chunks={n} order={order.tolist()} delay={delay} hint={hint}")
     arr = Arrival(chunks, BF16, hidden)
     arr.poison()
-    off, sp, H = _moe_ag_run(arr, inp, e0, nl, order, arr.next_epoch(), delay_cycles=delay)
+    off, sp, H = _moe_ag_run(arr, inp, e0, nl, order, arr.next_epoch(), hint=hint_order,
+                             delay_cycles=delay)
     assert arr.err.item() == 0
     roff, rsp = oracle.moe_route(inp["topk_ids"], e0, nl)
     rows = int(roff[-1])

@@ -131,11 +131,17 @@ def test_chunk_push_dma_validation():
 def test_moe_ag_gather_validation():
     L = fm.lib()
     args = (1, 64, 64, 64, 2, 0, 8, P, P, P, P, P, P)
-    assert L.fm_moe_ag_gather_gemm(*args, 4, None, 1, None, 0, None) == fm.FM_ERR_INVALID_ARG
-    assert L.fm_moe_ag_gather_gemm(*args, 0, P3, 1, None, 0, None) == fm.FM_ERR_INVALID_ARG
-    assert L.fm_moe_ag_gather_gemm(*args, 3, P3, 1, None, 0, None) == fm.FM_ERR_INVALID_ARG
-    assert L.fm_moe_ag_gather_gemm(*args, 65, P3, 1, None, 0, None) == fm.FM_ERR_INVALID_ARG
-    assert L.fm_moe_ag_gather_gemm(*args, 4, P3, 1, None, -1, None) == fm.FM_ERR_INVALID_ARG
+    def call(n, flags, order=None, spin=0):
+        o = None if order is None else ctypes.cast((ctypes.c_int32 * len(order))(*order),
+                                                   ctypes.c_void_p)
+        return L.fm_moe_ag_gather_gemm(*args, n, flags, 1, o, None, spin, None)
+    assert call(4, None) == fm.FM_ERR_INVALID_ARG                 # flags required
+    assert call(0, P3) == fm.FM_ERR_INVALID_ARG
+    assert call(3, P3) == fm.FM_ERR_INVALID_ARG                   # T % n_chunks
+    assert call(65, P3) == fm.FM_ERR_INVALID_ARG
+    assert call(4, P3, spin=-1) == fm.FM_ERR_INVALID_ARG
+    assert call(4, P3, order=[0, 1, 1, 2]) == fm.FM_ERR_INVALID_ARG   # not a permutation
+    assert call(4, P3, order=[0, 1, 2, 4]) == fm.FM_ERR_INVALID_ARG
 
 
 def test_oracle_is_not_reachable_from_the_product():

@@ -67,7 +67,7 @@ def lib() -> ctypes.CDLL:
                                      p, p]
     L.fm_moe_ag_gather_gemm.restype = ctypes.c_int
     L.fm_moe_ag_gather_gemm.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32, p, p, p, p,
-                                        p, p, i32, p, u32, p, i64, p]
+                                        p, p, i32, p, u32, p, p, i64, p]
     L.fm_moe_gemm_scatter.restype = ctypes.c_int
     L.fm_moe_gemm_scatter.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, p, p, p, p, p, p, p]
     _lib = L
@@ -213,19 +213,25 @@ def fm_moe_gather_gemm(X, topk_ids, W1, H, sorted_pairs, expert_offsets, expert_
 
 
 def fm_moe_ag_gather_gemm(X, topk_ids, W1, H, sorted_pairs, expert_offsets, expert_begin: int,
-                          flags, epoch: int, n_chunks: int, err_word=None, spin_limit: int = 0,
-                          stream=None) -> None:
+                          flags, epoch: int, n_chunks: int, order=None, err_word=None,
+                          spin_limit: int = 0, stream=None) -> None:
     """fm_moe_gather_gemm behind a token AllGather: token chunk c of X is read
-    after flags[c] >= epoch."""
+    after flags[c] >= epoch; `order` is the expected arrival order."""
     T, hidden = X.shape
     n_local, h2, ffn = W1.shape
     topk = topk_ids.shape[1]
     if h2 != hidden or H.shape[1] != ffn or H.shape[0] < T * topk or W1.dtype != X.dtype:
         raise ValueError("fm_moe_ag_gather_gemm: shape or dtype mismatch")
+    order_arr = None
+    if order is not None:
+        order = [int(c) for c in order]
+        order_arr = (ctypes.c_int32 * len(order))(*order)
     _check("fm_moe_ag_gather_gemm", lib().fm_moe_ag_gather_gemm(
         _dt(X), T, hidden, ffn, topk, int(expert_begin), n_local, _ptr(X), _ptr(topk_ids),
         _ptr(W1), _ptr(H), _ptr(sorted_pairs), _ptr(expert_offsets), int(n_chunks), _ptr(flags),
-        ctypes.c_uint32(epoch & 0xFFFFFFFF), _ptr(err_word), int(spin_limit), _stream(stream)))
+        ctypes.c_uint32(epoch & 0xFFFFFFFF),
+        ctypes.cast(order_arr, ctypes.c_void_p) if order_arr is not None else None,
+        _ptr(err_word), int(spin_limit), _stream(stream)))
 
 
 def fm_moe_gemm_scatter(H, W2, sorted_pairs, expert_offsets, topk_weights, out,

@@ -21,6 +21,7 @@ namespace fm {
 
 constexpr int kMaxLocalExperts = 64;
 constexpr int kMaxMTiles = 1024;                      // token ranges cached in LDS
+constexpr int kMaxBands = 256;                        // bands ordered by arrival in LDS
 constexpr int kRouteThreads = 256;
 constexpr int kRouteWaves = kRouteThreads / 64;
 // Per-chunk expert counts live in the route region of the library's
@@ -149,6 +150,10 @@ struct MoeArgs {
   int64_t chunk_tokens;
   int32_t* err_word;
   int64_t chunk_spin;
+  // Bands of ag_group M-tiles of one expert run in the order of the last
+  // chunk they need to arrive (chunk_pos[c] = arrival position of chunk c).
+  int ag_group;
+  uint8_t chunk_pos[64];
 };
 
 // Epochs of the combine's tile flags: one per call, process-wide, never 0
@@ -208,20 +213,82 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   __shared__ int s_ftok[SCATTER ? kMaxMTiles : 1];
   __shared__ int s_ltok[SCATTER ? kMaxMTiles : 1];
   __shared__ int s_abort;
+  // token AllGather: bands of M-tiles sorted by the arrival of their chunks
+  __shared__ int s_band0[SCATTER ? 1 : kMaxLocalExperts + 1];
+  __shared__ uint8_t s_blvl[SCATTER ? 1 : kMaxBands];
+  __shared__ uint16_t s_bord[SCATTER ? 1 : kMaxBands];   // expert << 8 | band of the expert
+  __shared__ int s_btile0[SCATTER ? 1 : kMaxBands + 1];
   uint64_t ready = 0;   // token chunks this workgroup has already acquired
 
   const int t = threadIdx.x;
+  const int gmb = SCATTER ? 1 : a.ag_group;
   if (t <= a.n_local) s_off[t] = a.offsets[t];
   __syncthreads();
   if (t == 0) {
-    int acc = 0;
+    int acc = 0, nb = 0;
     for (int e = 0; e < a.n_local; ++e) {
+      const int tiles_me = (int)cdiv(s_off[e + 1] - s_off[e], BM);
       s_tile0[e] = acc;
-      acc += (int)cdiv(s_off[e + 1] - s_off[e], BM) * a.tiles_n;
+      acc += tiles_me * a.tiles_n;
+      if constexpr (!SCATTER) {
+        s_band0[e] = nb;
+        nb += (tiles_me + gmb - 1) / gmb;
+      }
     }
     s_tile0[a.n_local] = acc;
+    if constexpr (!SCATTER) s_band0[a.n_local] = nb;
   }
   __syncthreads();
+
+  // Token AllGather: a band of up to ag_group M-tiles of one expert covers an
+  // increasing token range; bands run in the order in which the last chunk
+  // they need arrives (stable, so expert-major within one arrival position).
+  // This only orders the tiles: every tile still waits for its own chunks.
+  bool by_arrival = false;
+  int n_bands = 0;
+  if constexpr (!SCATTER) {
+    n_bands = s_band0[a.n_local];
+    by_arrival = a.flags != nullptr && n_bands <= kMaxBands;
+    if (by_arrival) {
+      for (int g = t; g < n_bands; g += 64 * NW) {
+        int e = 0;
+        while (e + 1 < a.n_local && s_band0[e + 1] <= g) ++e;
+        const int b = g - s_band0[e];
+        const int rows_e = s_off[e + 1] - s_off[e];
+        const int r0 = s_off[e] + b * gmb * BM;
+        const int r1 = s_off[e] + min((b + 1) * gmb * BM, rows_e) - 1;
+        const int c_lo = (int)(a.sorted_pairs[r0] / a.topk / a.chunk_tokens);
+        const int c_hi = (int)(a.sorted_pairs[r1] / a.topk / a.chunk_tokens);
+        int lvl = 0;
+        for (int c = c_lo; c <= c_hi; ++c) lvl = max(lvl, (int)a.chunk_pos[c]);
+        s_blvl[g] = (uint8_t)lvl;
+      }
+      __syncthreads();
+      for (int g = t; g < n_bands; g += 64 * NW) {
+        const int lvl = s_blvl[g];
+        int rank = 0;
+        for (int g2 = 0; g2 < n_bands; ++g2) {
+          const int l2 = s_blvl[g2];
+          rank += (l2 < lvl) | ((l2 == lvl) & (g2 < g));
+        }
+        int e = 0;
+        while (e + 1 < a.n_local && s_band0[e + 1] <= g) ++e;
+        s_bord[rank] = (uint16_t)((e << 8) | (g - s_band0[e]));
+      }
+      __syncthreads();
+      if (t == 0) {
+        int acc = 0;
+        for (int k = 0; k < n_bands; ++k) {
+          const int e = s_bord[k] >> 8, b = s_bord[k] & 255;
+          const int tiles_me = (int)cdiv(s_off[e + 1] - s_off[e], BM);
+          s_btile0[k] = acc;
+          acc += min(gmb, tiles_me - b * gmb) * a.tiles_n;
+        }
+        s_btile0[n_bands] = acc;
+      }
+      __syncthreads();
+    }
+  }
 
   // Combine: token range of every M-tile.  Rows of an expert are sorted by
   // pair id, hence by token, and hold each token at most once, so the tiles
@@ -256,13 +323,27 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
 
   for (int L2 = slot; L2 < n_items; L2 += G) {
     const int L = pos0 + L2 / sub_n, sub = L2 % sub_n;
-    int e = 0;
-    while (e + 1 < a.n_local && s_tile0[e + 1] <= L) ++e;
+    int e = 0, tm, tn;
+    if (by_arrival) {
+      int lo = 0, hi = n_bands - 1;   // last band starting at or before L
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_btile0[mid] <= L) lo = mid; else hi = mid - 1;
+      }
+      e = s_bord[lo] >> 8;
+      const int b = s_bord[lo] & 255;
+      const int tiles_e = (int)cdiv(s_off[e + 1] - s_off[e], BM);
+      const int rows_b = min(gmb, tiles_e - b * gmb);
+      const int li = L - s_btile0[lo];
+      tm = b * gmb + li % rows_b;
+      tn = li / rows_b;
+    } else {
+      while (e + 1 < a.n_local && s_tile0[e + 1] <= L) ++e;
+      const int tiles_e = (int)cdiv(s_off[e + 1] - s_off[e], BM);
+      band_coords(L - s_tile0[e], tiles_e, a.tiles_n, min(a.group_m, tiles_e), tm, tn);
+    }
     const int row_base = s_off[e];
     const int rows_e = s_off[e + 1] - row_base;
-    const int tiles_me = (int)cdiv(rows_e, BM);
-    int tm, tn;
-    band_coords(L - s_tile0[e], tiles_me, a.tiles_n, min(a.group_m, tiles_me), tm, tn);
     const int m0 = tm * BM;
     const int64_t n0 = ((int64_t)tn * sub_n + sub) * BN;
     if (n0 >= N) continue;   // the right half of an edge tile that lies past N
@@ -414,6 +495,19 @@ MoeTile moe_tile(bool scatter) {
   return {256, 256, nw_default};
 }
 
+// M-tiles per band of the token-AllGather order.  At the EP=8 shape two
+// 256-row tiles of one expert span about a quarter of a 2048-token chunk, so
+// the first waves need only the earliest chunks.  Measured with copy-engine
+// arrival (all chunks in ~0.3 ms): ECT 0.11 ms with bands of 2, 0.16 ms with
+// whole experts; with kernel copies (~0.13 ms) the band size hardly matters.
+int moe_ag_group() {
+  if (const char* env = std::getenv("FM_MOE_AG_GROUP")) {
+    const int g = std::atoi(env);
+    if (g >= 1 && g <= 16) return g;
+  }
+  return 2;
+}
+
 template <bool SCATTER>
 void launch_moe_part(fm_dtype_t dt, MoeTile cfg, const MoeArgs& a, hipStream_t stream);
 
@@ -516,8 +610,8 @@ fm_status_t moe_gather_impl(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ff
                             int32_t expert_begin, int32_t n_local, const void* X,
                             const int32_t* topk_ids, const void* W1, void* H,
                             int32_t* sorted_pairs, int32_t* expert_offsets, int32_t n_chunks,
-                            const uint32_t* flags, uint32_t epoch, int32_t* err_word,
-                            int64_t spin_limit, hipStream_t stream) {
+                            const uint32_t* flags, uint32_t epoch, const int32_t* order,
+                            int32_t* err_word, int64_t spin_limit, hipStream_t stream) {
   if (dt != FM_F16 && dt != FM_BF16) return FM_ERR_UNSUPPORTED;
   fm_status_t st = check_route_args(T, topk, n_local, topk_ids, sorted_pairs, expert_offsets);
   if (st != FM_OK) return st;
@@ -525,10 +619,18 @@ fm_status_t moe_gather_impl(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ff
   if (T > 0 && ffn > 0 &&
       (!X || !W1 || !H || !aligned16(X) || !aligned16(W1) || !aligned16(H)))
     return FM_ERR_INVALID_ARG;
+  uint8_t pos[64] = {};
   if (flags) {
     if (n_chunks < 1 || n_chunks > 64 || T % n_chunks || spin_limit < 0 ||
         (reinterpret_cast<uintptr_t>(flags) & 3u))
       return FM_ERR_INVALID_ARG;
+    bool seen[64] = {};
+    for (int i = 0; i < n_chunks; ++i) {
+      const int c = order ? order[i] : i;
+      if (c < 0 || c >= n_chunks || seen[c]) return FM_ERR_INVALID_ARG;
+      seen[c] = true;
+      pos[c] = (uint8_t)i;
+    }
   }
   // gathered-row byte offsets are 32-bit
   if (hidden >= (1ll << 22) || ffn >= (1ll << 22) || T * hidden >= (1ll << 31))
@@ -554,7 +656,9 @@ fm_status_t moe_gather_impl(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ff
     a.chunk_tokens = T / n_chunks;
     a.err_word = err_word;
     a.chunk_spin = spin_limit ? spin_limit : (1ll << 24);
+    std::memcpy(a.chunk_pos, pos, sizeof(pos));
   }
+  a.ag_group = moe_ag_group();
   return launch_moe<false>(dt, moe_tile(false), a, stream);
 }
 
@@ -568,7 +672,8 @@ extern "C" fm_status_t fm_moe_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidd
                                           int32_t* sorted_pairs, int32_t* expert_offsets,
                                           hipStream_t stream) {
   return moe_gather_impl(dt, T, hidden, ffn, topk, expert_begin, n_local, X, topk_ids, W1, H,
-                         sorted_pairs, expert_offsets, 0, nullptr, 0, nullptr, 0, stream);
+                         sorted_pairs, expert_offsets, 0, nullptr, 0, nullptr, nullptr, 0,
+                         stream);
 }
 
 extern "C" fm_status_t fm_moe_ag_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidden,
@@ -577,11 +682,12 @@ extern "C" fm_status_t fm_moe_ag_gather_gemm(fm_dtype_t dt, int64_t T, int64_t h
                                              const int32_t* topk_ids, const void* W1, void* H,
                                              int32_t* sorted_pairs, int32_t* expert_offsets,
                                              int32_t n_chunks, const uint32_t* flags,
-                                             uint32_t epoch, int32_t* err_word,
-                                             int64_t spin_limit, hipStream_t stream) {
+                                             uint32_t epoch, const int32_t* order,
+                                             int32_t* err_word, int64_t spin_limit,
+                                             hipStream_t stream) {
   if (!flags) return FM_ERR_INVALID_ARG;
   return moe_gather_impl(dt, T, hidden, ffn, topk, expert_begin, n_local, X, topk_ids, W1, H,
-                         sorted_pairs, expert_offsets, n_chunks, flags, epoch, err_word,
+                         sorted_pairs, expert_offsets, n_chunks, flags, epoch, order, err_word,
                          spin_limit, stream);
 }
 
