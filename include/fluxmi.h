@@ -10,8 +10,10 @@
  *   fm_moe_gather_gemm   token gather fused with grouped expert GEMM (MoE layer 0)
  *   fm_moe_gemm_scatter  grouped expert GEMM fused with top-k weighted
  *                        scatter-reduce (MoE layer 1)
- * plus the producer half of the chunk-arrival protocol (fm_chunk_push) and
- * the routing index on its own (fm_moe_route).
+ * plus the AllGather variants fm_ag_gemm_pull (chunks read in place) and
+ * fm_moe_ag_gather_gemm (MoE layer 0 behind a token AllGather), the producer
+ * half of the chunk-arrival protocol (fm_chunk_push, fm_chunk_push_dma,
+ * fm_chunk_signal_paced) and the routing index on its own (fm_moe_route).
  *
  * Conventions for every call:
  *  - All matrices are dense and row-major.  A / X are [M, K]; B / W are [K, N].
@@ -106,6 +108,41 @@ fm_status_t fm_ag_gemm(fm_dtype_t dt, int64_t M, int64_t N, int64_t K, int32_t n
                        const void* X, const void* W, void* C,
                        const uint32_t* flags, uint32_t epoch, const int32_t* order,
                        int32_t* err_word, int64_t spin_limit, hipStream_t stream);
+
+/*
+ * fm_ag_gemm_pull -- fm_ag_gemm in pull mode (FLUX review, "拉取 vs 推送数据
+ * 传输": the compute tiles fetch the communicated data themselves).  No
+ * gathered buffer exists: chunk c (rows [c*M/n_chunks, (c+1)*M/n_chunks) of
+ * the gathered activation) is read in place from chunks[c], e.g. a peer's
+ * buffer mapped into this process, once flags[c] >= epoch.
+ *   chunks   host array of n_chunks device pointers, each to a 16-byte
+ *            aligned [M/n_chunks, K] row-major block.
+ *   W, C, n_chunks, flags, epoch, order, err_word, spin_limit  as fm_ag_gemm.
+ * Row tiles are cut per chunk, so no tile reads two buffers; a chunk whose
+ * row count is not a multiple of the tile height ends in a partial tile.
+ * The result equals fm_gemm on the concatenated chunks, bit for bit.
+ */
+fm_status_t fm_ag_gemm_pull(fm_dtype_t dt, int64_t M, int64_t N, int64_t K, int32_t n_chunks,
+                            const void* const* chunks, const void* W, void* C,
+                            const uint32_t* flags, uint32_t epoch, const int32_t* order,
+                            int32_t* err_word, int64_t spin_limit, hipStream_t stream);
+
+/*
+ * fm_chunk_signal_paced -- emulated arrival at link speed: publish
+ * flags[order[a]] = epoch (release, device scope) once arrive_ns[a]
+ * nanoseconds have passed since this call's kernel started, for a = 0 ..
+ * n_chunks-1.  The chunk data must already be in place (pull mode, or a
+ * pre-filled gathered buffer); only the signals are timed, as a peer's
+ * transfer over a link of known bandwidth would deliver them (the review's
+ * "拉取 vs 推送数据传输" with the link as the only cost).  One workgroup of one
+ * active lane, sleeping between signals, so it takes no measurable compute
+ * from a kernel running beside it.
+ *   order      host array, a permutation of 0..n_chunks-1, or NULL (index order).
+ *   arrive_ns  host array of n_chunks non-decreasing times in [0, 1e9].
+ * Times use the device's constant-rate wall clock (hipDeviceAttributeWallClockRate).
+ */
+fm_status_t fm_chunk_signal_paced(uint32_t* flags, int32_t n_chunks, const int32_t* order,
+                                  const int64_t* arrive_ns, uint32_t epoch, hipStream_t stream);
 
 /*
  * fm_chunk_push -- producer side of the chunk-arrival protocol: copy `bytes`

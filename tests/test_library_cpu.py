@@ -128,6 +128,51 @@ def test_chunk_push_dma_validation():
     assert L.fm_chunk_push_dma(None, P2, 64, P3, 1, None) == fm.FM_ERR_INVALID_ARG
 
 
+def _arr(ctype, vals):
+    return ctypes.cast((ctype * len(vals))(*vals), ctypes.c_void_p)
+
+
+def test_ag_gemm_pull_validation():
+    L = fm.lib()
+    chunks4 = _arr(ctypes.c_void_p, [0x10000, 0x20000, 0x30000, 0x40000])
+
+    def call(M=256, n=4, chunks=chunks4, W=P, C=P2, flags=P3, order=None, spin=0, K=64):
+        return L.fm_ag_gemm_pull(0, M, 64, K, n, chunks, W, C, flags, 1, order, None, spin, None)
+    assert call(n=3) == fm.FM_ERR_INVALID_ARG                          # M % n_chunks
+    assert call(n=0) == fm.FM_ERR_INVALID_ARG
+    assert call(chunks=None) == fm.FM_ERR_INVALID_ARG
+    assert call(flags=None) == fm.FM_ERR_INVALID_ARG
+    assert call(K=60) == fm.FM_ERR_INVALID_ARG                         # K % 8
+    assert call(spin=-1) == fm.FM_ERR_INVALID_ARG
+    assert call(chunks=_arr(ctypes.c_void_p, [0x10000, 0x20000, 0, 0x40000])) == \
+        fm.FM_ERR_INVALID_ARG                                          # a null chunk
+    assert call(chunks=_arr(ctypes.c_void_p, [0x10000, 0x20008, 0x30000, 0x40000])) == \
+        fm.FM_ERR_INVALID_ARG                                          # misaligned chunk
+    assert call(order=_arr(ctypes.c_int32, [0, 0, 1, 2])) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_ag_gemm_pull(2, 256, 64, 64, 4, chunks4, P, P2, P3, 1, None, None, 0, None) == \
+        fm.FM_ERR_UNSUPPORTED                                          # fp32 operands
+    assert call(M=0) == fm.FM_OK                                       # nothing to do
+
+
+def test_chunk_signal_paced_validation():
+    L = fm.lib()
+    t = _arr(ctypes.c_int64, [0, 10, 20, 30])
+    assert L.fm_chunk_signal_paced(None, 4, None, t, 1, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_chunk_signal_paced(ctypes.c_void_p(0x30002), 4, None, t, 1, None) == \
+        fm.FM_ERR_INVALID_ARG                                          # flag alignment
+    assert L.fm_chunk_signal_paced(P3, 0, None, t, 1, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_chunk_signal_paced(P3, 65, None, t, 1, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_chunk_signal_paced(P3, 4, None, None, 1, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_chunk_signal_paced(P3, 4, None, _arr(ctypes.c_int64, [0, 20, 10, 30]), 1,
+                                   None) == fm.FM_ERR_INVALID_ARG     # decreasing
+    assert L.fm_chunk_signal_paced(P3, 4, None, _arr(ctypes.c_int64, [0, 0, 0, 2 * 10**9]), 1,
+                                   None) == fm.FM_ERR_INVALID_ARG     # beyond one second
+    assert L.fm_chunk_signal_paced(P3, 4, None, _arr(ctypes.c_int64, [-1, 0, 0, 0]), 1,
+                                   None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_chunk_signal_paced(P3, 4, _arr(ctypes.c_int32, [0, 1, 2, 2]), t, 1, None) == \
+        fm.FM_ERR_INVALID_ARG                                          # not a permutation
+
+
 def test_moe_ag_gather_validation():
     L = fm.lib()
     args = (1, 64, 64, 64, 2, 0, 8, P, P, P, P, P, P)

@@ -20,8 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libfluxmi.so")
 FM_OK, FM_ERR_INVALID_ARG, FM_ERR_UNSUPPORTED, FM_ERR_HIP, FM_ERR_TIMEOUT = range(5)
 FM_F16, FM_BF16, FM_F32 = 0, 1, 2
 
-EXPORTS = ("fm_version", "fm_status_str", "fm_gemm", "fm_ag_gemm", "fm_chunk_push",
-           "fm_chunk_push_dma",
+EXPORTS = ("fm_version", "fm_status_str", "fm_gemm", "fm_ag_gemm", "fm_ag_gemm_pull",
+           "fm_chunk_push", "fm_chunk_push_dma", "fm_chunk_signal_paced",
            "fm_gemm_rs", "fm_moe_route", "fm_moe_gather_gemm", "fm_moe_ag_gather_gemm",
            "fm_moe_gemm_scatter")
 
@@ -54,6 +54,11 @@ def lib() -> ctypes.CDLL:
     L.fm_gemm.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, p, p, p, p]
     L.fm_ag_gemm.restype = ctypes.c_int
     L.fm_ag_gemm.argtypes = [ctypes.c_int, i64, i64, i64, i32, p, p, p, p, u32, p, p, i64, p]
+    L.fm_ag_gemm_pull.restype = ctypes.c_int
+    L.fm_ag_gemm_pull.argtypes = [ctypes.c_int, i64, i64, i64, i32, p, p, p, p, u32, p, p, i64,
+                                  p]
+    L.fm_chunk_signal_paced.restype = ctypes.c_int
+    L.fm_chunk_signal_paced.argtypes = [p, i32, p, p, u32, p]
     L.fm_chunk_push.restype = ctypes.c_int
     L.fm_chunk_push.argtypes = [p, p, i64, p, p, u32, i32, p]
     L.fm_chunk_push_dma.restype = ctypes.c_int
@@ -150,6 +155,42 @@ def fm_ag_gemm(X, W, C, flags, epoch: int, n_chunks: int, order=None, err_word=N
         ctypes.c_uint32(epoch & 0xFFFFFFFF),
         ctypes.cast(order_arr, ctypes.c_void_p) if order_arr is not None else None,
         _ptr(err_word), int(spin_limit), _stream(stream)))
+
+
+def _order_arg(order):
+    if order is None:
+        return None
+    order = [int(c) for c in order]
+    return (ctypes.c_int32 * len(order))(*order)
+
+
+def fm_ag_gemm_pull(chunks, W, C, flags, epoch: int, order=None, err_word=None,
+                    spin_limit: int = 0, stream=None) -> None:
+    """C = concat(chunks) @ W, each chunk read in place after flags[c] >= epoch."""
+    n = len(chunks)
+    Mc, K = chunks[0].shape
+    K2, N = W.shape
+    M = n * Mc
+    if (K2 != K or tuple(C.shape) != (M, N) or C.dtype != W.dtype
+            or any(tuple(x.shape) != (Mc, K) or x.dtype != W.dtype for x in chunks)):
+        raise ValueError("fm_ag_gemm_pull: shape or dtype mismatch")
+    ptrs = (ctypes.c_void_p * n)(*[_ptr(x) for x in chunks])
+    o = _order_arg(order)
+    _check("fm_ag_gemm_pull", lib().fm_ag_gemm_pull(
+        _dt(W), M, N, K, n, ctypes.cast(ptrs, ctypes.c_void_p), _ptr(W), _ptr(C), _ptr(flags),
+        ctypes.c_uint32(epoch & 0xFFFFFFFF),
+        ctypes.cast(o, ctypes.c_void_p) if o is not None else None,
+        _ptr(err_word), int(spin_limit), _stream(stream)))
+
+
+def fm_chunk_signal_paced(flags, arrive_ns, epoch: int, order=None, stream=None) -> None:
+    """Publish flags[order[a]] = epoch once arrive_ns[a] ns have passed on the device."""
+    n = len(arrive_ns)
+    t = (ctypes.c_int64 * n)(*[int(x) for x in arrive_ns])
+    o = _order_arg(order)
+    _check("fm_chunk_signal_paced", lib().fm_chunk_signal_paced(
+        _ptr(flags), n, ctypes.cast(o, ctypes.c_void_p) if o is not None else None,
+        ctypes.cast(t, ctypes.c_void_p), ctypes.c_uint32(epoch & 0xFFFFFFFF), _stream(stream)))
 
 
 def fm_chunk_push(src, dst, flag, counter, epoch: int, n_workgroups: int = 0,

@@ -20,7 +20,8 @@ namespace fm {
 
 // RS: ReduceScatter epilogue for tiles that never straddle a slice (slice
 // rows a multiple of BM) with plain adds; RSG: any slice size, or atomic adds.
-enum class Mode : int { Gemm = 0, AG = 1, RS = 2, RSG = 3 };
+// AGP: AllGather in pull mode, each chunk read in place from its own buffer.
+enum class Mode : int { Gemm = 0, AG = 1, RS = 2, RSG = 3, AGP = 4 };
 
 constexpr int kMaxRanks = 16;
 // In-tile byte offsets are 32-bit (tile rows x row pitch), which bounds each
@@ -39,6 +40,11 @@ struct DenseArgs {
   int64_t chunk_rows;
   int64_t spin_limit;
   uint32_t epoch;
+  // AllGather, pull mode: chunk c's rows live at chunk_a[c]; M-tile tm is
+  // tile tm % tiles_per_chunk of chunk tm / tiles_per_chunk, so no tile
+  // straddles two buffers (a ragged chunk ends in a partial tile).
+  int tiles_per_chunk;
+  const char* chunk_a[kMaxChunks];
   // ReduceScatter: destination slices
   int32_t atomic;
   int64_t slice_rows;
@@ -60,17 +66,18 @@ __device__ __forceinline__ void store_run(char* C, int64_t idx, const f32x4& v) 
   }
 }
 
-// Point the engine's DMA at the A rows [m0, m0+BM) (clamped to M) and the B
-// columns [n0, n0+BN) of one tile.
+// Point the engine's DMA at the `rows` A rows starting at a_tile (the tile's
+// first row; rows past the last are clamped to it) and the B columns
+// [n0, n0+BN) of one tile.
 template <class Eng>
-__device__ __forceinline__ void setup_operands(Eng& eng, const DenseArgs& args, int64_t m0,
-                                               int64_t n0) {
-  const int64_t M = args.M, N = args.N, K = args.K;
-  eng.set_a_base(args.A + m0 * K * 2);
+__device__ __forceinline__ void setup_operands(Eng& eng, const DenseArgs& args,
+                                               const char* a_tile, int rows, int64_t n0) {
+  const int64_t N = args.N, K = args.K;
+  eng.set_a_base(a_tile);
 #pragma unroll
   for (int i = 0; i < Eng::A_DMA; ++i) {
-    const int64_t row = min(m0 + eng.a_dma_row(i), M - 1);
-    eng.set_a(i, (uint32_t)((row - m0) * K * 2));
+    const int row = min(eng.a_dma_row(i), rows - 1);
+    eng.set_a(i, (uint32_t)(row * K * 2));
   }
   eng.set_b(args.B, N * 2, n0, N);
 }
@@ -79,9 +86,8 @@ __device__ __forceinline__ void setup_operands(Eng& eng, const DenseArgs& args, 
 // fp32) and store runs of 4 columns, a wave covering whole rows per access.
 template <class E, bool OUT32, class Eng>
 __device__ __forceinline__ void store_tile(Eng& eng, const DenseArgs& args, int64_t m0,
-                                           int64_t n0) {
-  const int64_t M = args.M, N = args.N;
-  const int64_t m_end = min(m0 + Eng::BM_, M);
+                                           int64_t m_end, int64_t n0) {
+  const int64_t N = args.N;
   const int col = eng.ep_col();
   const bool col_ok = n0 + col < N;
   constexpr int EB = OUT32 ? 4 : 2;
@@ -119,12 +125,30 @@ __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args)
     int tm_pos, tn;
     band_coords(P, args.order.tiles_m, args.order.tiles_n, args.order.group_m, tm_pos, tn);
     const int tm = args.order.has_morder ? (int)args.order.morder[tm_pos] : tm_pos;
-    const int64_t m0 = (int64_t)tm * BM;
     const int64_t n0 = ((int64_t)tn * args.sub_n + sub) * BN;
-    const int64_t m_end = min(m0 + BM, M);
+    int64_t m0, m_end;       // output rows of the tile
+    const char* a_tile;      // its first A row
+    if constexpr (MODE == Mode::AGP) {
+      const int c = tm / args.tiles_per_chunk;
+      const int64_t r0 = (int64_t)(tm - c * args.tiles_per_chunk) * BM;
+      m0 = c * args.chunk_rows + r0;
+      m_end = c * args.chunk_rows + min(r0 + BM, args.chunk_rows);
+      // The chunk index is uniform, but the table lookup is not seen as such:
+      // the DMA base must sit in scalar registers.  readfirstlane yields a
+      // signed int, so each half goes through uint32_t before widening (a
+      // sign-extended low half would corrupt the upper address bits).
+      const uint64_t pa = (uint64_t)(uintptr_t)(args.chunk_a[c] + r0 * K * 2);
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)pa);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(pa >> 32));
+      a_tile = (const char*)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+    } else {
+      m0 = (int64_t)tm * BM;
+      m_end = min(m0 + BM, M);
+      a_tile = args.A + m0 * K * 2;
+    }
     if (n0 >= N) continue;   // a part of an edge tile that lies past N
 
-    if constexpr (MODE == Mode::AG) {
+    if constexpr (MODE == Mode::AG || MODE == Mode::AGP) {
       // Tile prologue: wait for every chunk overlapping rows [m0, m_end).
       if (threadIdx.x == 0) {
         const bool ok = wait_chunks(args.flags, args.epoch, (int)(m0 / args.chunk_rows),
@@ -138,7 +162,7 @@ __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args)
       if (abort_now) return;
     }
 
-    setup_operands(eng, args, m0, n0);
+    setup_operands(eng, args, a_tile, (int)(m_end - m0), n0);
     eng.run();
 
     // Epilogue through the LDS staging regions: each global access of a wave
@@ -208,7 +232,7 @@ __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args)
         }
       }
     } else {
-      store_tile<E, OUT32>(eng, args, m0, n0);
+      store_tile<E, OUT32>(eng, args, m0, m_end, n0);
     }
     eng.ep_end();
   }
@@ -333,7 +357,7 @@ fm_status_t launch_dense(fm_dtype_t dt, TileCfg cfg, DenseArgs& args, hipStream_
   if (split_tail_ok(cfg, T, G)) {
     const int rem = T % G, full = T - rem;
     const TileCfg half{cfg.bm, 128, 4};
-    if (MODE == Mode::AG) {
+    if (MODE == Mode::AG || MODE == Mode::AGP) {
       // AllGather: the halves take the first positions (the chunks that
       // arrive first), so the wave that may wait on arrivals is made of the
       // shorter tiles, and the full tiles run once every chunk is likely in.
@@ -438,6 +462,51 @@ extern "C" fm_status_t fm_ag_gemm(fm_dtype_t dt, int64_t M, int64_t N, int64_t K
   }
   set_morder(args.order, key);
   return launch_dense<Mode::AG, false>(dt, cfg, args, stream);
+}
+
+extern "C" fm_status_t fm_ag_gemm_pull(fm_dtype_t dt, int64_t M, int64_t N, int64_t K,
+                                       int32_t n_chunks, const void* const* chunks,
+                                       const void* W, void* C, const uint32_t* flags,
+                                       uint32_t epoch, const int32_t* order, int32_t* err_word,
+                                       int64_t spin_limit, hipStream_t stream) {
+  if (!valid_ab(dt)) return FM_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 0 || N % 8 || K % 8) return FM_ERR_INVALID_ARG;
+  if (n_chunks < 1 || n_chunks > kMaxChunks || M % n_chunks) return FM_ERR_INVALID_ARG;
+  if (!chunks || !W || !C || !flags || !aligned16(W) || !aligned16(C)) return FM_ERR_INVALID_ARG;
+  for (int c = 0; c < n_chunks; ++c)
+    if (!chunks[c] || !aligned16(chunks[c])) return FM_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(flags) & 3u) || spin_limit < 0) return FM_ERR_INVALID_ARG;
+  std::vector<int> pos(n_chunks, -1);
+  for (int a = 0; a < n_chunks; ++a) {
+    const int c = order ? order[a] : a;
+    if (c < 0 || c >= n_chunks || pos[c] != -1) return FM_ERR_INVALID_ARG;
+    pos[c] = a;
+  }
+  if (M == 0 || N == 0) return FM_OK;
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FM_ERR_UNSUPPORTED;
+  const int64_t Mc = M / n_chunks;
+  // The tile shape is chosen as for fm_ag_gemm; tiles are then cut per chunk.
+  const TileCfg cfg = choose_tile(M, N, device_cu_count());
+  const int tpc = (int)cdiv(Mc, cfg.bm);
+  DenseArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.B = (const char*)W;
+  args.C = (char*)C;
+  args.M = M;
+  args.N = N;
+  args.K = K;
+  args.flags = flags;
+  args.epoch = epoch;
+  args.chunk_rows = Mc;
+  args.err_word = err_word;
+  args.spin_limit = spin_limit ? spin_limit : (1ll << 24);
+  args.tiles_per_chunk = tpc;
+  for (int c = 0; c < n_chunks; ++c) args.chunk_a[c] = (const char*)chunks[c];
+  fill_order(args.order, (int64_t)n_chunks * tpc * cfg.bm, N, cfg);
+  std::vector<int> key(args.order.tiles_m);
+  for (int tm = 0; tm < args.order.tiles_m; ++tm) key[tm] = pos[tm / tpc];
+  set_morder(args.order, key);
+  return launch_dense<Mode::AGP, false>(dt, cfg, args, stream);
 }
 
 extern "C" fm_status_t fm_gemm_rs(fm_dtype_t dt, int64_t M, int64_t N, int64_t K,

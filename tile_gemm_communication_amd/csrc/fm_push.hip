@@ -8,6 +8,7 @@
 // signal) and the push mode of the FLUX review ("拉取 vs 推送数据传输"), with
 // the peer's buffer being local HBM on one GPU.
 #include <algorithm>
+#include <cstring>
 
 #include "fm_common.hpp"
 
@@ -44,9 +45,61 @@ __global__ __launch_bounds__(256) void push_kernel(const u32x4* __restrict__ src
   }
 }
 
+// Paced arrival: the a-th flag of the schedule is published once the
+// device's constant-rate wall clock has advanced by `at[a]` ticks since the
+// kernel started.  One lane does the work; the wait is bounded by the last
+// arrival time, which the host limits.
+struct PacedArgs {
+  uint32_t* flags;
+  uint32_t epoch;
+  int32_t n;
+  int32_t chunk[64];
+  uint64_t at[64];
+};
+
+__global__ __launch_bounds__(64) void paced_kernel(const PacedArgs p) {
+  if (threadIdx.x != 0) return;
+  const uint64_t t0 = wall_clock64();
+  for (int a = 0; a < p.n; ++a) {
+    while (wall_clock64() - t0 < p.at[a]) __builtin_amdgcn_s_sleep(4);
+    __hip_atomic_store(p.flags + p.chunk[a], p.epoch, __ATOMIC_RELEASE,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 }  // namespace fm
 
 using namespace fm;
+
+extern "C" fm_status_t fm_chunk_signal_paced(uint32_t* flags, int32_t n_chunks,
+                                             const int32_t* order, const int64_t* arrive_ns,
+                                             uint32_t epoch, hipStream_t stream) {
+  if (!flags || (reinterpret_cast<uintptr_t>(flags) & 3u) || !arrive_ns) return FM_ERR_INVALID_ARG;
+  if (n_chunks < 1 || n_chunks > 64) return FM_ERR_INVALID_ARG;
+  PacedArgs p;
+  std::memset(&p, 0, sizeof(p));
+  p.flags = flags;
+  p.epoch = epoch;
+  p.n = n_chunks;
+  bool seen[64] = {};
+  for (int a = 0; a < n_chunks; ++a) {
+    const int c = order ? order[a] : a;
+    if (c < 0 || c >= n_chunks || seen[c]) return FM_ERR_INVALID_ARG;
+    seen[c] = true;
+    // arrival times: non-decreasing, at most one second
+    if (arrive_ns[a] < 0 || arrive_ns[a] > 1000000000ll || (a > 0 && arrive_ns[a] < arrive_ns[a - 1]))
+      return FM_ERR_INVALID_ARG;
+    p.chunk[a] = c;
+  }
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+    return FM_ERR_HIP;
+  for (int a = 0; a < n_chunks; ++a)   // round up: a signal is never early
+    p.at[a] = (uint64_t)((arrive_ns[a] * (int64_t)khz + 999999) / 1000000);
+  hipLaunchKernelGGL(paced_kernel, dim3(1), dim3(64), 0, stream, p);
+  return launch_status();
+}
 
 extern "C" fm_status_t fm_chunk_push(const void* src, void* dst, int64_t bytes, uint32_t* flag,
                                      uint32_t* counter, uint32_t epoch, int32_t n_workgroups,
