@@ -245,6 +245,9 @@ class Workload:
         if evs: evs[4].record(cs)
 
 
+LINK_BYTES_PER_S = 153e9   # one MI355X xGMI link, per direction
+
+
 def time_loop(fn, iters, warmup):
     """Median per-iteration time (ms) of fn() on the current stream, with events."""
     import torch
@@ -311,6 +314,48 @@ def ect_block(w, iters):
     res["ag_ect_naive_ms"] = round(res["ag_naive_chunked_ms"] - nonsplit, 4)
     res["ag_ect_frac_of_nonsplit"] = round(res["ag_ect_ms"] / nonsplit, 4)
     assert int(w.err.item()) == 0, "fm_ag_gemm reported a timeout"
+
+    # --- AllGather-GEMM in pull mode, chunks signalled at link speed --------
+    # One xGMI link moves a 12.58 MB chunk in t_link = bytes / 153 GB/s.  Ring:
+    # the chunk at position a lands at a * t_link.  Direct: every peer pushes
+    # over its own link, so all seven land at t_link.  The chunks are read in
+    # place from the peers' buffers: no copy competes with the GEMM.
+    t_link = int(w.Mc * w.K1 * 2 / LINK_BYTES_PER_S * 1e9)
+    sched = {"ring": [a * t_link for a in range(w.n)],
+             "direct": [0] + [t_link] * (w.n - 1)}
+
+    def pull(times):
+        def fn():
+            w.epoch += 1
+            s = w.sides[0]
+            s.wait_stream(cs)
+            fm.fm_chunk_signal_paced(w.flags, times, w.epoch, order=w.order, stream=s)
+            fm.fm_ag_gemm_pull(w.peers, w.W1, w.Out1, w.flags, w.epoch, order=w.order,
+                               err_word=w.err)
+            cs.wait_stream(s)
+        return fn
+
+    def pull_naive(times):
+        def fn():
+            w.epoch += 1
+            s = w.sides[0]
+            s.wait_stream(cs)
+            fm.fm_chunk_signal_paced(w.flags, times, w.epoch, order=w.order, stream=s)
+            cs.wait_stream(s)                   # the whole AllGather first
+            fm.fm_gemm(w.X, w.W1, w.Out1)
+        return fn
+
+    log("ECT: pull-mode AllGather-GEMM, link-paced arrival")
+    res["pull_link_chunk_us"] = round(t_link / 1e3, 1)
+    for name, times in sched.items():
+        med, _ = time_loop(pull(times), iters, 3)
+        res[f"pull_{name}_fused_ms"] = round(med, 4)
+        med, _ = time_loop(pull_naive(times), iters, 3)
+        res[f"pull_{name}_gather_then_gemm_ms"] = round(med, 4)
+        res[f"pull_{name}_ect_ms"] = round(res[f"pull_{name}_fused_ms"] - nonsplit, 4)
+        res[f"pull_{name}_ect_naive_ms"] = round(res[f"pull_{name}_gather_then_gemm_ms"]
+                                                 - nonsplit, 4)
+    assert int(w.err.item()) == 0, "fm_ag_gemm_pull reported a timeout"
 
     # --- GEMM-ReduceScatter -------------------------------------------------
     tmp16 = torch.empty((w.M, w.N2), dtype=torch.float16, device=w.dev)
