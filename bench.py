@@ -292,6 +292,12 @@ def ect_block(w, iters):
 
     chunk_ev = [torch.cuda.Event() for _ in range(w.n)]
 
+    def producers():
+        # the copies run on producer workgroups of the GEMM's own launch
+        w.epoch += 1
+        fm.fm_ag_gemm_producers([None] + w.peers[1:], w.X, w.W1, w.Out1, w.flags, w.counters,
+                                w.epoch, order=w.order, err_word=w.err)
+
     def naive():
         # the prior-art sequence: one GEMM launch per chunk, each after its chunk
         w.epoch += 1
@@ -305,13 +311,14 @@ def ect_block(w, iters):
 
     log("ECT: AllGather-GEMM")
     for name, fn in [("nonsplit_fm_gemm", ns_fm), ("nonsplit_hipblaslt", ns_blas),
-                     ("fused", fused), ("naive_chunked", naive)]:
+                     ("fused", fused), ("naive_chunked", naive), ("producers", producers)]:
         med, best = time_loop(fn, iters, 3)
         res[f"ag_{name}_ms"] = round(med, 4)
     nonsplit = min(res["ag_nonsplit_fm_gemm_ms"], res["ag_nonsplit_hipblaslt_ms"])
     res["ag_ect_ms"] = round(res["ag_fused_ms"] - nonsplit, 4)
     res["ag_ect_vs_fm_gemm_ms"] = round(res["ag_fused_ms"] - res["ag_nonsplit_fm_gemm_ms"], 4)
     res["ag_ect_naive_ms"] = round(res["ag_naive_chunked_ms"] - nonsplit, 4)
+    res["ag_ect_producers_ms"] = round(res["ag_producers_ms"] - nonsplit, 4)
     res["ag_ect_frac_of_nonsplit"] = round(res["ag_ect_ms"] / nonsplit, 4)
     assert int(w.err.item()) == 0, "fm_ag_gemm reported a timeout"
 

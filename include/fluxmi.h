@@ -10,7 +10,8 @@
  *   fm_moe_gather_gemm   token gather fused with grouped expert GEMM (MoE layer 0)
  *   fm_moe_gemm_scatter  grouped expert GEMM fused with top-k weighted
  *                        scatter-reduce (MoE layer 1)
- * plus the AllGather variants fm_ag_gemm_pull (chunks read in place) and
+ * plus the AllGather variants fm_ag_gemm_pull (chunks read in place),
+ * fm_ag_gemm_producers (copies done by workgroups of the same launch) and
  * fm_moe_ag_gather_gemm (MoE layer 0 behind a token AllGather), the producer
  * half of the chunk-arrival protocol (fm_chunk_push, fm_chunk_push_dma,
  * fm_chunk_signal_paced) and the routing index on its own (fm_moe_route).
@@ -126,6 +127,37 @@ fm_status_t fm_ag_gemm_pull(fm_dtype_t dt, int64_t M, int64_t N, int64_t K, int3
                             const void* const* chunks, const void* W, void* C,
                             const uint32_t* flags, uint32_t epoch, const int32_t* order,
                             int32_t* err_word, int64_t spin_limit, hipStream_t stream);
+
+/*
+ * fm_ag_gemm_producers -- fm_ag_gemm with the data movement inside the same
+ * launch, on workgroups of its own (COMET article, "COMET 的技术原理": thread
+ * blocks are split into communication and computation roles, their ratio
+ * adapted to the workload).  The first P workgroups of the grid are
+ * producers: for each chunk in `order`, together they copy src[c] into rows
+ * [c*M/n_chunks, (c+1)*M/n_chunks) of X and publish flags[c] = epoch
+ * (release) once the whole chunk is in.  The other workgroups run the
+ * AllGather-GEMM tiles, each after the flags of its chunks.  Producers take
+ * the lowest workgroup ids and are dispatched first, so a waiting consumer
+ * never holds back the producer it waits for.
+ *   src          host array of n_chunks device pointers to [M/n_chunks, K]
+ *                source blocks (a peer's chunk); NULL = chunk already in X
+ *                (published at the start).  Sources must not overlap X.
+ *   X            [M, K] gathered buffer (written by the producers, read by
+ *                the consumers).
+ *   counters     device uint32 [n_chunks], zero before the first call and
+ *                left zero by every call.
+ *   n_producers  P, a multiple of 8 (one per XCD per round) up to half the
+ *                CUs; 0 picks the largest P that keeps the consumers' tile
+ *                waves at their minimum, at most one per MiB copied (the
+ *                per-shape choice of the producer:consumer ratio).
+ *   W, C, flags, epoch, order, err_word, spin_limit  as fm_ag_gemm.
+ * The result equals fm_gemm on the gathered X, bit for bit.
+ */
+fm_status_t fm_ag_gemm_producers(fm_dtype_t dt, int64_t M, int64_t N, int64_t K,
+                                 int32_t n_chunks, const void* const* src, void* X,
+                                 const void* W, void* C, uint32_t* flags, uint32_t* counters,
+                                 uint32_t epoch, const int32_t* order, int32_t n_producers,
+                                 int32_t* err_word, int64_t spin_limit, hipStream_t stream);
 
 /*
  * fm_chunk_signal_paced -- emulated arrival at link speed: publish

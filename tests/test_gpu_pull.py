@@ -149,3 +149,94 @@ def test_full_pull_ag_gemm_link_paced(oracle):
     got = C[r, cc].float().cpu().numpy().astype(np.float64)
     assert_close(got, oracle.gemm_entries(F16, X, W, rows, cols), "full pull samples")
     assert np.array_equal(bits16(C), bits16(_gemm_concat(chunks, Wd, F16)))
+
+
+# ---------------------------------------------------------------------------
+# AllGather-GEMM with producer workgroups in the same launch
+# ---------------------------------------------------------------------------
+
+def _producers_run(chunks_bits, dt, Wd, N, order, local=(), n_prod=0, counters=None):
+    """Sources for every chunk except those in `local` (already in X); returns
+    (C, X, flags, counters)."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    n, Mc, K = chunks_bits.shape
+    src = [None if c in local else dev16(chunks_bits[c], dt) for c in range(n)]
+    X = torch.full((n * Mc, K), float("nan"), dtype=Wd.dtype, device="cuda:0")
+    for c in local:
+        X[c * Mc:(c + 1) * Mc].copy_(dev16(chunks_bits[c], dt))
+    flags = torch.zeros(n, dtype=torch.int32, device="cuda:0")
+    if counters is None:
+        counters = torch.zeros(n, dtype=torch.int32, device="cuda:0")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    C = torch.empty((n * Mc, N), dtype=Wd.dtype, device="cuda:0")
+    Pull._epoch += 1
+    fm.fm_ag_gemm_producers(src, X, Wd, C, flags, counters, Pull._epoch, order=list(order),
+                            n_producers=n_prod, err_word=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert torch.all(flags == Pull._epoch).item()
+    assert torch.count_nonzero(counters).item() == 0
+    return C, X
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_producers_tiny_random_arrival(oracle, monkeypatch, tile):
+    """4 chunks of 64 x 512 fp16 copied by 8 producer workgroups in a seeded
+    random order: X holds the concatenation afterwards, and C equals the
+    oracle and fm_gemm bit for bit."""
+    monkeypatch.setenv("FM_TILE", tile)
+    c = wl.TINY_AG
+    chunks, W, order = wl.ag_inputs(c["n_chunks"], c["Mc"], c["N"], c["K"], F16, seed=c["seed"],
+                                    arrival="random")
+    say(f"fm_ag_gemm_producers tiny tile={tile} order={order.tolist()}")
+    Wd = dev16(W, F16)
+    C, X = _producers_run(chunks, F16, Wd, c["N"], order, n_prod=8)
+    assert np.array_equal(bits16(X), np.concatenate(list(chunks), axis=0))
+    assert_close(host64(C), oracle.ag_gemm(F16, list(chunks), W, arrival=order), "producers")
+    assert np.array_equal(bits16(C), bits16(_gemm_concat(chunks, Wd, F16)))
+
+
+@pytest.mark.parametrize("n_chunks,Mc,dt,n_prod,local", [(1, 300, F16, 8, ()),
+                                                         (3, 512, BF16, 16, (0,)),
+                                                         (5, 200, F16, 64, (2,)),
+                                                         (16, 32, BF16, 24, (0, 1)),
+                                                         (8, 64, F16, 8, tuple(range(8)))])
+def test_producers_layouts(oracle, n_chunks, Mc, dt, n_prod, local):
+    """Chunk sizes around the tile height, a ragged K, local chunks already in
+    place (all of them in the last case), and producer counts from 8 to 64."""
+    K, N = 136, 264
+    chunks, W, order = wl.ag_inputs(n_chunks, Mc, N, K, dt, seed=n_chunks * 13 + Mc,
+                                    arrival="random")
+    say(f"fm_ag_gemm_producers layout n={n_chunks} Mc={Mc} P={n_prod} local={local}")
+    Wd = dev16(W, dt)
+    C, X = _producers_run(chunks, dt, Wd, N, order, local=local, n_prod=n_prod)
+    assert np.array_equal(bits16(X), np.concatenate(list(chunks), axis=0))
+    assert_close(host64(C), oracle.ag_gemm(dt, list(chunks), W, arrival=order), "producers")
+    assert np.array_equal(bits16(C), bits16(_gemm_concat(chunks, Wd, dt)))
+
+
+def test_full_producers_ag_gemm(oracle):
+    """TP=8 rank 0 with the default producer count: the local chunk in place,
+    seven copied in ring order; sampled outputs against the oracle, X and C
+    bit-identical to the concatenation and to fm_gemm; a second call with the
+    same counters (left at zero) gives the same bits."""
+    import torch
+    c = wl.AG_TP8
+    n, Mc, N, K = c["n_chunks"], c["Mc"], c["N"], c["K"]
+    say(f"full fm_ag_gemm_producers {n}x{Mc} x {N} x {K}")
+    chunks, W, order = wl.ag_inputs(n, Mc, N, K, F16, seed=c["seed"], arrival="ring")
+    Wd = dev16(W, F16)
+    counters = torch.zeros(n, dtype=torch.int32, device="cuda:0")
+    C, X = _producers_run(chunks, F16, Wd, N, order, local=(0,), counters=counters)
+    assert np.array_equal(bits16(X), np.concatenate(list(chunks), axis=0))
+    Xh = np.concatenate(list(chunks), axis=0)
+    rows, cols = sample_coords(n * Mc, N, 3000, seed=6, tile=(256, 128))
+    r = torch.from_numpy(rows).to(C.device)
+    cc = torch.from_numpy(cols).to(C.device)
+    got = C[r, cc].float().cpu().numpy().astype(np.float64)
+    assert_close(got, oracle.gemm_entries(F16, Xh, W, rows, cols), "full producers samples")
+    ref = bits16(_gemm_concat(chunks, Wd, F16))
+    assert np.array_equal(bits16(C), ref)
+    C2, _ = _producers_run(chunks, F16, Wd, N, order, local=(0,), counters=counters)
+    assert np.array_equal(bits16(C2), ref)

@@ -154,6 +154,29 @@ def test_ag_gemm_pull_validation():
     assert call(M=0) == fm.FM_OK                                       # nothing to do
 
 
+def test_ag_gemm_producers_validation():
+    L = fm.lib()
+    src4 = _arr(ctypes.c_void_p, [0, 0x50000, 0x60000, 0x70000])
+    X = ctypes.c_void_p(0x100000)
+
+    def call(M=256, n=4, src=src4, X=X, flags=P3, counters=P2, order=None, nprod=0, spin=0):
+        return L.fm_ag_gemm_producers(0, M, 64, 64, n, src, X, P, P, flags, counters, 1, order,
+                                      nprod, None, spin, None)
+    assert call(src=None) == fm.FM_ERR_INVALID_ARG
+    assert call(counters=None) == fm.FM_ERR_INVALID_ARG
+    assert call(counters=ctypes.c_void_p(0x20002)) == fm.FM_ERR_INVALID_ARG
+    assert call(n=3) == fm.FM_ERR_INVALID_ARG                          # M % n_chunks
+    assert call(nprod=4) == fm.FM_ERR_INVALID_ARG                      # below 8
+    assert call(nprod=12) == fm.FM_ERR_INVALID_ARG                     # not a multiple of 8
+    assert call(spin=-1) == fm.FM_ERR_INVALID_ARG
+    assert call(src=_arr(ctypes.c_void_p, [0, 0x50008, 0x60000, 0x70000])) == \
+        fm.FM_ERR_INVALID_ARG                                          # misaligned source
+    assert call(src=_arr(ctypes.c_void_p, [0, 0x100000 + 4096, 0, 0])) == \
+        fm.FM_ERR_INVALID_ARG                                          # source inside X
+    assert call(order=_arr(ctypes.c_int32, [3, 3, 1, 0])) == fm.FM_ERR_INVALID_ARG
+    assert call(M=0) == fm.FM_OK
+
+
 def test_chunk_signal_paced_validation():
     L = fm.lib()
     t = _arr(ctypes.c_int64, [0, 10, 20, 30])

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libfluxmi.so")
 FM_OK, FM_ERR_INVALID_ARG, FM_ERR_UNSUPPORTED, FM_ERR_HIP, FM_ERR_TIMEOUT = range(5)
 FM_F16, FM_BF16, FM_F32 = 0, 1, 2
 
-EXPORTS = ("fm_version", "fm_status_str", "fm_gemm", "fm_ag_gemm", "fm_ag_gemm_pull",
+EXPORTS = ("fm_version", "fm_status_str", "fm_gemm", "fm_ag_gemm", "fm_ag_gemm_pull", "fm_ag_gemm_producers",
            "fm_chunk_push", "fm_chunk_push_dma", "fm_chunk_signal_paced",
            "fm_gemm_rs", "fm_moe_route", "fm_moe_gather_gemm", "fm_moe_ag_gather_gemm",
            "fm_moe_gemm_scatter")
@@ -57,6 +57,9 @@ def lib() -> ctypes.CDLL:
     L.fm_ag_gemm_pull.restype = ctypes.c_int
     L.fm_ag_gemm_pull.argtypes = [ctypes.c_int, i64, i64, i64, i32, p, p, p, p, u32, p, p, i64,
                                   p]
+    L.fm_ag_gemm_producers.restype = ctypes.c_int
+    L.fm_ag_gemm_producers.argtypes = [ctypes.c_int, i64, i64, i64, i32, p, p, p, p, p, p, u32,
+                                       p, i32, p, i64, p]
     L.fm_chunk_signal_paced.restype = ctypes.c_int
     L.fm_chunk_signal_paced.argtypes = [p, i32, p, p, u32, p]
     L.fm_chunk_push.restype = ctypes.c_int
@@ -180,6 +183,28 @@ def fm_ag_gemm_pull(chunks, W, C, flags, epoch: int, order=None, err_word=None,
         _dt(W), M, N, K, n, ctypes.cast(ptrs, ctypes.c_void_p), _ptr(W), _ptr(C), _ptr(flags),
         ctypes.c_uint32(epoch & 0xFFFFFFFF),
         ctypes.cast(o, ctypes.c_void_p) if o is not None else None,
+        _ptr(err_word), int(spin_limit), _stream(stream)))
+
+
+def fm_ag_gemm_producers(src, X, W, C, flags, counters, epoch: int, order=None,
+                         n_producers: int = 0, err_word=None, spin_limit: int = 0,
+                         stream=None) -> None:
+    """C = X @ W where producer workgroups of the same launch copy src[c] (None:
+    already in X) into X's chunk c and publish flags[c] = epoch."""
+    n = len(src)
+    M, K = X.shape
+    K2, N = W.shape
+    Mc = M // n
+    if (K2 != K or tuple(C.shape) != (M, N) or C.dtype != X.dtype or W.dtype != X.dtype
+            or any(x is not None and (tuple(x.shape) != (Mc, K) or x.dtype != X.dtype)
+                   for x in src)):
+        raise ValueError("fm_ag_gemm_producers: shape or dtype mismatch")
+    ptrs = (ctypes.c_void_p * n)(*[_ptr(x) if x is not None else None for x in src])
+    o = _order_arg(order)
+    _check("fm_ag_gemm_producers", lib().fm_ag_gemm_producers(
+        _dt(X), M, N, K, n, ctypes.cast(ptrs, ctypes.c_void_p), _ptr(X), _ptr(W), _ptr(C),
+        _ptr(flags), _ptr(counters), ctypes.c_uint32(epoch & 0xFFFFFFFF),
+        ctypes.cast(o, ctypes.c_void_p) if o is not None else None, int(n_producers),
         _ptr(err_word), int(spin_limit), _stream(stream)))
 
 

@@ -21,7 +21,9 @@ namespace fm {
 // RS: ReduceScatter epilogue for tiles that never straddle a slice (slice
 // rows a multiple of BM) with plain adds; RSG: any slice size, or atomic adds.
 // AGP: AllGather in pull mode, each chunk read in place from its own buffer.
-enum class Mode : int { Gemm = 0, AG = 1, RS = 2, RSG = 3, AGP = 4 };
+// AGX: AllGather with its own producer workgroups (the first n_prod of the
+// grid copy the chunks into X and publish them; the rest run AG tiles).
+enum class Mode : int { Gemm = 0, AG = 1, RS = 2, RSG = 3, AGP = 4, AGX = 5 };
 
 constexpr int kMaxRanks = 16;
 // In-tile byte offsets are 32-bit (tile rows x row pitch), which bounds each
@@ -45,6 +47,13 @@ struct DenseArgs {
   // straddles two buffers (a ragged chunk ends in a partial tile).
   int tiles_per_chunk;
   const char* chunk_a[kMaxChunks];
+  // AllGather with producer workgroups: chunk_a[c] is chunk c's source (null:
+  // already in X), copied into xw by n_prod workgroups in the order order_c.
+  int n_prod;
+  char* xw;
+  uint32_t* flags_w;
+  uint32_t* counters;
+  uint8_t order_c[kMaxChunks];
   // ReduceScatter: destination slices
   int32_t atomic;
   int64_t slice_rows;
@@ -106,6 +115,52 @@ __device__ __forceinline__ void store_tile(Eng& eng, const DenseArgs& args, int6
   }
 }
 
+// Producer workgroup p of P (AGX): for each chunk in arrival order, copy its
+// p-th share into X, then check in on the chunk's counter; the last of the P
+// workgroups resets the counter and publishes the chunk's flag (release).
+// All producers work on the same chunk at a time, so chunks complete in
+// arrival order.  Chunks without a source are published by workgroup 0.
+template <int NT>
+__device__ __forceinline__ void produce_chunks(const DenseArgs& args) {
+  const int p = blockIdx.x, P = args.n_prod, t = threadIdx.x;
+  const int64_t chunk_bytes = args.chunk_rows * args.K * 2;
+  const int64_t n16 = chunk_bytes / 16;
+  const int64_t per = cdiv(cdiv(n16, P), NT) * NT;
+  const int64_t b0 = min((int64_t)p * per, n16), b1 = min(b0 + per, n16);
+  const int n_chunks = (int)(args.M / args.chunk_rows);
+  if (p == 0 && t == 0)
+    for (int c = 0; c < n_chunks; ++c)
+      if (!args.chunk_a[c])
+        __hip_atomic_store(args.flags_w + c, args.epoch, __ATOMIC_RELEASE,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  for (int a = 0; a < n_chunks; ++a) {
+    const int c = args.order_c[a];
+    if (!args.chunk_a[c]) continue;
+    const u32x4* __restrict__ src = reinterpret_cast<const u32x4*>(args.chunk_a[c]);
+    u32x4* __restrict__ dst = reinterpret_cast<u32x4*>(args.xw + c * chunk_bytes);
+    int64_t i = b0 + t;
+    for (; i + 3 * NT < b1; i += 4 * NT) {
+      const u32x4 x0 = src[i], x1 = src[i + NT], x2 = src[i + 2 * NT], x3 = src[i + 3 * NT];
+      dst[i] = x0;
+      dst[i + NT] = x1;
+      dst[i + 2 * NT] = x2;
+      dst[i + 3 * NT] = x3;
+    }
+    for (; i < b1; i += NT) dst[i] = src[i];
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (t == 0) {
+      const uint32_t prev =
+          __hip_atomic_fetch_add(args.counters + c, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == (uint32_t)P - 1) {
+        __hip_atomic_store(args.counters + c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(args.flags_w + c, args.epoch, __ATOMIC_RELEASE,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
 template <class E, int BM, int BN, int NW, Mode MODE, bool OUT32, bool KTAIL>
 __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args) {
   // One wave per SIMD has the register room for a two-sub-step read-ahead.
@@ -113,10 +168,20 @@ __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args)
   __shared__ __attribute__((aligned(16))) char smem[Eng::LDS_BYTES];
   __shared__ int s_abort;
 
+  int wg = blockIdx.x, G = gridDim.x;
+  if constexpr (MODE == Mode::AGX) {
+    // The producers take the first workgroup ids, so they are dispatched
+    // before any consumer that may wait on them.
+    if (wg < args.n_prod) {
+      produce_chunks<64 * NW>(args);
+      return;
+    }
+    wg -= args.n_prod;
+    G -= args.n_prod;
+  }
   Eng eng(smem, args.K);
   const int64_t M = args.M, N = args.N, K = args.K;
-  const int G = gridDim.x;
-  const int slot = xcd_slot(blockIdx.x, G);
+  const int slot = xcd_slot(wg, G);
   uint64_t ready = 0;
 
   const int n_pos = (args.pos_end - args.pos0) * args.sub_n;
@@ -148,7 +213,7 @@ __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args)
     }
     if (n0 >= N) continue;   // a part of an edge tile that lies past N
 
-    if constexpr (MODE == Mode::AG || MODE == Mode::AGP) {
+    if constexpr (MODE == Mode::AG || MODE == Mode::AGP || MODE == Mode::AGX) {
       // Tile prologue: wait for every chunk overlapping rows [m0, m_end).
       if (threadIdx.x == 0) {
         const bool ok = wait_chunks(args.flags, args.epoch, (int)(m0 / args.chunk_rows),
@@ -260,7 +325,8 @@ bool split_tail_ok(TileCfg cfg, int64_t tiles, int G) {
   return rem > 0 && 2 * rem <= G;
 }
 
-TileCfg choose_tile(int64_t M, int64_t N, int G) {
+// split: the launch may run a half-full last wave as 256x128 halves.
+TileCfg choose_tile(int64_t M, int64_t N, int G, bool split = true) {
   if (const char* env = std::getenv("FM_TILE")) {
     int bm = 0, bn = 0, nw = 0;
     const int got = std::sscanf(env, "%dx%dw%d", &bm, &bn, &nw);
@@ -277,7 +343,7 @@ TileCfg choose_tile(int64_t M, int64_t N, int G) {
     const int64_t tiles = cdiv(M, cands[c].bm) * cdiv(N, cands[c].bn);
     const double area = (double)cands[c].bm * cands[c].bn / eff[c];
     double cost = (double)cdiv(tiles, G) * area;
-    if (split_tail_ok(cands[c], tiles, G))   // last partial wave as 256x128 halves
+    if (split && split_tail_ok(cands[c], tiles, G))   // last partial wave as 256x128 halves
       cost = (double)(tiles / G) * area + 256.0 * 128.0 / eff[1];
     if (cost < best_cost * 0.999) {
       best_cost = cost;
@@ -319,7 +385,7 @@ bool valid_ab(fm_dtype_t dt) { return dt == FM_F16 || dt == FM_BF16; }
 template <Mode MODE, bool OUT32>
 void launch_one(fm_dtype_t dt, TileCfg cfg, const DenseArgs& args, hipStream_t stream) {
   const int n_pos = (args.pos_end - args.pos0) * args.sub_n;
-  const dim3 grid(std::min(n_pos, device_cu_count()));
+  const dim3 grid(args.n_prod + std::min(n_pos, device_cu_count() - args.n_prod));
 #define FM_LAUNCH(E, BM, BN, NW)                                                              \
   do {                                                                                        \
     if (args.K % kBK) /* ragged K: the 4-wave form keeps the tail path spill-free */          \
@@ -507,6 +573,113 @@ extern "C" fm_status_t fm_ag_gemm_pull(fm_dtype_t dt, int64_t M, int64_t N, int6
   for (int tm = 0; tm < args.order.tiles_m; ++tm) key[tm] = pos[tm / tpc];
   set_morder(args.order, key);
   return launch_dense<Mode::AGP, false>(dt, cfg, args, stream);
+}
+
+// Producer workgroups for an M x N AllGather-GEMM that copies `bytes`: the
+// largest multiple of 8 (one per XCD per round) that keeps the consumers'
+// tile waves at their minimum, capped at one producer per MiB copied and at
+// half the CUs.  More producers copy faster, and the chip clocks higher with
+// fewer CUs in the GEMM, until the consumers lose a wave.  Measured on the
+// TP=8 AllGather (384 tiles, 7 chunks of 12.58 MB): 8/16/32/48/64 producers
+// took 0.75/0.69/0.64/0.60/0.59 ms; 80, which leaves 176 consumers and a
+// third wave, 0.97 ms.
+int producers_default(int64_t M, int64_t N, int64_t bytes, int cus) {
+  if (const char* env = std::getenv("FM_PRODUCERS")) {
+    const int p = std::atoi(env);
+    if (p >= 8 && p <= cus / 2 && p % 8 == 0) return p;
+  }
+  const int cap = (int)std::max<int64_t>(
+      8, std::min<int64_t>(cus / 2 / 8 * 8, (cdiv(bytes, 1ll << 20) + 7) / 8 * 8));
+  int best = 8;
+  double best_cost = 1e300;
+  for (int P = 8; P <= cap; P += 8) {
+    const int G = cus - P;
+    const TileCfg cfg = choose_tile(M, N, G, false);
+    const double eff = cfg.bn == 256 ? 1.0 : (cfg.bm == 256 ? 0.85 : 0.7);
+    const int64_t tiles = cdiv(M, cfg.bm) * cdiv(N, cfg.bn);
+    const double cost = (double)cdiv(tiles, G) * cfg.bm * cfg.bn / eff;
+    if (cost <= best_cost * 1.0001) {   // ties go to more producers
+      best_cost = std::min(best_cost, cost);
+      best = P;
+    }
+  }
+  return best;
+}
+
+extern "C" fm_status_t fm_ag_gemm_producers(fm_dtype_t dt, int64_t M, int64_t N, int64_t K,
+                                            int32_t n_chunks, const void* const* src, void* X,
+                                            const void* W, void* C, uint32_t* flags,
+                                            uint32_t* counters, uint32_t epoch,
+                                            const int32_t* order, int32_t n_producers,
+                                            int32_t* err_word, int64_t spin_limit,
+                                            hipStream_t stream) {
+  if (!valid_ab(dt)) return FM_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 0 || N % 8 || K % 8) return FM_ERR_INVALID_ARG;
+  if (n_chunks < 1 || n_chunks > kMaxChunks || M % n_chunks) return FM_ERR_INVALID_ARG;
+  if (!src || !X || !W || !C || !flags || !counters || !aligned16(X) || !aligned16(W) ||
+      !aligned16(C))
+    return FM_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(flags) & 3u) || (reinterpret_cast<uintptr_t>(counters) & 3u) ||
+      spin_limit < 0)
+    return FM_ERR_INVALID_ARG;
+  if (n_producers != 0 && (n_producers < 8 || n_producers % 8)) return FM_ERR_INVALID_ARG;
+  const int64_t chunk_bytes = (M / n_chunks) * K * 2;
+  const char* xb = (const char*)X;
+  int64_t copy_bytes = 0;
+  for (int c = 0; c < n_chunks; ++c) {
+    const char* sc = (const char*)src[c];
+    if (!sc) continue;
+    if (!aligned16(sc)) return FM_ERR_INVALID_ARG;
+    if (sc < xb + M * K * 2 && xb < sc + chunk_bytes) return FM_ERR_INVALID_ARG;   // overlaps X
+    copy_bytes += chunk_bytes;
+  }
+  std::vector<int> pos(n_chunks, -1);
+  for (int a = 0; a < n_chunks; ++a) {
+    const int c = order ? order[a] : a;
+    if (c < 0 || c >= n_chunks || pos[c] != -1) return FM_ERR_INVALID_ARG;
+    pos[c] = a;
+  }
+  if (M == 0 || N == 0) return FM_OK;
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FM_ERR_UNSUPPORTED;
+  const int cus = device_cu_count();
+  const int P = n_producers ? n_producers : producers_default(M, N, copy_bytes, cus);
+  if (P > cus / 2) return FM_ERR_INVALID_ARG;
+  // The consumers hold the CUs the producers leave free.
+  const TileCfg cfg = choose_tile(M, N, cus - P, false);
+  DenseArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.A = xb;
+  args.B = (const char*)W;
+  args.C = (char*)C;
+  args.M = M;
+  args.N = N;
+  args.K = K;
+  args.flags = flags;
+  args.flags_w = flags;
+  args.counters = counters;
+  args.xw = (char*)X;
+  args.epoch = epoch;
+  args.chunk_rows = M / n_chunks;
+  args.err_word = err_word;
+  args.spin_limit = spin_limit ? spin_limit : (1ll << 24);
+  args.n_prod = P;
+  for (int c = 0; c < n_chunks; ++c) args.chunk_a[c] = (const char*)src[c];
+  for (int a = 0; a < n_chunks; ++a) args.order_c[a] = (uint8_t)(order ? order[a] : a);
+  fill_order(args.order, M, N, cfg);
+  std::vector<int> key(args.order.tiles_m);
+  for (int tm = 0; tm < args.order.tiles_m; ++tm) {
+    const int64_t r0 = (int64_t)tm * cfg.bm, r1 = std::min<int64_t>(r0 + cfg.bm, M) - 1;
+    int k = 0;
+    for (int64_t c = r0 / args.chunk_rows; c <= r1 / args.chunk_rows; ++c) k = std::max(k, pos[c]);
+    key[tm] = k;
+  }
+  set_morder(args.order, key);
+  // one launch: producers and consumers must run together
+  args.pos0 = 0;
+  args.pos_end = args.order.total;
+  args.sub_n = 1;
+  launch_one<Mode::AGX, false>(dt, cfg, args, stream);
+  return launch_status();
 }
 
 extern "C" fm_status_t fm_gemm_rs(fm_dtype_t dt, int64_t M, int64_t N, int64_t K,
