@@ -263,7 +263,8 @@ def _moe_ag_run(arr, inp, e0, nl, order, epoch, dt=BF16, spin=0, hint=None, **pu
     ids = inp["topk_ids"]
     T, topk = ids.shape
     ffn = inp["W1"].shape[2]
-    H = torch.zeros((T * topk, ffn), dtype=torch.bfloat16, device="cuda:0")
+    H = torch.zeros((T * topk, ffn), dtype=torch.float16 if dt == F16 else torch.bfloat16,
+                    device="cuda:0")
     sp = torch.full((T * topk,), -1, dtype=torch.int32, device="cuda:0")
     off = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
     arr.err.zero_()
@@ -311,6 +312,52 @@ def test_moe_ag_gather_random_arrival(oracle, monkeypatch, T, n, delay, hint):
                           e0)
     torch.cuda.synchronize()
     assert torch.equal(H[:rows].view(torch.int16), H2[:rows].view(torch.int16))
+
+
+@pytest.mark.parametrize("T,n,topk,nl,e0", [(640, 1, 2, 8, 0), (1200, 4, 4, 16, 16)])
+def test_moe_ag_f16_layouts(oracle, T, n, topk, nl, e0):
+    """fp16, a single chunk (nothing to gather but the local one) and top-4
+    over 16 local experts: routing bit-exact, H within the bar of the oracle
+    and bit-identical to the non-fused layer 0."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    from gpu_util import Arrival
+    hidden, ffn, E = 192, 136, 64
+    inp = wl.moe_inputs(T, hidden, ffn, E, nl, topk, F16, seed=T + topk)
+    chunks = inp["X"].reshape(n, T // n, hidden)
+    order = list(range(n))
+    say(f"moe ag fp16 T={T} chunks={n} topk={topk} experts {e0}..{e0 + nl - 1}")
+    arr = Arrival(chunks, F16, hidden)
+    arr.poison()
+    off, sp, H = _moe_ag_run(arr, inp, e0, nl, order, arr.next_epoch(), dt=F16, local=0)
+    assert arr.err.item() == 0
+    roff, rsp = oracle.moe_route(inp["topk_ids"], e0, nl)
+    rows = int(roff[-1])
+    assert np.array_equal(off, roff) and np.array_equal(sp[:rows], rsp)
+    ref = oracle.moe_ag_layer0(F16, list(chunks), inp["W1"], rsp, roff, topk, arrival=order)
+    assert_close(host64(H[:rows]), ref, "moe ag fp16")
+    H2 = torch.zeros_like(H)
+    sp2 = torch.full((T * topk,), -1, dtype=torch.int32, device="cuda:0")
+    off2 = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
+    fm.fm_moe_gather_gemm(arr.X, _i32(inp["topk_ids"]), dev16(inp["W1"], F16), H2, sp2, off2, e0)
+    torch.cuda.synchronize()
+    assert torch.equal(H[:rows].view(torch.int16), H2[:rows].view(torch.int16))
+
+
+def test_moe_ag_nothing_local_waits_for_nothing():
+    """No pair is routed to this rank: no tile exists, so no chunk is waited
+    for (none is ever pushed) and the call neither times out nor writes H."""
+    import torch
+    from gpu_util import Arrival
+    T, hidden, ffn, nl, n = 512, 128, 64, 4, 4
+    inp = wl.moe_inputs(T, hidden, ffn, 16, nl, 2, BF16, seed=12)
+    inp["topk_ids"] = np.full((T, 2), 12, dtype=np.int32)
+    arr = Arrival(inp["X"].reshape(n, T // n, hidden), BF16, hidden)
+    off, sp, H = _moe_ag_run(arr, inp, 0, nl, list(range(n)), arr.next_epoch(), spin=2000,
+                             skip=tuple(range(n)))
+    assert arr.err.item() == 0
+    assert off.tolist() == [0] * (nl + 1) and bool((sp == -1).all())
+    assert torch.count_nonzero(H).item() == 0
 
 
 def test_moe_ag_withheld_chunk_times_out():
