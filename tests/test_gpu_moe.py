@@ -360,6 +360,35 @@ def test_moe_ag_nothing_local_waits_for_nothing():
     assert torch.count_nonzero(H).item() == 0
 
 
+def test_moe_layer_end_to_end(oracle):
+    """A whole MoE layer on one rank, each stage fed by the previous one on the
+    GPU: token AllGather (8 chunks, seeded random arrival) into layer 0, then
+    layer 1 with the weighted combine on the GPU's own H.  Compared with the
+    oracle's chain (layer 0, H rounded to bf16, layer 1) on the delta of out."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    from gpu_util import Arrival
+    T, hidden, ffn, E, nl, e0, n = 4096, 384, 264, 32, 8, 8, 8
+    inp = wl.moe_inputs(T, hidden, ffn, E, nl, 2, BF16, seed=4242, zipf_s=1.2)
+    chunks = inp["X"].reshape(n, T // n, hidden)
+    order = wl.permutation(n, seed=4243)
+    say(f"moe layer end to end T={T} experts {e0}..{e0 + nl - 1} order={order.tolist()}")
+    arr = Arrival(chunks, BF16, hidden)
+    arr.poison()
+    off, sp, H = _moe_ag_run(arr, inp, e0, nl, order, arr.next_epoch(), hint=order.tolist())
+    assert arr.err.item() == 0
+    out = devf32(inp["out_seed"])
+    fm.fm_moe_gemm_scatter(H, dev16(inp["W2"], BF16), _i32(sp), _i32(off),
+                           devf32(inp["topk_weights"]), out)
+    torch.cuda.synchronize()
+    roff, rsp = oracle.moe_route(inp["topk_ids"], e0, nl)
+    assert np.array_equal(off, roff)
+    Href = oracle.moe_ag_layer0(BF16, list(chunks), inp["W1"], rsp, roff, 2, arrival=order)
+    ref = oracle.moe_layer1(BF16, oracle.round_bf16(Href), inp["W2"], inp["topk_ids"],
+                            inp["topk_weights"], rsp, roff, inp["out_seed"], e0)
+    assert_close(host64(out) - inp["out_seed"], ref - inp["out_seed"], "moe layer end to end")
+
+
 def test_moe_ag_withheld_chunk_times_out():
     """A token chunk that never arrives: the bounded wait writes
     FM_ERR_TIMEOUT to err_word and the kernel exits (no hang)."""
