@@ -415,14 +415,24 @@ def ect_block(w, iters):
         w.join_sides()
         fm.fm_moe_gather_gemm(w.mXg, w.ids, w.mW1, w.H, w.sp, w.off, w.e0)
 
+    def moe_producers():
+        # the token copies run on producer workgroups of layer 0's own launch
+        w.epoch += 1
+        fm.fm_moe_ag_gather_gemm_producers([None] + w.mpeers[1:], w.mXg, w.ids, w.mW1, w.H, w.sp,
+                                           w.off, w.e0, w.mflags, w.mcounters, w.epoch,
+                                           order=w.order, err_word=w.err)
+
     log("ECT: token AllGather + MoE layer 0")
-    for name, fn in [("nonsplit", moe_ns), ("fused", moe_fused), ("gather_then_gemm", moe_naive)]:
+    for name, fn in [("nonsplit", moe_ns), ("fused", moe_fused), ("gather_then_gemm", moe_naive),
+                     ("producers", moe_producers)]:
         med, best = time_loop(fn, iters, 3)
         res[f"moe_ag_{name}_ms"] = round(med, 4)
     res["moe_ag_ect_ms"] = round(res["moe_ag_fused_ms"] - res["moe_ag_nonsplit_ms"], 4)
     res["moe_ag_ect_naive_ms"] = round(res["moe_ag_gather_then_gemm_ms"]
                                        - res["moe_ag_nonsplit_ms"], 4)
     res["moe_ag_ect_frac_of_nonsplit"] = round(res["moe_ag_ect_ms"] / res["moe_ag_nonsplit_ms"], 4)
+    res["moe_ag_ect_producers_ms"] = round(res["moe_ag_producers_ms"] - res["moe_ag_nonsplit_ms"],
+                                           4)
     assert int(w.err.item()) == 0, "fm_moe_ag_gather_gemm reported a timeout"
     res["nonsplit_fm_gemm_tflops_4096x12288x6144"] = round(
         w.flop_rs / (res["rs_nonsplit_fm_gemm_ms"] * 1e-3) / 1e12, 1)

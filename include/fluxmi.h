@@ -11,8 +11,9 @@
  *   fm_moe_gemm_scatter  grouped expert GEMM fused with top-k weighted
  *                        scatter-reduce (MoE layer 1)
  * plus the AllGather variants fm_ag_gemm_pull (chunks read in place),
- * fm_ag_gemm_producers (copies done by workgroups of the same launch) and
- * fm_moe_ag_gather_gemm (MoE layer 0 behind a token AllGather), the producer
+ * fm_ag_gemm_producers (copies done by workgroups of the same launch),
+ * fm_moe_ag_gather_gemm (MoE layer 0 behind a token AllGather) and its
+ * producer-workgroup form fm_moe_ag_gather_gemm_producers, the producer
  * half of the chunk-arrival protocol (fm_chunk_push, fm_chunk_push_dma,
  * fm_chunk_signal_paced) and the routing index on its own (fm_moe_route).
  *
@@ -292,6 +293,34 @@ fm_status_t fm_moe_ag_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidden, int6
                                   int32_t n_chunks, const uint32_t* flags, uint32_t epoch,
                                   const int32_t* order, int32_t* err_word, int64_t spin_limit,
                                   hipStream_t stream);
+
+/*
+ * fm_moe_ag_gather_gemm_producers -- fm_moe_ag_gather_gemm with the token
+ * AllGather done inside the same launch by producer workgroups (COMET
+ * article, "COMET 的技术原理": communication and computation thread blocks
+ * of one fused MoE kernel).  The first P workgroups copy src[c] into token
+ * rows [c*T/n_chunks, (c+1)*T/n_chunks) of X, chunks taken in `order`, and
+ * publish flags[c] = epoch once a chunk is complete; the other workgroups
+ * run the layer-0 tiles behind those flags, in the arrival-ordered bands of
+ * fm_moe_ag_gather_gemm.  Producers hold the lowest workgroup ids and are
+ * dispatched first.
+ *   X            [T, hidden] gathered token buffer (written by the producers).
+ *   src          host array of n_chunks device pointers to [T/n_chunks, hidden]
+ *                blocks; NULL = chunk already in X (published at the start).
+ *                Sources are 16-byte aligned and do not overlap X.
+ *   counters     device uint32 [n_chunks], zero before the first call and
+ *                left zero by every call.
+ *   n_producers  P: a multiple of 8, 8 .. half the CUs; 0 = one per ~5 MiB
+ *                copied, 8..64.
+ *   the rest     as fm_moe_ag_gather_gemm.
+ * The result equals fm_moe_gather_gemm on the gathered X, bit for bit.
+ */
+fm_status_t fm_moe_ag_gather_gemm_producers(
+    fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn, int32_t topk, int32_t expert_begin,
+    int32_t n_local, void* X, const int32_t* topk_ids, const void* W1, void* H,
+    int32_t* sorted_pairs, int32_t* expert_offsets, int32_t n_chunks, const void* const* src,
+    uint32_t* flags, uint32_t* counters, uint32_t epoch, const int32_t* order,
+    int32_t n_producers, int32_t* err_word, int64_t spin_limit, hipStream_t stream);
 
 /*
  * fm_moe_gemm_scatter -- MoE layer 1 on this rank with the top-k weighted

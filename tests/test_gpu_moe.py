@@ -389,6 +389,99 @@ def test_moe_layer_end_to_end(oracle):
     assert_close(host64(out) - inp["out_seed"], ref - inp["out_seed"], "moe layer end to end")
 
 
+def _moe_prod_run(inp, chunks, e0, nl, order, local, n_prod, dt=BF16, counters=None):
+    """fm_moe_ag_gather_gemm_producers with sources for every chunk not in
+    `local`; returns (off, sp, H, X)."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    n, Tc, hidden = chunks.shape
+    T = n * Tc
+    topk = inp["topk_ids"].shape[1]
+    ffn = inp["W1"].shape[2]
+    src = [None if c in local else dev16(chunks[c], dt) for c in range(n)]
+    X = torch.full((T, hidden), float("nan"), dtype=torch.bfloat16 if dt == BF16
+                   else torch.float16, device="cuda:0")
+    for c in local:
+        X[c * Tc:(c + 1) * Tc].copy_(dev16(chunks[c], dt))
+    H = torch.zeros((T * topk, ffn), dtype=X.dtype, device="cuda:0")
+    sp = torch.full((T * topk,), -1, dtype=torch.int32, device="cuda:0")
+    off = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
+    flags = torch.zeros(n, dtype=torch.int32, device="cuda:0")
+    if counters is None:
+        counters = torch.zeros(n, dtype=torch.int32, device="cuda:0")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    fm.fm_moe_ag_gather_gemm_producers(src, X, _i32(inp["topk_ids"]), dev16(inp["W1"], dt), H,
+                                       sp, off, e0, flags, counters, 7, order=order,
+                                       n_producers=n_prod, err_word=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert torch.all(flags == 7).item() and torch.count_nonzero(counters).item() == 0
+    return off.cpu().numpy(), sp.cpu().numpy(), H, X
+
+
+@pytest.mark.parametrize("T,n,n_prod,local", [(3000, 8, 8, (0,)), (2048, 4, 16, ()),
+                                              (1000, 2, 64, (0, 1))])
+def test_moe_ag_producers(oracle, T, n, n_prod, local):
+    """Producer workgroups of layer 0's own launch copy the token chunks in a
+    seeded random order: X holds the gathered tokens, H equals the oracle and
+    fm_moe_gather_gemm on the gathered X bit for bit."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    hidden, ffn, E, nl, e0 = 256, 264, 16, 8, 0
+    inp = wl.moe_inputs(T, hidden, ffn, E, nl, 2, BF16, seed=T + 7 * n, zipf_s=1.2)
+    chunks = inp["X"].reshape(n, T // n, hidden)
+    order = wl.permutation(n, seed=T + 1).tolist()
+    say(f"moe ag producers T={T} chunks={n} P={n_prod} local={local} order={order}")
+    off, sp, H, X = _moe_prod_run(inp, chunks, e0, nl, order, local, n_prod)
+    assert np.array_equal(bits16(X), inp["X"])
+    roff, rsp = oracle.moe_route(inp["topk_ids"], e0, nl)
+    rows = int(roff[-1])
+    assert np.array_equal(off, roff) and np.array_equal(sp[:rows], rsp)
+    ref = oracle.moe_ag_layer0(BF16, list(chunks), inp["W1"], rsp, roff, 2, arrival=order)
+    assert_close(host64(H[:rows]), ref, "moe ag producers")
+    H2 = torch.zeros_like(H)
+    sp2 = torch.full_like(H2[:, 0], 0, dtype=torch.int32)
+    off2 = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
+    fm.fm_moe_gather_gemm(X, _i32(inp["topk_ids"]), dev16(inp["W1"], BF16), H2, sp2, off2, e0)
+    torch.cuda.synchronize()
+    assert torch.equal(H[:rows].view(torch.int16), H2[:rows].view(torch.int16))
+
+
+def test_full_moe_ag_producers_rank0(oracle):
+    """EP=8 rank 0 with the default producer count, the local chunk in place
+    and seven copied: sampled rows against the oracle, bit-identical to the
+    non-fused layer 0, and a second call on the same counters."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    c = wl.MOE_EP8
+    say("full moe ag producers EP=8 rank 0")
+    inp = wl.moe_inputs(c["T"], c["hidden"], c["ffn"], c["n_experts"], c["n_local"], c["topk"],
+                        BF16, seed=c["seed"], zipf_s=c["zipf_s"])
+    e0, n = c["rank"] * c["n_local"], 8
+    chunks = inp["X"].reshape(n, c["T"] // n, c["hidden"])
+    counters = torch.zeros(n, dtype=torch.int32, device="cuda:0")
+    off, sp, H, X = _moe_prod_run(inp, chunks, e0, c["n_local"], list(range(n)), (0,), 0,
+                                  counters=counters)
+    roff, rsp = oracle.moe_route(inp["topk_ids"], e0, c["n_local"])
+    rows = int(roff[-1])
+    assert np.array_equal(off, roff) and np.array_equal(sp[:rows], rsp)
+    rng = np.random.default_rng(10)
+    srows = np.unique(np.concatenate([rng.integers(0, rows, 48), roff[:-1], roff[1:] - 1]))
+    srows = srows[(srows >= 0) & (srows < rows)]
+    Hs = oracle.moe_layer0_rows(BF16, inp["X"], inp["W1"], rsp, roff, 2, srows)
+    idx = torch.from_numpy(srows).to("cuda:0")
+    assert_close(host64(H[idx]), Hs, "full moe ag producers rows")
+    H2 = torch.zeros_like(H)
+    sp2 = torch.full((c["T"] * 2,), -1, dtype=torch.int32, device="cuda:0")
+    off2 = torch.zeros(c["n_local"] + 1, dtype=torch.int32, device="cuda:0")
+    fm.fm_moe_gather_gemm(X, _i32(inp["topk_ids"]), dev16(inp["W1"], BF16), H2, sp2, off2, e0)
+    torch.cuda.synchronize()
+    assert torch.equal(H[:rows].view(torch.int16), H2[:rows].view(torch.int16))
+    _, _, H3, _ = _moe_prod_run(inp, chunks, e0, c["n_local"], list(range(n)), (0,), 0,
+                                counters=counters)
+    assert torch.equal(H3[:rows].view(torch.int16), H[:rows].view(torch.int16))
+
+
 def test_moe_ag_withheld_chunk_times_out():
     """A token chunk that never arrives: the bounded wait writes
     FM_ERR_TIMEOUT to err_word and the kernel exits (no hang)."""

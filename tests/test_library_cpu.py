@@ -177,6 +177,25 @@ def test_ag_gemm_producers_validation():
     assert call(M=0) == fm.FM_OK
 
 
+def test_moe_ag_producers_validation():
+    L = fm.lib()
+    X = ctypes.c_void_p(0x100000)
+    src4 = _arr(ctypes.c_void_p, [0, 0x50000, 0x60000, 0x70000])
+
+    def call(n=4, src=src4, flags=P3, counters=P2, nprod=0, order=None):
+        return L.fm_moe_ag_gather_gemm_producers(1, 64, 64, 64, 2, 0, 8, X, P, P, P, P, P, n, src,
+                                                 flags, counters, 1, order, nprod, None, 0, None)
+    assert call(src=None) == fm.FM_ERR_INVALID_ARG
+    assert call(flags=None) == fm.FM_ERR_INVALID_ARG
+    assert call(counters=None) == fm.FM_ERR_INVALID_ARG
+    assert call(nprod=12) == fm.FM_ERR_INVALID_ARG
+    assert call(nprod=4) == fm.FM_ERR_INVALID_ARG
+    assert call(n=3) == fm.FM_ERR_INVALID_ARG                          # T % n_chunks
+    assert call(src=_arr(ctypes.c_void_p, [0, 0x50008, 0, 0])) == fm.FM_ERR_INVALID_ARG
+    assert call(src=_arr(ctypes.c_void_p, [0, 0x100000 + 1024, 0, 0])) == fm.FM_ERR_INVALID_ARG
+    assert call(order=_arr(ctypes.c_int32, [0, 0, 1, 2])) == fm.FM_ERR_INVALID_ARG
+
+
 def test_chunk_signal_paced_validation():
     L = fm.lib()
     t = _arr(ctypes.c_int64, [0, 10, 20, 30])

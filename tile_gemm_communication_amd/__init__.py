@@ -23,6 +23,7 @@ FM_F16, FM_BF16, FM_F32 = 0, 1, 2
 EXPORTS = ("fm_version", "fm_status_str", "fm_gemm", "fm_ag_gemm", "fm_ag_gemm_pull", "fm_ag_gemm_producers",
            "fm_chunk_push", "fm_chunk_push_dma", "fm_chunk_signal_paced",
            "fm_gemm_rs", "fm_moe_route", "fm_moe_gather_gemm", "fm_moe_ag_gather_gemm",
+           "fm_moe_ag_gather_gemm_producers",
            "fm_moe_gemm_scatter")
 
 
@@ -76,6 +77,10 @@ def lib() -> ctypes.CDLL:
     L.fm_moe_ag_gather_gemm.restype = ctypes.c_int
     L.fm_moe_ag_gather_gemm.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32, p, p, p, p,
                                         p, p, i32, p, u32, p, p, i64, p]
+    L.fm_moe_ag_gather_gemm_producers.restype = ctypes.c_int
+    L.fm_moe_ag_gather_gemm_producers.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32, p,
+                                                  p, p, p, p, p, i32, p, p, p, u32, p, i32, p,
+                                                  i64, p]
     L.fm_moe_gemm_scatter.restype = ctypes.c_int
     L.fm_moe_gemm_scatter.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, p, p, p, p, p, p, p]
     _lib = L
@@ -297,6 +302,31 @@ def fm_moe_ag_gather_gemm(X, topk_ids, W1, H, sorted_pairs, expert_offsets, expe
         _ptr(W1), _ptr(H), _ptr(sorted_pairs), _ptr(expert_offsets), int(n_chunks), _ptr(flags),
         ctypes.c_uint32(epoch & 0xFFFFFFFF),
         ctypes.cast(order_arr, ctypes.c_void_p) if order_arr is not None else None,
+        _ptr(err_word), int(spin_limit), _stream(stream)))
+
+
+def fm_moe_ag_gather_gemm_producers(src, X, topk_ids, W1, H, sorted_pairs, expert_offsets,
+                                    expert_begin: int, flags, counters, epoch: int, order=None,
+                                    n_producers: int = 0, err_word=None, spin_limit: int = 0,
+                                    stream=None) -> None:
+    """fm_moe_ag_gather_gemm whose own producer workgroups copy token chunk c
+    from src[c] (None: already in X) into X and publish flags[c] = epoch."""
+    T, hidden = X.shape
+    n_local, h2, ffn = W1.shape
+    topk = topk_ids.shape[1]
+    n = len(src)
+    if (h2 != hidden or H.shape[1] != ffn or H.shape[0] < T * topk or W1.dtype != X.dtype
+            or T % n or any(x is not None and (tuple(x.shape) != (T // n, hidden)
+                                               or x.dtype != X.dtype) for x in src)):
+        raise ValueError("fm_moe_ag_gather_gemm_producers: shape or dtype mismatch")
+    ptrs = (ctypes.c_void_p * n)(*[_ptr(x) if x is not None else None for x in src])
+    o = _order_arg(order)
+    _check("fm_moe_ag_gather_gemm_producers", lib().fm_moe_ag_gather_gemm_producers(
+        _dt(X), T, hidden, ffn, topk, int(expert_begin), n_local, _ptr(X), _ptr(topk_ids),
+        _ptr(W1), _ptr(H), _ptr(sorted_pairs), _ptr(expert_offsets), n,
+        ctypes.cast(ptrs, ctypes.c_void_p), _ptr(flags), _ptr(counters),
+        ctypes.c_uint32(epoch & 0xFFFFFFFF),
+        ctypes.cast(o, ctypes.c_void_p) if o is not None else None, int(n_producers),
         _ptr(err_word), int(spin_limit), _stream(stream)))
 
 

@@ -47,13 +47,9 @@ struct DenseArgs {
   // straddles two buffers (a ragged chunk ends in a partial tile).
   int tiles_per_chunk;
   const char* chunk_a[kMaxChunks];
-  // AllGather with producer workgroups: chunk_a[c] is chunk c's source (null:
-  // already in X), copied into xw by n_prod workgroups in the order order_c.
-  int n_prod;
-  char* xw;
-  uint32_t* flags_w;
-  uint32_t* counters;
-  uint8_t order_c[kMaxChunks];
+  // AllGather with producer workgroups (AGX): the first prod.n_prod
+  // workgroups copy the chunks into X.
+  ProducerArgs prod;
   // ReduceScatter: destination slices
   int32_t atomic;
   int64_t slice_rows;
@@ -115,52 +111,6 @@ __device__ __forceinline__ void store_tile(Eng& eng, const DenseArgs& args, int6
   }
 }
 
-// Producer workgroup p of P (AGX): for each chunk in arrival order, copy its
-// p-th share into X, then check in on the chunk's counter; the last of the P
-// workgroups resets the counter and publishes the chunk's flag (release).
-// All producers work on the same chunk at a time, so chunks complete in
-// arrival order.  Chunks without a source are published by workgroup 0.
-template <int NT>
-__device__ __forceinline__ void produce_chunks(const DenseArgs& args) {
-  const int p = blockIdx.x, P = args.n_prod, t = threadIdx.x;
-  const int64_t chunk_bytes = args.chunk_rows * args.K * 2;
-  const int64_t n16 = chunk_bytes / 16;
-  const int64_t per = cdiv(cdiv(n16, P), NT) * NT;
-  const int64_t b0 = min((int64_t)p * per, n16), b1 = min(b0 + per, n16);
-  const int n_chunks = (int)(args.M / args.chunk_rows);
-  if (p == 0 && t == 0)
-    for (int c = 0; c < n_chunks; ++c)
-      if (!args.chunk_a[c])
-        __hip_atomic_store(args.flags_w + c, args.epoch, __ATOMIC_RELEASE,
-                           __HIP_MEMORY_SCOPE_AGENT);
-  for (int a = 0; a < n_chunks; ++a) {
-    const int c = args.order_c[a];
-    if (!args.chunk_a[c]) continue;
-    const u32x4* __restrict__ src = reinterpret_cast<const u32x4*>(args.chunk_a[c]);
-    u32x4* __restrict__ dst = reinterpret_cast<u32x4*>(args.xw + c * chunk_bytes);
-    int64_t i = b0 + t;
-    for (; i + 3 * NT < b1; i += 4 * NT) {
-      const u32x4 x0 = src[i], x1 = src[i + NT], x2 = src[i + 2 * NT], x3 = src[i + 3 * NT];
-      dst[i] = x0;
-      dst[i + NT] = x1;
-      dst[i + 2 * NT] = x2;
-      dst[i + 3 * NT] = x3;
-    }
-    for (; i < b1; i += NT) dst[i] = src[i];
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (t == 0) {
-      const uint32_t prev =
-          __hip_atomic_fetch_add(args.counters + c, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      if (prev == (uint32_t)P - 1) {
-        __hip_atomic_store(args.counters + c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(args.flags_w + c, args.epoch, __ATOMIC_RELEASE,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
-}
-
 template <class E, int BM, int BN, int NW, Mode MODE, bool OUT32, bool KTAIL>
 __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args) {
   // One wave per SIMD has the register room for a two-sub-step read-ahead.
@@ -172,12 +122,12 @@ __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args)
   if constexpr (MODE == Mode::AGX) {
     // The producers take the first workgroup ids, so they are dispatched
     // before any consumer that may wait on them.
-    if (wg < args.n_prod) {
-      produce_chunks<64 * NW>(args);
+    if (wg < args.prod.n_prod) {
+      produce_chunks<64 * NW>(args.prod);
       return;
     }
-    wg -= args.n_prod;
-    G -= args.n_prod;
+    wg -= args.prod.n_prod;
+    G -= args.prod.n_prod;
   }
   Eng eng(smem, args.K);
   const int64_t M = args.M, N = args.N, K = args.K;
@@ -385,7 +335,8 @@ bool valid_ab(fm_dtype_t dt) { return dt == FM_F16 || dt == FM_BF16; }
 template <Mode MODE, bool OUT32>
 void launch_one(fm_dtype_t dt, TileCfg cfg, const DenseArgs& args, hipStream_t stream) {
   const int n_pos = (args.pos_end - args.pos0) * args.sub_n;
-  const dim3 grid(args.n_prod + std::min(n_pos, device_cu_count() - args.n_prod));
+  const int P = args.prod.n_prod;
+  const dim3 grid(P + std::min(n_pos, device_cu_count() - P));
 #define FM_LAUNCH(E, BM, BN, NW)                                                              \
   do {                                                                                        \
     if (args.K % kBK) /* ragged K: the 4-wave form keeps the tail path spill-free */          \
@@ -655,16 +606,11 @@ extern "C" fm_status_t fm_ag_gemm_producers(fm_dtype_t dt, int64_t M, int64_t N,
   args.N = N;
   args.K = K;
   args.flags = flags;
-  args.flags_w = flags;
-  args.counters = counters;
-  args.xw = (char*)X;
   args.epoch = epoch;
   args.chunk_rows = M / n_chunks;
   args.err_word = err_word;
   args.spin_limit = spin_limit ? spin_limit : (1ll << 24);
-  args.n_prod = P;
-  for (int c = 0; c < n_chunks; ++c) args.chunk_a[c] = (const char*)src[c];
-  for (int a = 0; a < n_chunks; ++a) args.order_c[a] = (uint8_t)(order ? order[a] : a);
+  fill_producers(args.prod, P, n_chunks, chunk_bytes, src, order, X, flags, counters, epoch);
   fill_order(args.order, M, N, cfg);
   std::vector<int> key(args.order.tiles_m);
   for (int tm = 0; tm < args.order.tiles_m; ++tm) {

@@ -154,6 +154,9 @@ struct MoeArgs {
   // chunk they need to arrive (chunk_pos[c] = arrival position of chunk c).
   int ag_group;
   uint8_t chunk_pos[64];
+  // Token chunks copied by the first prod.n_prod workgroups of layer 0's own
+  // launch (prod.n_prod == 0: the chunks arrive from elsewhere).
+  ProducerArgs prod;
 };
 
 // Epochs of the combine's tile flags: one per call, process-wide, never 0
@@ -220,6 +223,17 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   __shared__ int s_btile0[SCATTER ? 1 : kMaxBands + 1];
   uint64_t ready = 0;   // token chunks this workgroup has already acquired
 
+  int wg = blockIdx.x, G = gridDim.x;
+  if constexpr (!SCATTER) {
+    // Producers take the lowest workgroup ids: they are dispatched before any
+    // consumer that may wait on their chunks.
+    if (wg < a.prod.n_prod) {
+      produce_chunks<64 * NW>(a.prod);
+      return;
+    }
+    wg -= a.prod.n_prod;
+    G -= a.prod.n_prod;
+  }
   const int t = threadIdx.x;
   const int gmb = SCATTER ? 1 : a.ag_group;
   if (t <= a.n_local) s_off[t] = a.offsets[t];
@@ -310,8 +324,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   Eng eng(smem, a.K);
   const int64_t N = a.N, K = a.K;
   const int total = s_tile0[a.n_local];
-  const int G = gridDim.x;
-  const int slot = xcd_slot(blockIdx.x, G);
+  const int slot = xcd_slot(wg, G);
   int full = total;
   if (a.split) {
     const int rem = total % a.g_ref;
@@ -495,6 +508,21 @@ MoeTile moe_tile(bool scatter) {
   return {256, 256, nw_default};
 }
 
+// Producer workgroups for layer 0's own token copies: one per ~5 MiB, a
+// multiple of 8 (one per XCD per round), 8..64.  The consumer tile count
+// lives on the device, so unlike the dense operator the choice cannot count
+// tile waves.  On the EP=8 workload (7 chunks of 16 MiB, ~5.5 waves of
+// tiles, so every producer CU costs compute) 8/16/24/32/48/64 producers took
+// 0.79/0.70/0.69/0.74/0.74/0.80 ms (non-fused layer 0: 0.65 ms).
+int moe_producers_default(int64_t bytes) {
+  if (const char* env = std::getenv("FM_PRODUCERS")) {
+    const int p = std::atoi(env);
+    if (p >= 8 && p <= device_cu_count() / 2 && p % 8 == 0) return p;
+  }
+  const int64_t p = (cdiv(bytes, 5ll << 20) + 7) / 8 * 8;
+  return (int)std::min<int64_t>(64, std::max<int64_t>(8, p));
+}
+
 // M-tiles per band of the token-AllGather order.  At the EP=8 shape two
 // 256-row tiles of one expert span about a quarter of a 2048-token chunk, so
 // the first waves need only the earliest chunks.  Measured with copy-engine
@@ -522,7 +550,11 @@ fm_status_t launch_moe(fm_dtype_t dt, MoeTile cfg, MoeArgs& a, hipStream_t strea
   a.spin_limit = 1ll << 26;
   a.g_ref = device_cu_count();
   const char* env = std::getenv("FM_SPLIT_TAIL");
-  a.split = (!SCATTER && cfg.bm == 256 && cfg.bn == 256 && !(env && env[0] == '0')) ? 1 : 0;
+  // (no split with producer workgroups: producers and consumers share one launch)
+  a.split = (!SCATTER && cfg.bm == 256 && cfg.bn == 256 && !(env && env[0] == '0') &&
+             a.prod.n_prod == 0)
+                ? 1
+                : 0;
   a.part = 0;
   if (SCATTER) {
     // one completion flag per (M-tile, N-tile); M-tiles <= pairs/BM + experts
@@ -611,7 +643,9 @@ fm_status_t moe_gather_impl(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ff
                             const int32_t* topk_ids, const void* W1, void* H,
                             int32_t* sorted_pairs, int32_t* expert_offsets, int32_t n_chunks,
                             const uint32_t* flags, uint32_t epoch, const int32_t* order,
-                            int32_t* err_word, int64_t spin_limit, hipStream_t stream) {
+                            int32_t* err_word, int64_t spin_limit, hipStream_t stream,
+                            const void* const* src = nullptr, uint32_t* counters = nullptr,
+                            int32_t n_producers = 0) {
   if (dt != FM_F16 && dt != FM_BF16) return FM_ERR_UNSUPPORTED;
   fm_status_t st = check_route_args(T, topk, n_local, topk_ids, sorted_pairs, expert_offsets);
   if (st != FM_OK) return st;
@@ -630,6 +664,21 @@ fm_status_t moe_gather_impl(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ff
       if (c < 0 || c >= n_chunks || seen[c]) return FM_ERR_INVALID_ARG;
       seen[c] = true;
       pos[c] = (uint8_t)i;
+    }
+  }
+  // Producer workgroups: sources must be aligned and lie outside X.
+  const int64_t chunk_bytes = flags ? (T / n_chunks) * hidden * 2 : 0;
+  if (src) {
+    if (!counters || (reinterpret_cast<uintptr_t>(counters) & 3u)) return FM_ERR_INVALID_ARG;
+    if (n_producers != 0 && (n_producers < 8 || n_producers % 8 ||
+                             n_producers > device_cu_count() / 2))
+      return FM_ERR_INVALID_ARG;
+    const char* xb = (const char*)X;
+    for (int c = 0; c < n_chunks; ++c) {
+      const char* sc = (const char*)src[c];
+      if (!sc) continue;
+      if (!aligned16(sc)) return FM_ERR_INVALID_ARG;
+      if (xb && sc < xb + T * hidden * 2 && xb < sc + chunk_bytes) return FM_ERR_INVALID_ARG;
     }
   }
   // gathered-row byte offsets are 32-bit
@@ -657,6 +706,11 @@ fm_status_t moe_gather_impl(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ff
     a.err_word = err_word;
     a.chunk_spin = spin_limit ? spin_limit : (1ll << 24);
     std::memcpy(a.chunk_pos, pos, sizeof(pos));
+  }
+  if (src) {
+    const int P = n_producers ? n_producers : moe_producers_default(chunk_bytes * n_chunks);
+    fill_producers(a.prod, P, n_chunks, chunk_bytes, src, order, const_cast<void*>(X),
+                   const_cast<uint32_t*>(flags), counters, epoch);
   }
   a.ag_group = moe_ag_group();
   return launch_moe<false>(dt, moe_tile(false), a, stream);
@@ -689,6 +743,18 @@ extern "C" fm_status_t fm_moe_ag_gather_gemm(fm_dtype_t dt, int64_t T, int64_t h
   return moe_gather_impl(dt, T, hidden, ffn, topk, expert_begin, n_local, X, topk_ids, W1, H,
                          sorted_pairs, expert_offsets, n_chunks, flags, epoch, order, err_word,
                          spin_limit, stream);
+}
+
+extern "C" fm_status_t fm_moe_ag_gather_gemm_producers(
+    fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn, int32_t topk, int32_t expert_begin,
+    int32_t n_local, void* X, const int32_t* topk_ids, const void* W1, void* H,
+    int32_t* sorted_pairs, int32_t* expert_offsets, int32_t n_chunks, const void* const* src,
+    uint32_t* flags, uint32_t* counters, uint32_t epoch, const int32_t* order,
+    int32_t n_producers, int32_t* err_word, int64_t spin_limit, hipStream_t stream) {
+  if (!flags || !src) return FM_ERR_INVALID_ARG;
+  return moe_gather_impl(dt, T, hidden, ffn, topk, expert_begin, n_local, X, topk_ids, W1, H,
+                         sorted_pairs, expert_offsets, n_chunks, flags, epoch, order, err_word,
+                         spin_limit, stream, src, counters, n_producers);
 }
 
 extern "C" fm_status_t fm_moe_gemm_scatter(fm_dtype_t dt, int64_t T, int64_t hidden,

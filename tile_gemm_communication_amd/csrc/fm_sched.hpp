@@ -76,6 +76,78 @@ __device__ __forceinline__ bool wait_chunks(const uint32_t* flags, uint32_t epoc
   return true;
 }
 
+// Producer workgroups of an AllGather launch (COMET-style split of
+// workgroups into communication and computation roles): chunk c's source
+// src[c] (null: already in X) is copied into rows of X by the first n_prod
+// workgroups, chunks taken in `order`.
+struct ProducerArgs {
+  int n_prod, n_chunks;
+  int64_t chunk_bytes;
+  char* X;
+  uint32_t* flags;
+  uint32_t* counters;   // zero before and after every launch
+  uint32_t epoch;
+  uint8_t order[64];
+  const char* src[64];
+};
+
+// Producer workgroup p of P: for each chunk in arrival order, copy its p-th
+// share into X, then check in on the chunk's counter; the last of the P
+// workgroups resets the counter and publishes the chunk's flag (release).
+// All producers work on the same chunk at a time, so chunks complete in
+// arrival order.  Chunks without a source are published by workgroup 0.
+template <int NT>
+__device__ __forceinline__ void produce_chunks(const ProducerArgs& pa) {
+  const int p = blockIdx.x, P = pa.n_prod, t = threadIdx.x;
+  const int64_t n16 = pa.chunk_bytes / 16;
+  const int64_t per = cdiv(cdiv(n16, P), NT) * NT;
+  const int64_t b0 = min((int64_t)p * per, n16), b1 = min(b0 + per, n16);
+  if (p == 0 && t == 0)
+    for (int c = 0; c < pa.n_chunks; ++c)
+      if (!pa.src[c])
+        __hip_atomic_store(pa.flags + c, pa.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  for (int a = 0; a < pa.n_chunks; ++a) {
+    const int c = pa.order[a];
+    if (!pa.src[c]) continue;
+    const u32x4* __restrict__ src = reinterpret_cast<const u32x4*>(pa.src[c]);
+    u32x4* __restrict__ dst = reinterpret_cast<u32x4*>(pa.X + c * pa.chunk_bytes);
+    int64_t i = b0 + t;
+    for (; i + 3 * NT < b1; i += 4 * NT) {
+      const u32x4 x0 = src[i], x1 = src[i + NT], x2 = src[i + 2 * NT], x3 = src[i + 3 * NT];
+      dst[i] = x0;
+      dst[i + NT] = x1;
+      dst[i + 2 * NT] = x2;
+      dst[i + 3 * NT] = x3;
+    }
+    for (; i < b1; i += NT) dst[i] = src[i];
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are done
+    __syncthreads();
+    if (t == 0) {
+      const uint32_t prev =
+          __hip_atomic_fetch_add(pa.counters + c, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == (uint32_t)P - 1) {
+        __hip_atomic_store(pa.counters + c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(pa.flags + c, pa.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
+// Host: fill a ProducerArgs (order == null: index order).
+inline void fill_producers(ProducerArgs& pa, int P, int n_chunks, int64_t chunk_bytes,
+                           const void* const* src, const int32_t* order, void* X,
+                           uint32_t* flags, uint32_t* counters, uint32_t epoch) {
+  pa.n_prod = P;
+  pa.n_chunks = n_chunks;
+  pa.chunk_bytes = chunk_bytes;
+  pa.X = (char*)X;
+  pa.flags = flags;
+  pa.counters = counters;
+  pa.epoch = epoch;
+  for (int c = 0; c < n_chunks; ++c) pa.src[c] = (const char*)src[c];
+  for (int a = 0; a < n_chunks; ++a) pa.order[a] = (uint8_t)(order ? order[a] : a);
+}
+
 // Store 16 bytes written through every cache level (system-scope store):
 // once the wave's vmcnt drains, the data is visible device-wide without an
 // L2 write-back.  Used for data that a counted tile hands to a tile that may
