@@ -27,6 +27,11 @@ struct F16 {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
+  // 16x16x32 accumulating in place (the accumulator stays in its AGPRs; the
+  // builtin's result gets a register of its own and is copied back).
+  __device__ static inline void mfma16_acc(u32x4 a, u32x4 b, f32x4& c) {
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  }
   // Round two fp32 values to nearest-even 16-bit and pack (lo = x, hi = y).
   __device__ static inline uint32_t pack2(float x, float y) {
     _Float16 a = (_Float16)x, b = (_Float16)y;
@@ -39,6 +44,9 @@ struct BF16 {
   __device__ static inline f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline void mfma16_acc(u32x4 a, u32x4 b, f32x4& c) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
   }
   __device__ static inline uint32_t pack2(float x, float y) {
     __bf16 a = (__bf16)x, b = (__bf16)y;

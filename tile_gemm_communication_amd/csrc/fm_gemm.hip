@@ -26,6 +26,14 @@ namespace fm {
 enum class Mode : int { Gemm = 0, AG = 1, RS = 2, RSG = 3, AGP = 4, AGX = 5 };
 
 constexpr int kMaxRanks = 16;
+// Dense kernels with one wave per SIMD may use the 16x16x32 MFMA form (the
+// engine's MF16 path).  It passes every parity test but measured no faster
+// than 32x32x16 here (AG shape 0.51 vs 0.50 ms, GEMM-RS 0.54 vs 0.53 ms), so
+// it is off; the compile-time switch keeps it for later tuning.
+#ifndef FM_MFMA16
+#define FM_MFMA16 0
+#endif
+constexpr bool kMfma16 = FM_MFMA16 != 0;
 // In-tile byte offsets are 32-bit (tile rows x row pitch), which bounds each
 // dimension to 2^22 elements.
 constexpr int64_t kMaxDim = 1ll << 22;
@@ -113,8 +121,9 @@ __device__ __forceinline__ void store_tile(Eng& eng, const DenseArgs& args, int6
 
 template <class E, int BM, int BN, int NW, Mode MODE, bool OUT32, bool KTAIL>
 __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args) {
-  // One wave per SIMD has the register room for a two-sub-step read-ahead.
-  using Eng = Engine<E, BM, BN, KTAIL, NW, 4, NW == 4 ? 2 : 1>;
+  // One wave per SIMD has the register room for a two-sub-step read-ahead,
+  // or for the 16x16x32 MFMA form.
+  using Eng = Engine<E, BM, BN, KTAIL, NW, 4, NW == 4 ? 2 : 1, kMfma16 && NW == 4 && !KTAIL>;
   __shared__ __attribute__((aligned(16))) char smem[Eng::LDS_BYTES];
   __shared__ int s_abort;
 

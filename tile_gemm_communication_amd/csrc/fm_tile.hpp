@@ -46,7 +46,24 @@
 // result block is C^T in the instruction's layout: lane l holds row
 // m = l % 32 of C and, for item 4r+q, column n = 8r + 4(l/32) + q; every lane
 // owns runs of 4 consecutive output columns.
+//
+// MF16 selects v_mfma_f32_16x16x32 instead (one wave per SIMD only).  Under
+// the chip's power limit it does more work per joule in isolation: with
+// N(0,1) operands a register-only loop ran 1786 TFLOP/s at 1.82 GHz against
+// 1650 at 1.65 GHz for the 32x32x16 form, since it moves a quarter of the
+// accumulator bits per flop; in the full GEMM (LDS and DMA traffic, one wave
+// per SIMD) it measured 1-3% slower, so the kernels build it only on request.
+// The MFMA is issued from inline assembly with the accumulator tied in place:
+// the builtin's result takes fresh AGPRs, and the copies back filled the K
+// loop with ~470 accumulator moves and spills.  A K step then has two sub-steps of 32; the fragments of a 16x16
+// block come from the same LDS layout (A: one 16-byte read, rows 16i + l%16,
+// K chunk 4ks + l/16; B: two transposing reads, K rows 32ks + 8(l/16) + 0..7
+// of column l%16), and the result block (C^T again) gives lane l row
+// 16i + l%16 and columns 4(l/16)..+3 of its 16-column block.
 #pragma once
+
+#include <type_traits>
+#include <utility>
 
 #include "fm_common.hpp"
 
@@ -77,6 +94,18 @@ __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t
 }
 #pragma clang diagnostic pop
 
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1,
+// every iteration its own code (no loop left for the compiler to keep, so
+// register arrays indexed by I stay in registers however long the body).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // Scheduling hint: alternate MFMAs and LDS reads (one each, READS times),
 // then the remaining MFMAs.
 template <int MFMAS, int READS>
@@ -89,18 +118,23 @@ __device__ __forceinline__ void interleave() {
   if constexpr (MFMAS > READS) __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - READS, 0);
 }
 
-template <class E, int BM, int BN, bool KTAIL, int NW = 4, int BSWZ = 4, int DEPTH_ = 1>
+template <class E, int BM, int BN, bool KTAIL, int NW = 4, int BSWZ = 4, int DEPTH_ = 1,
+          bool MF16 = false>
 struct Engine {
   // Fragment read-ahead in sub-steps: 1 = the next sub-step (two register
   // slots), 2 = two sub-steps ahead (four slots, one per sub-step; needs the
-  // register room of one wave per SIMD).  A K tail always uses 1.
-  static constexpr int DEPTH = KTAIL ? 1 : DEPTH_;
+  // register room of one wave per SIMD).  A K tail, and the 16x16 form (whose
+  // sub-step is already half a K step), always use 1.
+  static constexpr int DEPTH = (KTAIL || MF16) ? 1 : DEPTH_;
   static constexpr int NSLOT = DEPTH == 2 ? 4 : 2;
   static constexpr int NWM = 2, NWN = NW / 2;          // wave grid over the tile
   static constexpr int THREADS = 64 * NW;
   static constexpr int BM_ = BM, BN_ = BN;
   static constexpr int WM = BM / NWM, WN = BN / NWN;
   static constexpr int FM = WM / 32, FN = WN / 32;     // 32x32 blocks per wave
+  static constexpr int BMF = MF16 ? 16 : 32;            // MFMA block edge
+  static constexpr int FMB = WM / BMF, FNB = WN / BMF;  // MFMA blocks per wave
+  static constexpr int NSUB = MF16 ? 2 : 4;             // sub-steps per K step
   static constexpr int A_STAGE = BM * 128;
   static constexpr int B_ROW = BN * 2;
   static constexpr int B_STAGE = 64 * B_ROW;
@@ -112,13 +146,14 @@ struct Engine {
   static constexpr int B_RPI = 64 / B_CPR;              // B rows per 1 KB DMA instruction
   static constexpr int B_DMA = BN / (8 * NW);
   static constexpr int DMA = A_DMA + B_DMA;
-  static constexpr int READS = FM + 2 * FN;             // LDS reads per sub-step
-  static constexpr int MFMAS = FM * FN;                 // MFMAs per sub-step
+  static constexpr int READS = FMB + 2 * FNB;           // LDS reads per sub-step
+  static constexpr int MFMAS = FMB * FNB;               // MFMAs per sub-step
   static_assert(BM == 128 || BM == 256, "BM must be 128 or 256");
   static_assert(BN == 128 || BN == 256, "BN must be 128 or 256");
   static_assert(BSWZ == 2 || BSWZ == 4, "B swizzle step");
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(A_DMA >= 1 && B_DMA >= 1 && WN >= 32, "tile too small for the wave grid");
+  static_assert(!MF16 || NW == 4, "the 16x16 form needs the registers of one wave per SIMD");
 
   char* smem;
   uint32_t lds0;   // LDS byte address of smem (wave-uniform)
@@ -126,9 +161,10 @@ struct Engine {
   int64_t K;
   int KT;
 
-  f32x16 acc[FM][FN];
-  u32x4 fa[NSLOT][FM];
-  u32x4 fb[NSLOT][FN];
+  using AccT = typename std::conditional<MF16, f32x4, f32x16>::type;
+  AccT acc[FMB][FNB];
+  u32x4 fa[NSLOT][FMB];
+  u32x4 fb[NSLOT][FNB];
 
   // DMA sources: wave-uniform bases (K offset 0) plus per-lane 32-bit offsets.
   const char* a_base;
@@ -140,8 +176,12 @@ struct Engine {
   // LDS read offsets (bytes from smem): A by (sub-step, block parity), B by
   // block-column variant; everything else is an immediate.
   static constexpr int BV = (BSWZ == 2) ? 2 : 4;   // B address variants
-  uint32_t ra_off[4][2];
-  uint32_t rb_off[BV];
+  // MF16: A offsets by swizzle variant p (sub-step ks uses p ^ 2ks), B by
+  // bits 1-2 of the block index (bit 0 is an immediate).
+  static constexpr int RA_KS = MF16 ? 1 : 4, RA_P = MF16 ? 4 : 2;
+  static constexpr int RB_N = MF16 ? 4 : BV;
+  uint32_t ra_off[RA_KS][RA_P];
+  uint32_t rb_off[RB_N];
 
   __device__ __forceinline__ Engine(char* s, int64_t K_) : smem(s), K(K_) {
     const int t = threadIdx.x;
@@ -151,6 +191,30 @@ struct Engine {
     wn = w % NWN;
     lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)s);
     KT = (int)cdiv(K, kBK);
+    if constexpr (MF16) {
+      // A fragment of 16x16 block i, sub-step ks: row m = wm*WM + 16i + r16,
+      // chunk 4ks + l/16 = 4ks ^ q4; swz_a(m) = s0 ^ 2(i&3) with
+      // s0 = (r16 ^ r16>>3) & 7, so the physical chunk is
+      // q4 ^ s0 ^ 2((i&3) ^ 2ks): variant p = (i ^ 2ks) & 3.
+      const int r16 = lane & 15, q4 = lane >> 4;
+      const int s0 = (r16 ^ (r16 >> 3)) & 7;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        ra_off[0][p] = (wm * WM + r16) * 128 + (((q4 ^ s0 ^ (2 * p)) & 7) << 4);
+      // B fragment of block j = 2a + b: group g = l/16 covers K rows 8g..+7
+      // of the sub-step and the block's 16 columns; lane j16 addresses K row
+      // +(j16>>2) (swizzle z) and columns 16j + 4(j16&3), i.e. chunk
+      // wn*WN/8 + 4a + 2b + ((j16&3)>>1).  The xor with z only touches bits
+      // 2-3, so variant a carries it and b is an immediate of 32 bytes.
+      const int j16 = lane & 15;
+      const int z = BSWZ * ((j16 >> 2) & 3);
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int X = wn * WN / 8 + 4 * a4 + ((j16 & 3) >> 1);
+        rb_off[a4] = LDS_B + (8 * q4 + (j16 >> 2)) * B_ROW + ((X ^ z) << 4) + 8 * (j16 & 1);
+      }
+      return;
+    }
     // A fragment of block i, sub-step ks: row m = wm*WM + 32i + r32, chunk
     // 2ks + hi; swz_a(m) = s0 ^ 4(i&1) with s0 = (r32 ^ r32>>3) & 7.
     const int r32 = lane & 31, hi = lane >> 5;
@@ -205,9 +269,9 @@ struct Engine {
 
   __device__ __forceinline__ void zero_acc() {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FMB; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+      for (int j = 0; j < FNB; ++j) acc[i][j] = AccT{};
   }
 
   // Issue the DMA of K step kt into buffer buf.  check: mask K chunks >= K
@@ -242,9 +306,9 @@ struct Engine {
   static constexpr int RITEMS = READS;
   static constexpr int item_code(int q) {
     int n = 0;
-    for (int k = 0; k < (FM > FN ? FM : FN); ++k) {
-      if (k < FM) { if (n == q) return k * 4 + 0; ++n; }
-      if (k < FN) {
+    for (int k = 0; k < (FMB > FNB ? FMB : FNB); ++k) {
+      if (k < FMB) { if (n == q) return k * 4 + 0; ++n; }
+      if (k < FNB) {
         if (n == q) return k * 4 + 1;
         ++n;
         if (n == q) return k * 4 + 2;
@@ -260,10 +324,17 @@ struct Engine {
     const int code = item_code(q);
     const int j = code >> 2, kind = code & 3;
     if (kind == 0) {
-      fa[slot][j] = *reinterpret_cast<const u32x4*>(sa + ra_off[ks][j & 1] + j * 32 * 128);
+      if constexpr (MF16)
+        fa[slot][j] =
+            *reinterpret_cast<const u32x4*>(sa + ra_off[0][(j ^ (2 * ks)) & 3] + j * 16 * 128);
+      else
+        fa[slot][j] = *reinterpret_cast<const u32x4*>(sa + ra_off[ks][j & 1] + j * 32 * 128);
     } else {
       const int hh = kind - 1;
-      const char* p = sb + rb_off[j % BV] + (16 * ks + 4 * hh) * B_ROW + (j / BV) * (64 * BV);
+      const char* p = MF16 ? sb + rb_off[(j >> 1) & 3] + (32 * ks + 4 * hh) * B_ROW +
+                                 (j & 1) * 32 + (j >> 3) * 256
+                           : sb + rb_off[j % RB_N] + (16 * ks + 4 * hh) * B_ROW +
+                                 (j / BV) * (64 * BV);
       const s16x4 h = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FM_LDS4(p));
       const u32x2 hv = __builtin_bit_cast(u32x2, h);
       if (hh == 0) { fb[slot][j][0] = hv[0]; fb[slot][j][1] = hv[1]; }
@@ -301,10 +372,13 @@ struct Engine {
   // [d0, d1) of K step dma_kt.
   __device__ __forceinline__ void substep_g(int mslot, int nbuf, int nks, int rslot,
                                             bool do_read, int dma_kt, int dbuf, int d0, int d1) {
-#pragma unroll
-    for (int q = 0; q < MFMAS; ++q) {
-      const int i = q / FN, j = q % FN;
-      acc[i][j] = E::mfma32(fb[mslot][j], fa[mslot][i], acc[i][j]);
+    static_for<MFMAS>([&](auto qc) {
+      constexpr int q = decltype(qc)::value;
+      constexpr int i = q / FNB, j = q % FNB;
+      if constexpr (MF16)
+        E::mfma16_acc(fb[mslot][j], fa[mslot][i], acc[i][j]);
+      else
+        acc[i][j] = E::mfma32(fb[mslot][j], fa[mslot][i], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
       if (do_read && q < RITEMS) {
         read_item(q, nbuf, nks, rslot);
@@ -314,7 +388,7 @@ struct Engine {
         dma_item(d0 + q, dma_kt, dbuf);
         __builtin_amdgcn_sched_barrier(0);
       }
-    }
+    });
     if (do_read) {       // more read items than MFMAs (small tiles)
 #pragma unroll
       for (int q = MFMAS; q < RITEMS; ++q) read_item(q, nbuf, nks, rslot);
@@ -340,14 +414,6 @@ struct Engine {
     substep_g(3, cur ^ 1, 1, 1, true, dk, cur, DMA / 2, DMA);
   }
 
-  __device__ __forceinline__ void mma(int slot, int i0, int i1) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      if (i < i0 || i >= i1) continue;
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = E::mfma32(fb[slot][j], fa[slot][i], acc[i][j]);
-    }
-  }
 
   // One K step kt (buffer cur = kt & 1):
   //   sub-steps 0..2: MFMAs on the fragments in registers while the next
@@ -362,6 +428,19 @@ struct Engine {
   // data is never overwritten).  The accumulators thus stay in one place.
   __device__ __forceinline__ void step(int kt) {
     const int cur = kt & 1;
+    if constexpr (MF16) {
+      // two sub-steps of 32: the second reads sub-step 0 of stage kt+1
+      substep(0, cur, 1, true, -1, 0);
+      wait_all0();
+      __syncthreads();
+      if constexpr (!KTAIL) {
+        substep(1, cur ^ 1, 0, true, min(kt + 2, KT - 1), cur);
+      } else {
+        if (kt + 2 < KT) dma(kt + 2, cur, kt + 3 == KT);
+        substep(1, cur ^ 1, 0, true, -1, 0);
+      }
+      return;
+    }
     substep(0, cur, 1, true, -1, 0);
     substep(1, cur, 2, true, -1, 0);
     substep(0, cur, 3, true, -1, 0);
@@ -398,19 +477,17 @@ struct Engine {
     }
   }
 
-  // Output coordinates (within the tile) owned by this lane: block (i, j),
-  // 4-column run r (0..3) holds row out_row(i) and columns out_col(j, r)..+3.
-  __device__ __forceinline__ int out_row(int i) const { return wm * WM + i * 32 + (lane & 31); }
-  __device__ __forceinline__ int out_col(int j, int r) const {
-    return wn * WN + j * 32 + 8 * r + 4 * (lane >> 5);
-  }
   // Pin accumulator block (i, j) in AGPRs at this point of the program, so
   // its copy into VGPRs for the epilogue cannot be hoisted above the stores
   // of earlier blocks (which would need all 256 accumulators in VGPRs).
   __device__ __forceinline__ void pin(int i, int j) { asm volatile("" : "+a"(acc[i][j])); }
   __device__ __forceinline__ f32x4 out_vals(int i, int j, int r) const {
-    return f32x4{acc[i][j][4 * r + 0], acc[i][j][4 * r + 1], acc[i][j][4 * r + 2],
-                 acc[i][j][4 * r + 3]};
+    if constexpr (MF16) {
+      return acc[i][j];
+    } else {
+      return f32x4{acc[i][j][4 * r + 0], acc[i][j][4 * r + 1], acc[i][j][4 * r + 2],
+                   acc[i][j][4 * r + 3]};
+    }
   }
 
   // -- LDS-staged epilogue ----------------------------------------------------
@@ -432,6 +509,12 @@ struct Engine {
   // wave reads K-loop data any more.  After the last ep_read: ep_end() before
   // the next tile's DMA may overwrite the regions.
   __device__ __forceinline__ void ep_begin() {
+    if constexpr (MF16) {
+      // The 16x16 MFMAs are issued from inline assembly, so the compiler
+      // inserts no wait states between the last of them and the epilogue's
+      // reads of their accumulators: give them 24 explicitly.
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    }
     wait_vmcnt<0>();
     __syncthreads();
   }
@@ -441,6 +524,19 @@ struct Engine {
     // fence the compiler hoists the loads of later blocks and spills.
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (MF16) {
+      // 16x16 blocks 2i and 2i+1: lane l holds row 16h + l%16 of the staged
+      // block and columns 16j + 4(l/16)..+3.
+      char* reg16 = smem + w * (32 * EP_STRIDE) + (lane & 15) * EP_STRIDE + 16 * (lane >> 4);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < FNB; ++j) {
+          pin(2 * i + h, j);
+          *reinterpret_cast<f32x4*>(reg16 + 16 * h * EP_STRIDE + 64 * j) = acc[2 * i + h][j];
+        }
+      return;
+    }
     char* reg = smem + w * (32 * EP_STRIDE) + (lane & 31) * EP_STRIDE + 16 * (lane >> 5);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
