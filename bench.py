@@ -422,6 +422,31 @@ def ect_block(w, iters):
                                            w.off, w.e0, w.mflags, w.mcounters, w.epoch,
                                            order=w.order, err_word=w.err)
 
+    # pull mode: layer 0 reads each owner's 16 MiB chunk in place, signals
+    # timed at one link's rate (direct: all seven land at t_link)
+    t_link_moe = int(w.mTc * w.hidden * 2 / LINK_BYTES_PER_S * 1e9)
+
+    def moe_pull(times):
+        def fn():
+            w.epoch += 1
+            s = w.sides[0]
+            s.wait_stream(cs)
+            fm.fm_chunk_signal_paced(w.mflags, times, w.epoch, order=w.order, stream=s)
+            fm.fm_moe_ag_gather_gemm_pull(w.mpeers, w.ids, w.mW1, w.H, w.sp, w.off, w.e0,
+                                          w.mflags, w.epoch, order=w.order, err_word=w.err)
+            cs.wait_stream(s)
+        return fn
+
+    def moe_pull_naive(times):
+        def fn():
+            w.epoch += 1
+            s = w.sides[0]
+            s.wait_stream(cs)
+            fm.fm_chunk_signal_paced(w.mflags, times, w.epoch, order=w.order, stream=s)
+            cs.wait_stream(s)                   # the whole AllGather first
+            w.moe0()
+        return fn
+
     log("ECT: token AllGather + MoE layer 0")
     for name, fn in [("nonsplit", moe_ns), ("fused", moe_fused), ("gather_then_gemm", moe_naive),
                      ("producers", moe_producers)]:
@@ -433,6 +458,15 @@ def ect_block(w, iters):
     res["moe_ag_ect_frac_of_nonsplit"] = round(res["moe_ag_ect_ms"] / res["moe_ag_nonsplit_ms"], 4)
     res["moe_ag_ect_producers_ms"] = round(res["moe_ag_producers_ms"] - res["moe_ag_nonsplit_ms"],
                                            4)
+    res["moe_pull_link_chunk_us"] = round(t_link_moe / 1e3, 1)
+    for name, times in [("direct", [0] + [t_link_moe] * (w.n - 1)),
+                        ("ring", [a * t_link_moe for a in range(w.n)])]:
+        med, _ = time_loop(moe_pull(times), iters, 3)
+        res[f"moe_pull_{name}_fused_ms"] = round(med, 4)
+        res[f"moe_pull_{name}_ect_ms"] = round(med - res["moe_ag_nonsplit_ms"], 4)
+        med, _ = time_loop(moe_pull_naive(times), iters, 3)
+        res[f"moe_pull_{name}_gather_then_gemm_ms"] = round(med, 4)
+        res[f"moe_pull_{name}_ect_naive_ms"] = round(med - res["moe_ag_nonsplit_ms"], 4)
     assert int(w.err.item()) == 0, "fm_moe_ag_gather_gemm reported a timeout"
     res["nonsplit_fm_gemm_tflops_4096x12288x6144"] = round(
         w.flop_rs / (res["rs_nonsplit_fm_gemm_ms"] * 1e-3) / 1e12, 1)

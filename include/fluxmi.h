@@ -12,8 +12,9 @@
  *                        scatter-reduce (MoE layer 1)
  * plus the AllGather variants fm_ag_gemm_pull (chunks read in place),
  * fm_ag_gemm_producers (copies done by workgroups of the same launch),
- * fm_moe_ag_gather_gemm (MoE layer 0 behind a token AllGather) and its
- * producer-workgroup form fm_moe_ag_gather_gemm_producers, the producer
+ * fm_moe_ag_gather_gemm (MoE layer 0 behind a token AllGather) with its
+ * producer-workgroup and pull-mode forms (fm_moe_ag_gather_gemm_producers,
+ * fm_moe_ag_gather_gemm_pull), the producer
  * half of the chunk-arrival protocol (fm_chunk_push, fm_chunk_push_dma,
  * fm_chunk_signal_paced) and the routing index on its own (fm_moe_route).
  *
@@ -321,6 +322,27 @@ fm_status_t fm_moe_ag_gather_gemm_producers(
     int32_t* sorted_pairs, int32_t* expert_offsets, int32_t n_chunks, const void* const* src,
     uint32_t* flags, uint32_t* counters, uint32_t epoch, const int32_t* order,
     int32_t n_producers, int32_t* err_word, int64_t spin_limit, hipStream_t stream);
+
+/*
+ * fm_moe_ag_gather_gemm_pull -- fm_moe_ag_gather_gemm in pull mode (FLUX
+ * review, "拉取 vs 推送数据传输"): no gathered token buffer; each layer-0 tile
+ * reads its token rows in place from the owners' chunk buffers (on a node, the
+ * peers' activations mapped into this process), after their flags.  Only the
+ * tokens routed to this rank's experts are ever read.
+ *   chunks  host array of n_chunks device pointers; chunks[c] is the
+ *           16-byte aligned [T/n_chunks, hidden] block of tokens
+ *           [c*T/n_chunks, (c+1)*T/n_chunks).
+ *   the rest  as fm_moe_ag_gather_gemm (flags, epoch, order, err_word,
+ *           spin_limit; signals from fm_chunk_signal_paced or a peer).
+ * The result equals fm_moe_gather_gemm on the concatenated chunks, bit for
+ * bit.
+ */
+fm_status_t fm_moe_ag_gather_gemm_pull(
+    fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn, int32_t topk, int32_t expert_begin,
+    int32_t n_local, const void* const* chunks, const int32_t* topk_ids, const void* W1, void* H,
+    int32_t* sorted_pairs, int32_t* expert_offsets, int32_t n_chunks, const uint32_t* flags,
+    uint32_t epoch, const int32_t* order, int32_t* err_word, int64_t spin_limit,
+    hipStream_t stream);
 
 /*
  * fm_moe_gemm_scatter -- MoE layer 1 on this rank with the top-k weighted

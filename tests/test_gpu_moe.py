@@ -482,6 +482,106 @@ def test_full_moe_ag_producers_rank0(oracle):
     assert torch.equal(H3[:rows].view(torch.int16), H[:rows].view(torch.int16))
 
 
+def _moe_pull_run(inp, chunks, e0, nl, order, times_ns, dt=BF16, spin=0):
+    """fm_moe_ag_gather_gemm_pull with the chunk flags published by
+    fm_chunk_signal_paced on a side stream; returns (off, sp, H, err)."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    n, Tc, hidden = chunks.shape
+    T = n * Tc
+    topk = inp["topk_ids"].shape[1]
+    ffn = inp["W1"].shape[2]
+    src = [dev16(chunks[c], dt) for c in range(n)]
+    H = torch.zeros((T * topk, ffn), dtype=src[0].dtype, device="cuda:0")
+    sp = torch.full((T * topk,), -1, dtype=torch.int32, device="cuda:0")
+    off = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
+    flags = torch.zeros(n, dtype=torch.int32, device="cuda:0")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    side = torch.cuda.Stream()
+    cs = torch.cuda.current_stream()
+    side.wait_stream(cs)
+    fm.fm_chunk_signal_paced(flags, times_ns, 5, order=order, stream=side)
+    fm.fm_moe_ag_gather_gemm_pull(src, _i32(inp["topk_ids"]), dev16(inp["W1"], dt), H, sp, off,
+                                  e0, flags, 5, order=order, err_word=err, spin_limit=spin)
+    cs.wait_stream(side)
+    torch.cuda.synchronize()
+    return off.cpu().numpy(), sp.cpu().numpy(), H, err.item()
+
+
+@pytest.mark.parametrize("T,n,gap_us", [(3000, 8, 20), (2048, 4, 0), (1000, 1, 0)])
+def test_moe_ag_pull(oracle, T, n, gap_us):
+    """Token rows read in place from per-owner chunk buffers, signalled in a
+    seeded random order: H equals the oracle and fm_moe_gather_gemm on the
+    concatenated tokens bit for bit."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    hidden, ffn, E, nl, e0 = 256, 264, 16, 8, 8
+    inp = wl.moe_inputs(T, hidden, ffn, E, nl, 2, BF16, seed=T + 11 * n, zipf_s=1.2)
+    chunks = inp["X"].reshape(n, T // n, hidden)
+    order = wl.permutation(n, seed=T + 3).tolist()
+    say(f"moe ag pull T={T} chunks={n} order={order} gap={gap_us} us")
+    off, sp, H, err = _moe_pull_run(inp, chunks, e0, nl, order,
+                                    [a * gap_us * 1000 for a in range(n)])
+    assert err == 0
+    roff, rsp = oracle.moe_route(inp["topk_ids"], e0, nl)
+    rows = int(roff[-1])
+    assert np.array_equal(off, roff) and np.array_equal(sp[:rows], rsp)
+    ref = oracle.moe_ag_layer0(BF16, list(chunks), inp["W1"], rsp, roff, 2, arrival=order)
+    assert_close(host64(H[:rows]), ref, "moe ag pull")
+    H2 = torch.zeros_like(H)
+    sp2 = torch.full((T * 2,), -1, dtype=torch.int32, device="cuda:0")
+    off2 = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
+    fm.fm_moe_gather_gemm(dev16(inp["X"], BF16), _i32(inp["topk_ids"]), dev16(inp["W1"], BF16),
+                          H2, sp2, off2, e0)
+    torch.cuda.synchronize()
+    assert torch.equal(H[:rows].view(torch.int16), H2[:rows].view(torch.int16))
+
+
+def test_moe_ag_pull_late_chunk_times_out():
+    """A chunk signalled long after the consumers' spin bound: FM_ERR_TIMEOUT."""
+    import tile_gemm_communication_amd as fm
+    T, hidden, ffn, n = 512, 128, 64, 4
+    inp = wl.moe_inputs(T, hidden, ffn, 8, 8, 2, BF16, seed=13)
+    chunks = inp["X"].reshape(n, T // n, hidden)
+    _, _, _, err = _moe_pull_run(inp, chunks, 0, 8, [0, 1, 2, 3], [0, 0, 0, 200_000_000],
+                                 spin=2000)
+    assert err == fm.FM_ERR_TIMEOUT
+
+
+def test_full_moe_ag_pull_link_paced(oracle):
+    """EP=8 rank 0 reading the 8 owners' 2048-token chunks in place, signalled
+    in ring order at the one-link rate (16 MiB at 153 GB/s apart): sampled rows
+    against the oracle, bit-identical to the non-fused layer 0."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    c = wl.MOE_EP8
+    say("full moe ag pull EP=8 rank 0, link-paced")
+    inp = wl.moe_inputs(c["T"], c["hidden"], c["ffn"], c["n_experts"], c["n_local"], c["topk"],
+                        BF16, seed=c["seed"], zipf_s=c["zipf_s"])
+    e0, n = c["rank"] * c["n_local"], 8
+    chunks = inp["X"].reshape(n, c["T"] // n, c["hidden"])
+    step = int(chunks[0].size * 2 / 153e9 * 1e9)
+    off, sp, H, err = _moe_pull_run(inp, chunks, e0, c["n_local"], list(range(n)),
+                                    [a * step for a in range(n)])
+    assert err == 0
+    roff, rsp = oracle.moe_route(inp["topk_ids"], e0, c["n_local"])
+    rows = int(roff[-1])
+    assert np.array_equal(off, roff) and np.array_equal(sp[:rows], rsp)
+    rng = np.random.default_rng(11)
+    srows = np.unique(np.concatenate([rng.integers(0, rows, 48), roff[:-1], roff[1:] - 1]))
+    srows = srows[(srows >= 0) & (srows < rows)]
+    Hs = oracle.moe_layer0_rows(BF16, inp["X"], inp["W1"], rsp, roff, 2, srows)
+    idx = torch.from_numpy(srows).to("cuda:0")
+    assert_close(host64(H[idx]), Hs, "full moe ag pull rows")
+    H2 = torch.zeros_like(H)
+    sp2 = torch.full((c["T"] * 2,), -1, dtype=torch.int32, device="cuda:0")
+    off2 = torch.zeros(c["n_local"] + 1, dtype=torch.int32, device="cuda:0")
+    fm.fm_moe_gather_gemm(dev16(inp["X"], BF16), _i32(inp["topk_ids"]), dev16(inp["W1"], BF16),
+                          H2, sp2, off2, e0)
+    torch.cuda.synchronize()
+    assert torch.equal(H[:rows].view(torch.int16), H2[:rows].view(torch.int16))
+
+
 def test_moe_ag_withheld_chunk_times_out():
     """A token chunk that never arrives: the bounded wait writes
     FM_ERR_TIMEOUT to err_word and the kernel exits (no hang)."""

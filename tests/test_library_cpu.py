@@ -196,6 +196,24 @@ def test_moe_ag_producers_validation():
     assert call(order=_arr(ctypes.c_int32, [0, 0, 1, 2])) == fm.FM_ERR_INVALID_ARG
 
 
+def test_moe_ag_pull_validation():
+    L = fm.lib()
+    ch4 = _arr(ctypes.c_void_p, [0x50000, 0x60000, 0x70000, 0x80000])
+
+    def call(n=4, chunks=ch4, flags=P3, order=None):
+        return L.fm_moe_ag_gather_gemm_pull(1, 64, 64, 64, 2, 0, 8, chunks, P, P, P, P, P, n,
+                                            flags, 1, order, None, 0, None)
+    assert call(chunks=None) == fm.FM_ERR_INVALID_ARG
+    assert call(flags=None) == fm.FM_ERR_INVALID_ARG
+    assert call(n=3) == fm.FM_ERR_INVALID_ARG                          # T % n_chunks
+    assert call(n=0) == fm.FM_ERR_INVALID_ARG
+    assert call(chunks=_arr(ctypes.c_void_p, [0x50000, 0, 0x70000, 0x80000])) == \
+        fm.FM_ERR_INVALID_ARG                                          # a null chunk
+    assert call(chunks=_arr(ctypes.c_void_p, [0x50000, 0x60008, 0x70000, 0x80000])) == \
+        fm.FM_ERR_INVALID_ARG                                          # misaligned chunk
+    assert call(order=_arr(ctypes.c_int32, [1, 1, 2, 3])) == fm.FM_ERR_INVALID_ARG
+
+
 def test_chunk_signal_paced_validation():
     L = fm.lib()
     t = _arr(ctypes.c_int64, [0, 10, 20, 30])

@@ -23,7 +23,7 @@ FM_F16, FM_BF16, FM_F32 = 0, 1, 2
 EXPORTS = ("fm_version", "fm_status_str", "fm_gemm", "fm_ag_gemm", "fm_ag_gemm_pull", "fm_ag_gemm_producers",
            "fm_chunk_push", "fm_chunk_push_dma", "fm_chunk_signal_paced",
            "fm_gemm_rs", "fm_moe_route", "fm_moe_gather_gemm", "fm_moe_ag_gather_gemm",
-           "fm_moe_ag_gather_gemm_producers",
+           "fm_moe_ag_gather_gemm_producers", "fm_moe_ag_gather_gemm_pull",
            "fm_moe_gemm_scatter")
 
 
@@ -81,6 +81,9 @@ def lib() -> ctypes.CDLL:
     L.fm_moe_ag_gather_gemm_producers.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32, p,
                                                   p, p, p, p, p, i32, p, p, p, u32, p, i32, p,
                                                   i64, p]
+    L.fm_moe_ag_gather_gemm_pull.restype = ctypes.c_int
+    L.fm_moe_ag_gather_gemm_pull.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32, p, p, p,
+                                             p, p, p, i32, p, u32, p, p, i64, p]
     L.fm_moe_gemm_scatter.restype = ctypes.c_int
     L.fm_moe_gemm_scatter.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, p, p, p, p, p, p, p]
     _lib = L
@@ -328,6 +331,29 @@ def fm_moe_ag_gather_gemm_producers(src, X, topk_ids, W1, H, sorted_pairs, exper
         ctypes.c_uint32(epoch & 0xFFFFFFFF),
         ctypes.cast(o, ctypes.c_void_p) if o is not None else None, int(n_producers),
         _ptr(err_word), int(spin_limit), _stream(stream)))
+
+
+def fm_moe_ag_gather_gemm_pull(chunks, topk_ids, W1, H, sorted_pairs, expert_offsets,
+                               expert_begin: int, flags, epoch: int, order=None, err_word=None,
+                               spin_limit: int = 0, stream=None) -> None:
+    """MoE layer 0 reading token chunk c in place from chunks[c] after
+    flags[c] >= epoch (no gathered buffer)."""
+    n = len(chunks)
+    Tc, hidden = chunks[0].shape
+    T = n * Tc
+    n_local, h2, ffn = W1.shape
+    topk = topk_ids.shape[1]
+    if (h2 != hidden or H.shape[1] != ffn or H.shape[0] < T * topk or topk_ids.shape[0] != T
+            or any(tuple(x.shape) != (Tc, hidden) or x.dtype != W1.dtype for x in chunks)):
+        raise ValueError("fm_moe_ag_gather_gemm_pull: shape or dtype mismatch")
+    ptrs = (ctypes.c_void_p * n)(*[_ptr(x) for x in chunks])
+    o = _order_arg(order)
+    _check("fm_moe_ag_gather_gemm_pull", lib().fm_moe_ag_gather_gemm_pull(
+        _dt(W1), T, hidden, ffn, topk, int(expert_begin), n_local,
+        ctypes.cast(ptrs, ctypes.c_void_p), _ptr(topk_ids), _ptr(W1), _ptr(H), _ptr(sorted_pairs),
+        _ptr(expert_offsets), n, _ptr(flags), ctypes.c_uint32(epoch & 0xFFFFFFFF),
+        ctypes.cast(o, ctypes.c_void_p) if o is not None else None, _ptr(err_word),
+        int(spin_limit), _stream(stream)))
 
 
 def fm_moe_gemm_scatter(H, W2, sorted_pairs, expert_offsets, topk_weights, out,

@@ -157,6 +157,8 @@ struct MoeArgs {
   // Token chunks copied by the first prod.n_prod workgroups of layer 0's own
   // launch (prod.n_prod == 0: the chunks arrive from elsewhere).
   ProducerArgs prod;
+  // Pull mode (layer 0): token chunk c is read in place from pull_src[c].
+  const char* pull_src[64];
 };
 
 // Epochs of the combine's tile flags: one per call, process-wide, never 0
@@ -202,11 +204,13 @@ __device__ __forceinline__ void wait_token_range(const MoeArgs& a, const int* s_
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-template <class E, int BM, int BN, int NW, bool SCATTER, bool KTAIL>
+template <class E, int BM, int BN, int NW, bool SCATTER, bool KTAIL, bool PULL = false>
 __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   // One wave per SIMD has the register room for a two-sub-step read-ahead
-  // (not next to the combine's epilogue state).
-  using Eng = Engine<E, BM, BN, KTAIL, NW, 4, (NW == 4 && !SCATTER) ? 2 : 1>;
+  // (not next to the combine's epilogue state).  PULL: the token rows are
+  // gathered from the owners' chunk buffers, one 64-bit address per row.
+  static_assert(!(SCATTER && PULL), "pull mode is a layer-0 form");
+  using Eng = Engine<E, BM, BN, KTAIL, NW, 4, (NW == 4 && !SCATTER) ? 2 : 1, false, PULL>;
   __shared__ __attribute__((aligned(16))) char smem[Eng::LDS_BYTES];
   __shared__ int s_off[kMaxLocalExperts + 1];
   __shared__ int s_tile0[kMaxLocalExperts + 1];
@@ -391,7 +395,12 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       } else {
         src_row = a.sorted_pairs[row_base + lr] / a.topk;     // gather: token of the pair
       }
-      eng.set_a(i, (uint32_t)(src_row * K * 2));
+      if constexpr (PULL) {
+        const int c = (int)(src_row / a.chunk_tokens);       // the token's owner
+        eng.set_a64(i, a.pull_src[c] + (src_row - (int64_t)c * a.chunk_tokens) * K * 2);
+      } else {
+        eng.set_a(i, (uint32_t)(src_row * K * 2));
+      }
     }
     eng.set_b(a.W + (int64_t)e * K * N * 2, N * 2, n0, N);
     // Combine: fetch each tile row's pair id now, so that the load overlaps
@@ -536,7 +545,7 @@ int moe_ag_group() {
   return 2;
 }
 
-template <bool SCATTER>
+template <bool SCATTER, bool PULL = false>
 void launch_moe_part(fm_dtype_t dt, MoeTile cfg, const MoeArgs& a, hipStream_t stream);
 
 // Layer 0 splits a half-empty last wave into 256x128 halves (part 1, a second
@@ -565,25 +574,27 @@ fm_status_t launch_moe(fm_dtype_t dt, MoeTile cfg, MoeArgs& a, hipStream_t strea
     a.tile_done += kColDone0;
     a.epoch = next_combine_epoch();
   }
-  launch_moe_part<SCATTER>(dt, cfg, a, stream);
+  if (!SCATTER && a.pull_src[0]) launch_moe_part<false, true>(dt, cfg, a, stream);
+  else launch_moe_part<SCATTER>(dt, cfg, a, stream);
   if (a.split) {
     a.part = 1;
-    launch_moe_part<SCATTER>(dt, MoeTile{256, 128, 4}, a, stream);
+    if (!SCATTER && a.pull_src[0]) launch_moe_part<false, true>(dt, MoeTile{256, 128, 4}, a, stream);
+    else launch_moe_part<SCATTER>(dt, MoeTile{256, 128, 4}, a, stream);
   }
   return launch_status();
 }
 
-template <bool SCATTER>
+template <bool SCATTER, bool PULL>
 void launch_moe_part(fm_dtype_t dt, MoeTile cfg, const MoeArgs& a, hipStream_t stream) {
   const dim3 grid(device_cu_count());
-#define FM_LAUNCH(E, BM, BN, NW)                                                             \
-  do {                                                                                       \
-    if (a.K % kBK) /* ragged K: the 4-wave form keeps the tail path spill-free */            \
-      hipLaunchKernelGGL((moe_kernel<E, BM, BN, 4, SCATTER, true>), grid, dim3(256), 0,       \
-                         stream, a);                                                         \
-    else                                                                                     \
-      hipLaunchKernelGGL((moe_kernel<E, BM, BN, NW, SCATTER, false>), grid, dim3(64 * NW), 0, \
-                         stream, a);                                                         \
+#define FM_LAUNCH(E, BM, BN, NW)                                                              \
+  do {                                                                                        \
+    if (a.K % kBK) /* ragged K: the 4-wave form keeps the tail path spill-free */             \
+      hipLaunchKernelGGL((moe_kernel<E, BM, BN, 4, SCATTER, true, PULL>), grid, dim3(256), 0,  \
+                         stream, a);                                                          \
+    else                                                                                      \
+      hipLaunchKernelGGL((moe_kernel<E, BM, BN, NW, SCATTER, false, PULL>), grid,             \
+                         dim3(64 * NW), 0, stream, a);                                        \
   } while (0)
 #define FM_LAUNCH_E(E)                                                                       \
   do {                                                                                       \
@@ -645,14 +656,20 @@ fm_status_t moe_gather_impl(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ff
                             const uint32_t* flags, uint32_t epoch, const int32_t* order,
                             int32_t* err_word, int64_t spin_limit, hipStream_t stream,
                             const void* const* src = nullptr, uint32_t* counters = nullptr,
-                            int32_t n_producers = 0) {
+                            int32_t n_producers = 0, const void* const* pull = nullptr) {
   if (dt != FM_F16 && dt != FM_BF16) return FM_ERR_UNSUPPORTED;
   fm_status_t st = check_route_args(T, topk, n_local, topk_ids, sorted_pairs, expert_offsets);
   if (st != FM_OK) return st;
   if (hidden < 0 || ffn < 0 || hidden % 8 || ffn % 8) return FM_ERR_INVALID_ARG;
+  // pull mode reads the chunks in place: no gathered X
   if (T > 0 && ffn > 0 &&
-      (!X || !W1 || !H || !aligned16(X) || !aligned16(W1) || !aligned16(H)))
+      ((!pull && (!X || !aligned16(X))) || !W1 || !H || !aligned16(W1) || !aligned16(H)))
     return FM_ERR_INVALID_ARG;
+  if (pull) {
+    if (!flags || n_chunks < 1 || n_chunks > 64) return FM_ERR_INVALID_ARG;
+    for (int c = 0; c < n_chunks; ++c)
+      if (!pull[c] || !aligned16(pull[c])) return FM_ERR_INVALID_ARG;
+  }
   uint8_t pos[64] = {};
   if (flags) {
     if (n_chunks < 1 || n_chunks > 64 || T % n_chunks || spin_limit < 0 ||
@@ -707,6 +724,8 @@ fm_status_t moe_gather_impl(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ff
     a.chunk_spin = spin_limit ? spin_limit : (1ll << 24);
     std::memcpy(a.chunk_pos, pos, sizeof(pos));
   }
+  if (pull)
+    for (int c = 0; c < n_chunks; ++c) a.pull_src[c] = (const char*)pull[c];
   if (src) {
     const int P = n_producers ? n_producers : moe_producers_default(chunk_bytes * n_chunks);
     fill_producers(a.prod, P, n_chunks, chunk_bytes, src, order, const_cast<void*>(X),
@@ -755,6 +774,18 @@ extern "C" fm_status_t fm_moe_ag_gather_gemm_producers(
   return moe_gather_impl(dt, T, hidden, ffn, topk, expert_begin, n_local, X, topk_ids, W1, H,
                          sorted_pairs, expert_offsets, n_chunks, flags, epoch, order, err_word,
                          spin_limit, stream, src, counters, n_producers);
+}
+
+extern "C" fm_status_t fm_moe_ag_gather_gemm_pull(
+    fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn, int32_t topk, int32_t expert_begin,
+    int32_t n_local, const void* const* chunks, const int32_t* topk_ids, const void* W1, void* H,
+    int32_t* sorted_pairs, int32_t* expert_offsets, int32_t n_chunks, const uint32_t* flags,
+    uint32_t epoch, const int32_t* order, int32_t* err_word, int64_t spin_limit,
+    hipStream_t stream) {
+  if (!flags || !chunks) return FM_ERR_INVALID_ARG;
+  return moe_gather_impl(dt, T, hidden, ffn, topk, expert_begin, n_local, nullptr, topk_ids, W1,
+                         H, sorted_pairs, expert_offsets, n_chunks, flags, epoch, order,
+                         err_word, spin_limit, stream, nullptr, nullptr, 0, chunks);
 }
 
 extern "C" fm_status_t fm_moe_gemm_scatter(fm_dtype_t dt, int64_t T, int64_t hidden,

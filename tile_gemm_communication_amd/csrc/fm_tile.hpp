@@ -92,6 +92,14 @@ __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t
                : "v"(voff), "s"(sbase), "s"(lds)
                : "memory", "m0");
 }
+// The same from a per-lane 64-bit address (rows of one tile in different
+// buffers).
+__device__ __forceinline__ void dma16_64(const void* vaddr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(vaddr), "s"(lds)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1,
@@ -119,7 +127,7 @@ __device__ __forceinline__ void interleave() {
 }
 
 template <class E, int BM, int BN, bool KTAIL, int NW = 4, int BSWZ = 4, int DEPTH_ = 1,
-          bool MF16 = false>
+          bool MF16 = false, bool A64 = false>
 struct Engine {
   // Fragment read-ahead in sub-steps: 1 = the next sub-step (two register
   // slots), 2 = two sub-steps ahead (four slots, one per sub-step; needs the
@@ -169,7 +177,8 @@ struct Engine {
   // DMA sources: wave-uniform bases (K offset 0) plus per-lane 32-bit offsets.
   const char* a_base;
   const char* b_base;
-  uint32_t a_off[A_DMA];
+  uint32_t a_off[A64 ? 1 : A_DMA];
+  const char* a_ptr[A64 ? A_DMA : 1];   // A64: per-lane row addresses
   uint32_t b_off[B_DMA];
   int64_t b_step;             // bytes of 64 B rows (one K step)
 
@@ -266,6 +275,17 @@ struct Engine {
   __device__ __forceinline__ void set_a(int i, uint32_t row_off) {
     a_off[i] = row_off + a_dma_chunk(i) * 16;
   }
+  // A64: DMA instruction i of this wave fetches its row from `row` (the
+  // row's first element; any buffer).
+  __device__ __forceinline__ void set_a64(int i, const char* row) {
+    a_ptr[i] = row + a_dma_chunk(i) * 16;
+  }
+  __device__ __forceinline__ void dma_a(int i, int64_t ka, const char* sa, uint32_t lds) {
+    if constexpr (A64)
+      dma16_64(a_ptr[i] + ka * 2, lds);
+    else
+      dma16(a_off[i], sa, lds);
+  }
 
   __device__ __forceinline__ void zero_acc() {
 #pragma unroll
@@ -285,7 +305,7 @@ struct Engine {
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i) {
       if (!check || ka + 8 * a_dma_chunk(i) < K)
-        dma16(a_off[i], sa, la + i * 1024);
+        dma_a(i, ka, sa, la + i * 1024);
       else
         *reinterpret_cast<u32x4*>(smem + (la - lds0) + i * 1024 + lane * 16) = u32x4{0, 0, 0, 0};
     }
@@ -351,7 +371,7 @@ struct Engine {
   __device__ __forceinline__ void dma_item(int d, int kt, int buf) {
     if (d < A_DMA) {
       const uint32_t la = lds0 + buf * A_STAGE + (w * A_ROWS) * 128;
-      dma16(a_off[d], a_base + (int64_t)kt * kBK * 2, la + d * 1024);
+      dma_a(d, (int64_t)kt * kBK, a_base + (int64_t)kt * kBK * 2, la + d * 1024);
     } else {
       const int i = d - A_DMA;
       const uint32_t lb = lds0 + LDS_B + buf * B_STAGE + (w * B_DMA) * 1024;
