@@ -204,22 +204,30 @@ __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args)
         float* base = args.dst[s_lo] + (m0 - (int64_t)s_lo * Ms) * N + n0;
         // rows of block i, run q are valid while i*32 + q*EP_RPI < lim
         const int lim = col_ok ? (int)(m_end - m0) - eng.ep_row(0, 0) : 0;
+        // at most 8 slice loads in flight per lane (32 VGPRs): the 4-wave
+        // tile has 16 per block, which would crowd out the loop state
+        constexpr int QH = Eng::EP_READS > 8 ? 8 : Eng::EP_READS;
 #pragma unroll
         for (int i = 0; i < Eng::FM; ++i) {
           float* p0 = base + (uint32_t)(eng.ep_row(i, 0) * (int)N + col);
-          // the slice rows are requested first; the accumulators are staged
-          // while the loads fly
-          f32x4 old[Eng::EP_READS];
 #pragma unroll
-          for (int q = 0; q < Eng::EP_READS; ++q)
-            if (i * 32 + q * Eng::EP_RPI < lim)
-              old[q] = *reinterpret_cast<const f32x4*>(p0 + (uint32_t)(q * Eng::EP_RPI * (int)N));
-          eng.ep_stage(i);
+          for (int q0 = 0; q0 < Eng::EP_READS; q0 += QH) {
+            // the slice rows are requested first; the accumulators are
+            // staged while the first loads fly
+            f32x4 old[QH];
 #pragma unroll
-          for (int q = 0; q < Eng::EP_READS; ++q) {
-            const f32x4 v = eng.ep_read(q);
-            if (i * 32 + q * Eng::EP_RPI < lim)
-              *reinterpret_cast<f32x4*>(p0 + (uint32_t)(q * Eng::EP_RPI * (int)N)) = old[q] + v;
+            for (int q = q0; q < q0 + QH; ++q)
+              if (i * 32 + q * Eng::EP_RPI < lim)
+                old[q - q0] =
+                    *reinterpret_cast<const f32x4*>(p0 + (uint32_t)(q * Eng::EP_RPI * (int)N));
+            if (q0 == 0) eng.ep_stage(i);
+#pragma unroll
+            for (int q = q0; q < q0 + QH; ++q) {
+              const f32x4 v = eng.ep_read(q);
+              if (i * 32 + q * Eng::EP_RPI < lim)
+                *reinterpret_cast<f32x4*>(p0 + (uint32_t)(q * Eng::EP_RPI * (int)N)) =
+                    old[q - q0] + v;
+            }
           }
         }
       } else {
