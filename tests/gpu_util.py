@@ -74,6 +74,21 @@ def sample_coords(M: int, N: int, n: int, seed: int, tile=(256, 256)):
     return np.array(rows, dtype=np.int64), np.array(cols, dtype=np.int64)
 
 
+_SIDE = None
+
+
+def side_stream():
+    """The one side stream every test uses for arrivals.  HIP maps streams
+    onto a few hardware queues in turn; a test that created a stream per call
+    would after a while get one that shares the compute stream's queue, and
+    its producer would then run before, not beside, the consumer."""
+    global _SIDE
+    import torch
+    if _SIDE is None:
+        _SIDE = torch.cuda.Stream()
+    return _SIDE
+
+
 class Arrival:
     """Emulated AllGather arrival on one GPU: peer chunk buffers in HBM, a side
     stream that pushes chunks into the gathered buffer and publishes flags."""
@@ -89,7 +104,7 @@ class Arrival:
         self.flags = torch.zeros(self.n, dtype=torch.int32, device="cuda:0")
         self.counters = torch.zeros(self.n, dtype=torch.int32, device="cuda:0")
         self.err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
-        self.side = torch.cuda.Stream()
+        self.side = side_stream()
 
     def next_epoch(self) -> int:
         Arrival._epoch += 1

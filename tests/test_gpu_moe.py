@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import workloads as wl
-from gpu_util import BF16, F16, assert_close, bits16, dev16, devf32, host64, say
+from gpu_util import BF16, F16, assert_close, bits16, dev16, devf32, host64, say, side_stream
 
 pytestmark = pytest.mark.gpu
 
@@ -482,9 +482,10 @@ def test_full_moe_ag_producers_rank0(oracle):
     assert torch.equal(H3[:rows].view(torch.int16), H[:rows].view(torch.int16))
 
 
-def _moe_pull_run(inp, chunks, e0, nl, order, times_ns, dt=BF16, spin=0):
+def _moe_pull_run(inp, chunks, e0, nl, order, times_ns, dt=BF16, spin=0, signal=None):
     """fm_moe_ag_gather_gemm_pull with the chunk flags published by
-    fm_chunk_signal_paced on a side stream; returns (off, sp, H, err)."""
+    fm_chunk_signal_paced on a side stream (signal: the chunks published, in
+    that order; default `order`); returns (off, sp, H, err)."""
     import torch
     import tile_gemm_communication_amd as fm
     n, Tc, hidden = chunks.shape
@@ -497,10 +498,11 @@ def _moe_pull_run(inp, chunks, e0, nl, order, times_ns, dt=BF16, spin=0):
     off = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
     flags = torch.zeros(n, dtype=torch.int32, device="cuda:0")
     err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
-    side = torch.cuda.Stream()
+    side = side_stream()
     cs = torch.cuda.current_stream()
     side.wait_stream(cs)
-    fm.fm_chunk_signal_paced(flags, times_ns, 5, order=order, stream=side)
+    fm.fm_chunk_signal_paced(flags, times_ns, 5, order=order if signal is None else signal,
+                             stream=side)
     fm.fm_moe_ag_gather_gemm_pull(src, _i32(inp["topk_ids"]), dev16(inp["W1"], dt), H, sp, off,
                                   e0, flags, 5, order=order, err_word=err, spin_limit=spin)
     cs.wait_stream(side)
@@ -537,14 +539,14 @@ def test_moe_ag_pull(oracle, T, n, gap_us):
     assert torch.equal(H[:rows].view(torch.int16), H2[:rows].view(torch.int16))
 
 
-def test_moe_ag_pull_late_chunk_times_out():
-    """A chunk signalled long after the consumers' spin bound: FM_ERR_TIMEOUT."""
+def test_moe_ag_pull_withheld_chunk_times_out():
+    """Chunk 3 is never signalled: the bounded wait reports FM_ERR_TIMEOUT."""
     import tile_gemm_communication_amd as fm
     T, hidden, ffn, n = 512, 128, 64, 4
     inp = wl.moe_inputs(T, hidden, ffn, 8, 8, 2, BF16, seed=13)
     chunks = inp["X"].reshape(n, T // n, hidden)
-    _, _, _, err = _moe_pull_run(inp, chunks, 0, 8, [0, 1, 2, 3], [0, 0, 0, 200_000_000],
-                                 spin=2000)
+    _, _, _, err = _moe_pull_run(inp, chunks, 0, 8, [0, 1, 2, 3], [0, 0, 0], spin=2000,
+                                 signal=[0, 1, 2])
     assert err == fm.FM_ERR_TIMEOUT
 
 

@@ -5,7 +5,8 @@ import numpy as np
 import pytest
 
 import workloads as wl
-from gpu_util import F16, BF16, assert_close, bits16, dev16, host64, say, sample_coords
+from gpu_util import (F16, BF16, assert_close, bits16, dev16, host64, say, sample_coords,
+                      side_stream)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,7 +31,7 @@ class Pull:
         self.chunks = [dev16(chunks_bits[c], dt) for c in range(self.n)]
         self.flags = torch.zeros(self.n, dtype=torch.int32, device="cuda:0")
         self.err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
-        self.side = torch.cuda.Stream()
+        self.side = side_stream()
 
     def run(self, Wd, N, order, times_ns, hint=None, spin=0, events=None):
         import torch
@@ -117,14 +118,24 @@ def test_pull_waits_for_paced_signal():
     assert np.array_equal(bits16(C), bits16(_gemm_concat(chunks, Wd, F16)))
 
 
-def test_pull_late_signal_times_out():
-    """A chunk signalled far later than the consumer's spin bound: the bound
-    writes FM_ERR_TIMEOUT to err_word and the GEMM exits; the paced kernel
-    still ends at its last time."""
+def test_pull_withheld_signal_times_out():
+    """Chunk 3 is never signalled (the paced producer publishes chunks 0..2
+    only): the consumers' bounded wait writes FM_ERR_TIMEOUT to err_word and
+    the GEMM exits."""
+    import torch
     import tile_gemm_communication_amd as fm
     chunks, W, order = wl.ag_inputs(4, 128, 128, 128, F16, seed=78, arrival="ring")
     p = Pull(chunks, F16)
-    p.run(dev16(W, F16), 128, order, [0, 0, 0, 200_000_000], spin=2000)
+    Pull._epoch += 1
+    C = torch.empty((512, 128), dtype=torch.float16, device="cuda:0")
+    p.err.zero_()
+    cs = torch.cuda.current_stream()
+    p.side.wait_stream(cs)
+    fm.fm_chunk_signal_paced(p.flags, [0, 0, 0], Pull._epoch, order=[0, 1, 2], stream=p.side)
+    fm.fm_ag_gemm_pull(p.chunks, dev16(W, F16), C, p.flags, Pull._epoch, err_word=p.err,
+                       spin_limit=2000)
+    cs.wait_stream(p.side)
+    torch.cuda.synchronize()
     assert p.err.item() == fm.FM_ERR_TIMEOUT
 
 
