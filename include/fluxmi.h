@@ -96,7 +96,9 @@ fm_status_t fm_gemm(fm_dtype_t ab, fm_dtype_t c, int64_t M, int64_t N, int64_t K
  *   flags    device array of n_chunks uint32 ready flags.  A producer writes
  *            the chunk, then publishes flags[c] = epoch with release
  *            semantics.  Epochs grow from call to call so flags never need
- *            resetting; the caller zero-fills them once.
+ *            resetting; the caller zero-fills them once.  In a HIP graph,
+ *            whose replays repeat one epoch, zero the flags with a kernel
+ *            (not a memset node) at the start of the graph instead.
  *   order    host array of n_chunks chunk indices, the expected arrival order
  *            (e.g. the local chunk first), or NULL for index order.  It only
  *            orders the tiles; the result does not depend on it.
@@ -358,9 +360,11 @@ fm_status_t fm_moe_ag_gather_gemm_pull(
  * fp32 loads and stores (no atomics), so the result is deterministic.  The
  * ordering uses per-(row tile, column tile) completion flags in a per-device
  * buffer that the library allocates on the first call (128 KiB, kept until
- * the process ends; FM_ERR_HIP if that allocation fails), stamped with a
- * per-call epoch: calls of this function on one device must not overlap in
- * time (issue them on one stream, or order the streams).  Requires
+ * the process ends; FM_ERR_HIP if that allocation fails), stamped with an
+ * epoch that the kernel itself advances in that buffer, so the call may be
+ * captured in a HIP graph and replayed (make the first call outside the
+ * capture: it allocates).  Calls of this function on one device must not
+ * overlap in time (issue them on one stream, or order the streams).  Requires
  * (ceil(T*topk/256) + n_local) * ceil(hidden/256) <= 16384, else
  * FM_ERR_UNSUPPORTED.
  */

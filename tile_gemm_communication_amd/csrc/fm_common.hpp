@@ -58,17 +58,21 @@ struct BF16 {
 // Device properties cached once per device (compute-unit count).
 int device_cu_count();
 
-// Per-device tile counters for ordered epilogues: kTileCounters zeroed
-// uint32 words, allocated on first use and kept until the process ends.
-// Every launch that uses them leaves them at zero again.  NULL if the
-// allocation fails.
+// Per-device counter buffer of the MoE operators: kTileCounters uint32
+// words, zeroed when allocated on first use and kept until the process ends.
+// NULL if the allocation fails.
 constexpr int kTileCounters = 32768;
 uint32_t* device_tile_counters();
-// Layout of the counter buffer, one region per user so that different
-// operators may overlap in time (calls of one operator on one device may not):
-constexpr int kColDone0 = 0, kColDoneN = 16384;            // MoE combine, per N column
+// Layout, one region per user so that different operators may overlap in
+// time (calls of one operator on one device may not):
+constexpr int kColDone0 = 0, kColDoneN = 16384;            // combine tile flags (epochs)
 constexpr int kRoute0 = kColDoneN;                          // route chunk histograms
-constexpr int kRouteN = kTileCounters - kRoute0;
+constexpr int kRouteN = kTileCounters - kRoute0 - 2;
+// The combine's epoch lives on the device: each launch stamps its tile flags
+// with the stored epoch + 1, and its last workgroup to finish stores that
+// value back, so a launch replayed from a graph still gets a fresh epoch.
+constexpr int kCombineEpoch = kTileCounters - 2;
+constexpr int kCombineDone = kTileCounters - 1;             // finished workgroups
 
 // Translate the last HIP launch error into a status.
 inline fm_status_t launch_status() {

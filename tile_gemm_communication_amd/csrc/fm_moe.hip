@@ -134,7 +134,7 @@ struct MoeArgs {
   const int32_t* offsets;
   const float* weights;       // [T * topk] (layer 1)
   uint32_t* tile_done;        // layer 1: per (M-tile, N-tile) completion epoch
-  uint32_t epoch;             // this call's epoch (flags >= epoch: done in this call)
+  uint32_t* ctr;              // layer 1: the counter buffer (epoch and finish count)
   int64_t K, N;
   int64_t spin_limit;
   int topk, n_local, tiles_n, group_m;
@@ -161,14 +161,6 @@ struct MoeArgs {
   const char* pull_src[64];
 };
 
-// Epochs of the combine's tile flags: one per call, process-wide, never 0
-// (the flags start at 0).
-uint32_t next_combine_epoch() {
-  static std::atomic<uint32_t> epoch{0};
-  uint32_t e = epoch.fetch_add(1) + 1;
-  if (e == 0) e = epoch.fetch_add(1) + 1;
-  return e;
-}
 
 // Called by one thread: wait until every tile of an expert before e in
 // column tn whose token range overlaps that of global M-tile gm has published
@@ -176,7 +168,8 @@ uint32_t next_combine_epoch() {
 // cached and every earlier tile of the column is waited for.
 __device__ __forceinline__ void wait_token_range(const MoeArgs& a, const int* s_tile0,
                                                  const int* s_ftok, const int* s_ltok,
-                                                 int total_m, int e, int gm, int tn) {
+                                                 int total_m, int e, int gm, int tn,
+                                                 uint32_t epoch) {
   const bool cached = total_m <= kMaxMTiles;
   const int lo_tok = cached ? s_ftok[gm] : 0;
   const int hi_tok = cached ? s_ltok[gm] : 0x7FFFFFFF;
@@ -195,7 +188,7 @@ __device__ __forceinline__ void wait_token_range(const MoeArgs& a, const int* s_
       const uint32_t* f = a.tile_done + (int64_t)m * a.tiles_n + tn;
       int64_t polls = 0;
       while (!flag_reached(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                           a.epoch)) {
+                           epoch)) {
         __builtin_amdgcn_s_sleep(2);
         if (++polls > a.spin_limit) break;   // safeguard only: see the deadlock note
       }
@@ -240,6 +233,12 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   }
   const int t = threadIdx.x;
   const int gmb = SCATTER ? 1 : a.ag_group;
+  // Combine: this launch's epoch (never 0, the flags' initial value).
+  uint32_t epoch = 0;
+  if constexpr (SCATTER) {
+    epoch = __hip_atomic_load(a.ctr + kCombineEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+    if (epoch == 0) epoch = 1;
+  }
   if (t <= a.n_local) s_off[t] = a.offsets[t];
   __syncthreads();
   if (t == 0) {
@@ -431,7 +430,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       // its tokens in order, about one expert's worth of tiles earlier).
       const int gm = s_tile0[e] / a.tiles_n + tm;   // this tile's global M-tile
       if (e > 0 && t == 0)
-        wait_token_range(a, s_tile0, s_ftok, s_ltok, total_m, e, gm, tn);
+        wait_token_range(a, s_tile0, s_ftok, s_ltok, total_m, e, gm, tn, epoch);
       __syncthreads();
       const int col = eng.ep_col();
       const bool col_ok = n0 + col < N;
@@ -470,7 +469,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       wait_vmcnt<0>();   // this wave's write-through stores are complete
       __syncthreads();
       if (t == 0)
-        __hip_atomic_store(a.tile_done + (int64_t)gm * a.tiles_n + tn, a.epoch, __ATOMIC_RELAXED,
+        __hip_atomic_store(a.tile_done + (int64_t)gm * a.tiles_n + tn, epoch, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     } else {
       // H rows in expert-sorted order, 16-bit.
@@ -491,6 +490,20 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       }
     }
     eng.ep_end();
+  }
+  if constexpr (SCATTER) {
+    // Every workgroup checks in once its tiles are done; the last one resets
+    // the count and stores this launch's epoch for the next launch.
+    __syncthreads();
+    if (t == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(a.ctr + kCombineDone, 1u, __ATOMIC_ACQ_REL,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == (uint32_t)G - 1) {
+        __hip_atomic_store(a.ctr + kCombineDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.ctr + kCombineEpoch, epoch, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
 }
 
@@ -569,10 +582,9 @@ fm_status_t launch_moe(fm_dtype_t dt, MoeTile cfg, MoeArgs& a, hipStream_t strea
     // one completion flag per (M-tile, N-tile); M-tiles <= pairs/BM + experts
     const int64_t m_tiles = cdiv(a.rows_cap, (int64_t)cfg.bm) + a.n_local;
     if (m_tiles * a.tiles_n > kColDoneN) return FM_ERR_UNSUPPORTED;
-    a.tile_done = device_tile_counters();
-    if (!a.tile_done) return FM_ERR_HIP;
-    a.tile_done += kColDone0;
-    a.epoch = next_combine_epoch();
+    a.ctr = device_tile_counters();
+    if (!a.ctr) return FM_ERR_HIP;
+    a.tile_done = a.ctr + kColDone0;
   }
   if (!SCATTER && a.pull_src[0]) launch_moe_part<false, true>(dt, cfg, a, stream);
   else launch_moe_part<SCATTER>(dt, cfg, a, stream);
