@@ -147,3 +147,21 @@ def test_wrong_order_hint_is_still_correct():
     C = _ag(arr, Wd, 128, order, arr.next_epoch(), hint=list(reversed(order.tolist())))
     assert arr.err.item() == 0
     assert np.array_equal(bits16(C), _reference(arr, Wd, 128))
+
+
+def test_readme_example_runs():
+    """The Python example in README.md runs as written and its AllGather-GEMM
+    equals fm_gemm on the gathered buffer bit for bit."""
+    import os
+    import re
+    import torch
+    import tile_gemm_communication_amd as fm
+    text = open(os.path.join(os.path.dirname(__file__), "..", "README.md")).read()
+    code = re.search(r"```python\n(.*?)```", text, re.S).group(1)
+    ns = {}
+    exec(compile(code, "README.md", "exec"), ns)
+    torch.cuda.synchronize()
+    ref = torch.empty_like(ns["C"])
+    fm.fm_gemm(ns["X"], ns["W"], ref)
+    torch.cuda.synchronize()
+    assert torch.equal(ns["C"].view(torch.int16), ref.view(torch.int16))
