@@ -539,6 +539,33 @@ def test_moe_ag_pull(oracle, T, n, gap_us):
     assert torch.equal(H[:rows].view(torch.int16), H2[:rows].view(torch.int16))
 
 
+def test_moe_ag_pull_and_producers_fp16_nothing_local(oracle):
+    """fp16 through both forms, then a routing with no local pair: the pull
+    form reads nothing and the producer form still gathers X and publishes
+    every flag, with no tile to run."""
+    import torch
+    T, hidden, ffn, E, nl, e0, n = 1536, 192, 136, 32, 8, 8, 4
+    inp = wl.moe_inputs(T, hidden, ffn, E, nl, 2, F16, seed=31, zipf_s=1.2)
+    chunks = inp["X"].reshape(n, T // n, hidden)
+    order = [2, 0, 3, 1]
+    roff, rsp = oracle.moe_route(inp["topk_ids"], e0, nl)
+    rows = int(roff[-1])
+    ref = oracle.moe_ag_layer0(F16, list(chunks), inp["W1"], rsp, roff, 2, arrival=order)
+    off, sp, H, err = _moe_pull_run(inp, chunks, e0, nl, order, [0, 5000, 10000, 15000], dt=F16)
+    assert err == 0 and np.array_equal(off, roff) and np.array_equal(sp[:rows], rsp)
+    assert_close(host64(H[:rows]), ref, "moe ag pull fp16")
+    off2, sp2, H2, X2 = _moe_prod_run(inp, chunks, e0, nl, order, (0,), 8, dt=F16)
+    assert np.array_equal(off2, roff) and np.array_equal(bits16(X2), inp["X"])
+    assert torch.equal(H2[:rows].view(torch.int16), H[:rows].view(torch.int16))
+    # nothing local
+    inp["topk_ids"] = np.full((T, 2), 0, dtype=np.int32)
+    off, sp, H, err = _moe_pull_run(inp, chunks, e0, nl, order, [0, 0, 0, 0], dt=F16, spin=2000)
+    assert err == 0 and off.tolist() == [0] * (nl + 1)
+    assert torch.count_nonzero(H).item() == 0
+    off2, sp2, H2, X2 = _moe_prod_run(inp, chunks, e0, nl, order, (), 8, dt=F16)
+    assert off2.tolist() == [0] * (nl + 1) and np.array_equal(bits16(X2), inp["X"])
+
+
 def test_moe_ag_pull_withheld_chunk_times_out():
     """Chunk 3 is never signalled: the bounded wait reports FM_ERR_TIMEOUT."""
     import tile_gemm_communication_amd as fm
