@@ -46,12 +46,12 @@ PEAK_TFLOPS = 2516.6          # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 
 # known-size copy (`bench.py --copy-probe 256`) gives: FETCH_SIZE x2.0,
 # WRITE_SIZE x1.0.  Keyed by the digest of the kernel sources they were taken
 # on: after any change to csrc/ they no longer apply and traffic is null.
-TRAFFIC_DIGEST = "d7f4a48d73dcb0ba"
+TRAFFIC_DIGEST = "04108e868d72b3b0"
 TRAFFIC_BYTES = {             # op name -> (read bytes, written bytes) per call
-    "ag_gemm": (1134261568, 50328564),
-    "gemm_rs": (1126565219, 201314256),
-    "moe_gather_gemm": (1346045802, 172517205),
-    "moe_gemm_scatter": (1656618706, 501563379),
+    "ag_gemm": (1121621044, 50328564),
+    "gemm_rs": (1129782112, 201314256),
+    "moe_gather_gemm": (1352171413, 172517205),
+    "moe_gemm_scatter": (1656981728, 501571634),
 }
 
 
