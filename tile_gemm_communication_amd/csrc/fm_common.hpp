@@ -67,7 +67,11 @@ uint32_t* device_tile_counters();
 // time (calls of one operator on one device may not):
 constexpr int kColDone0 = 0, kColDoneN = 16384;            // combine tile flags (epochs)
 constexpr int kRoute0 = kColDoneN;                          // route chunk histograms
-constexpr int kRouteN = kTileCounters - kRoute0 - 2;
+// 1 KiB the combine's epilogue reads and writes in place of rows it does not
+// own (lanes past the last row or column), so that every wave issues the same
+// number of memory instructions per block.  Its contents are meaningless.
+constexpr int kEpSink0 = kTileCounters - 512;
+constexpr int kRouteN = kEpSink0 - kRoute0;
 // The combine's epoch lives on the device: each launch stamps its tile flags
 // with the stored epoch + 1, and its last workgroup to finish stores that
 // value back, so a launch replayed from a graph still gets a fresh epoch.

@@ -204,7 +204,10 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   // gathered from the owners' chunk buffers, one 64-bit address per row.
   static_assert(!(SCATTER && PULL), "pull mode is a layer-0 form");
   using Eng = Engine<E, BM, BN, KTAIL, NW, 4, (NW == 4 && !SCATTER) ? 2 : 1, false, PULL>;
-  __shared__ __attribute__((aligned(16))) char smem[Eng::LDS_BYTES];
+  // the combine's epilogue also keeps its destination rows in LDS
+  constexpr int kSmem =
+      (SCATTER && Eng::EP_RMW_LDS > Eng::LDS_BYTES) ? Eng::EP_RMW_LDS : Eng::LDS_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
   __shared__ int s_off[kMaxLocalExperts + 1];
   __shared__ int s_tile0[kMaxLocalExperts + 1];
   __shared__ int s_tok[SCATTER ? BM : 1];      // combine: token and gate weight per tile row
@@ -432,37 +435,84 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       if (e > 0 && t == 0)
         wait_token_range(a, s_tile0, s_ftok, s_ltok, total_m, e, gm, tn, epoch);
       __syncthreads();
+      // Per wave and 32-row block i: the destination rows come into LDS by
+      // DMA, the accumulators are staged, and weight * row is added and
+      // stored through.  Block i+1's rows are requested before block i's
+      // stores, so a store never delays the next loads (vmcnt counts loads
+      // and stores in issue order).  Each block goes in two halves of H
+      // reads, which bounds the registers the results hold.  Lanes past the
+      // last row or column read and write the sink instead, so every live
+      // block issues exactly H loads and H stores per half and the waits can
+      // count them; blocks past the last row (or a wave past the last
+      // column) issue nothing.  Issue order: D(i) h0, D(i) h1 [block 0 only],
+      // then per half h of block i: D(i+1) h, S(i) h.
+      constexpr int H = Eng::EP_READS / 2;
       const int col = eng.ep_col();
       const bool col_ok = n0 + col < N;
+      float* const sink = reinterpret_cast<float*>(a.ctr + kEpSink0) + 4 * (t & 63);
+      const int row_w = m0 + eng.ep_row0();
+      const int live = (n0 + eng.ep_col0() < N && row_w < rows_e)
+                           ? min(Eng::FM, (int)cdiv(rows_e - row_w, 32))
+                           : 0;
+      // destinations of half h of block i (the token reads go out together)
+      auto dests = [&](int i, int h, float* (&p)[H]) {
+        int tok[H];
+#pragma unroll
+        for (int u = 0; u < H; ++u) tok[u] = s_tok[eng.ep_row(i, h * H + u)];
+#pragma unroll
+        for (int u = 0; u < H; ++u)
+          p[u] = (tok[u] >= 0 && col_ok)
+                     ? reinterpret_cast<float*>(a.out) + (int64_t)tok[u] * N + n0 + col
+                     : sink;
+      };
+      if (live > 0) {
+        float* p0[H];
+        float* p1[H];
+        dests(0, 0, p0);
+        dests(0, 1, p1);
+#pragma unroll
+        for (int u = 0; u < H; ++u) eng.ep_fetch(u, p0[u]);
+#pragma unroll
+        for (int u = 0; u < H; ++u) eng.ep_fetch(H + u, p1[u]);
+      }
 #pragma unroll
       for (int i = 0; i < Eng::FM; ++i) {
-        float* dst[Eng::EP_READS];
-        float wt[Eng::EP_READS];
+        if (i < live) {
+          eng.ep_stage(i);
+          const bool next = i + 1 < live;
 #pragma unroll
-        for (int q = 0; q < Eng::EP_READS; ++q) {
-          const int r = eng.ep_row(i, q);
-          const int tok = s_tok[r];
-          wt[q] = s_wt[r];
-          dst[q] = (tok >= 0 && col_ok)
-                       ? reinterpret_cast<float*>(a.out) + (int64_t)tok * N + n0 + col
-                       : nullptr;
-        }
-        // out loads go first; the accumulators are staged while they fly
-        f32x4 old[Eng::EP_READS];
+          for (int h = 0; h < 2; ++h) {
+            // Wait for D(i) h.  Issued after it: block 0: D(0) h1 (h = 0);
+            // D(1) h0 if any, S(0) h0 (h = 1).  Block i > 0: S(i-1) h0,
+            // D(i) h1, S(i-1) h1 (h = 0); S(i-1) h1, D(i+1) h0 if any,
+            // S(i) h0 (h = 1).
+            if (i == 0 && h == 0) wait_vm_mem<H>();
+            else if (h == 0) wait_vm_mem<3 * H>();
+            else if (i == 0) { if (next) wait_vm_mem<2 * H>(); else wait_vm_mem<H>(); }
+            else { if (next) wait_vm_mem<3 * H>(); else wait_vm_mem<2 * H>(); }
+            f32x4 o[H];
 #pragma unroll
-        for (int q = 0; q < Eng::EP_READS; ++q)
-          if (dst[q]) old[q] = *reinterpret_cast<const f32x4*>(dst[q]);
-        eng.ep_stage(i);
+            for (int u = 0; u < H; ++u) {
+              const int q = h * H + u;
+              const f32x4 v = eng.ep_read(q);
+              const float wt = s_wt[eng.ep_row(i, q)];
+              o[u] = eng.ep_fetched(q);
+              o[u][0] += wt * v[0];
+              o[u][1] += wt * v[1];
+              o[u][2] += wt * v[2];
+              o[u][3] += wt * v[3];
+            }
+            float* pc[H];
+            float* pn[H];
+            dests(i, h, pc);
+            if (next) dests(i + 1, h, pn);
+            wait_lgkm_mem();   // these slots are read: block i+1 may land in them
+            if (next) {
 #pragma unroll
-        for (int q = 0; q < Eng::EP_READS; ++q) {
-          const f32x4 v = eng.ep_read(q);
-          if (dst[q]) {
-            f32x4 o = old[q];
-            o[0] += wt[q] * v[0];
-            o[1] += wt[q] * v[1];
-            o[2] += wt[q] * v[2];
-            o[3] += wt[q] * v[3];
-            store_through(dst[q], o);
+              for (int u = 0; u < H; ++u) eng.ep_fetch(h * H + u, pn[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < H; ++u) store_through(pc[u], o[u]);
           }
         }
       }

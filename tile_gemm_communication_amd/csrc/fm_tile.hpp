@@ -81,6 +81,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | 0x0F70 | ((N >> 4) << 14));
 }
 __device__ __forceinline__ void wait_all0() { __builtin_amdgcn_s_waitcnt(0x0070); }
+// The same waits as compiler memory barriers: LDS reads of DMA-written data
+// are not hoisted above wait_vm_mem, and a DMA into LDS the wave still reads
+// is not hoisted above wait_lgkm_mem.
+template <int N>
+__device__ __forceinline__ void wait_vm_mem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm_mem() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // One 16-byte-per-lane direct-to-LDS load: lane i's 16 bytes from
 // sbase + voff_i land at LDS byte lds + 16 i.  sbase and lds are wave-uniform.
@@ -576,6 +585,24 @@ struct Engine {
                                            (q * EP_RPI + lane / EP_LPR) * EP_STRIDE +
                                            16 * (lane % EP_LPR));
   }
+
+  // Read-modify-write epilogues: after the staging regions each wave owns
+  // EP_READS slots of 1 KiB.  ep_fetch(q, p) loads lane l's 16 bytes at p
+  // (the destination values of its ep_read(q)) into slot q by DMA, and once
+  // that has landed ep_fetched(q) returns them, so a block's destination rows
+  // can be in flight without holding registers.
+  static constexpr int EP_STAGE_BYTES = NW * 32 * EP_STRIDE;
+  static constexpr int EP_RMW_LDS = EP_STAGE_BYTES + NW * EP_READS * 1024;
+  __device__ __forceinline__ void ep_fetch(int q, const void* p) const {
+    dma16_64(p, lds0 + EP_STAGE_BYTES + (w * EP_READS + q) * 1024);
+  }
+  __device__ __forceinline__ f32x4 ep_fetched(int q) const {
+    return *reinterpret_cast<const f32x4*>(smem + EP_STAGE_BYTES + (w * EP_READS + q) * 1024 +
+                                           lane * 16);
+  }
+  // First tile row of this wave's epilogue blocks, and its first column.
+  __device__ __forceinline__ int ep_row0() const { return wm * WM; }
+  __device__ __forceinline__ int ep_col0() const { return wn * WN; }
 };
 
 }  // namespace fm
