@@ -340,6 +340,17 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   const int pos0 = a.part ? full : 0;
   const int n_items = a.part ? 2 * (total - full) : full;
 
+  // Combine: flag index of the last tile whose stores are not yet known to
+  // be complete (-1: none).  publish() is called by every thread after a
+  // wait for this wave's stores and a barrier.
+  int pending = -1;
+  auto publish = [&] {
+    if (pending >= 0 && t == 0)
+      __hip_atomic_store(a.tile_done + pending, epoch, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    pending = -1;
+  };
+
   for (int L2 = slot; L2 < n_items; L2 += G) {
     const int L = pos0 + L2 / sub_n, sub = L2 % sub_n;
     int e = 0, tm, tn;
@@ -411,7 +422,9 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
     if constexpr (SCATTER) {
       if (t < BM && m0 + t < rows_e) my_p = a.sorted_pairs[row_base + m0 + t];
     }
-    eng.run();
+    eng.run([&] {
+      if constexpr (SCATTER) publish();
+    });
 
     // Epilogue through the LDS staging regions (whole-line global accesses).
     eng.ep_begin();
@@ -516,11 +529,10 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
           }
         }
       }
-      wait_vmcnt<0>();   // this wave's write-through stores are complete
-      __syncthreads();
-      if (t == 0)
-        __hip_atomic_store(a.tile_done + (int64_t)gm * a.tiles_n + tn, epoch, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+      // The tile's flag goes out once every wave's stores have completed:
+      // at the next tile's first K-step wait (which drains them while that
+      // tile's first stage loads), or after the last tile.
+      pending = (int)(gm * a.tiles_n + tn);
     } else {
       // H rows in expert-sorted order, 16-bit.
       const int col = eng.ep_col();
@@ -542,6 +554,11 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
     eng.ep_end();
   }
   if constexpr (SCATTER) {
+    if (pending >= 0) {
+      wait_vmcnt<0>();   // this wave's write-through stores are complete
+      __syncthreads();
+      publish();
+    }
     // Every workgroup checks in once its tiles are done; the last one resets
     // the count and stores this launch's epoch for the next launch.
     __syncthreads();

@@ -487,9 +487,21 @@ struct Engine {
   // passed the last step's barrier, so no wave reads this tile's data any more
   // and the next tile may start its DMA right away.  KTAIL selects the
   // variant that masks a partial last K step (K % 64 != 0).
-  __device__ __forceinline__ void run() {
+  //
+  // after_first_wait() runs once every wave's memory operations issued before
+  // run() have completed (right after the first stage has landed, while the
+  // second may still be in flight): a caller can publish there what an
+  // earlier tile's stores completed.
+  __device__ __forceinline__ void run() { run([] {}); }
+  template <class F>
+  __device__ __forceinline__ void run(F&& after_first_wait) {
     zero_acc();
-    if (KT == 0) return;
+    if (KT == 0) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      after_first_wait();
+      return;
+    }
     dma(0, 0, KTAIL && KT == 1);
     if (KT > 1) dma(1, 1, KTAIL && KT == 2);
     if (KT > 1 && !(KTAIL && KT == 2))
@@ -497,6 +509,7 @@ struct Engine {
     else
       wait_vmcnt<0>();     // a masked stage issues fewer loads: wait for all
     __syncthreads();
+    after_first_wait();
     read_frags(0, 0, 0);
     if constexpr (DEPTH == 2) {
       read_frags(0, 1, 1);
