@@ -79,6 +79,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--ect-iters", type=int, default=20)
     ap.add_argument("--no-ect", action="store_true", help="skip the ECT comparisons")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the one-off cold-cache timing of each op")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of the AllGather-GEMM the CPU oracle computes as its sample")
@@ -265,6 +267,33 @@ def time_loop(fn, iters, warmup):
     torch.cuda.synchronize()
     ms = sorted(x.elapsed_time(y) for x, y in times)
     return ms[len(ms) // 2], ms[0]
+
+
+def cold_ops(w):
+    """Each op of the step once with cold caches: a 512 MiB scratch buffer is
+    written before each (more than the 256 MiB Infinity Cache plus the eight
+    4 MiB L2s).  The chunks have all landed before the AllGather-GEMM starts,
+    so it is timed without arrival."""
+    import torch
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cs = torch.cuda.current_stream()
+    w.epoch += 1
+    w.push_all(w.epoch)
+    w.join_sides()
+    ops = (("ag_gemm", lambda: w.ag(w.epoch)), ("gemm_rs", w.rs),
+           ("moe_gather_gemm", w.moe0), ("moe_gemm_scatter", w.moe1))
+    evs = []
+    for i, (_, fn) in enumerate(ops):
+        scratch.fill_(i + 1)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(cs)
+        fn()
+        b.record(cs)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    del scratch
+    return {n: round(a.elapsed_time(b), 4) for (n, _), (a, b) in zip(ops, evs)}
 
 
 def ect_block(w, iters):
@@ -558,13 +587,16 @@ def main():
     assert int(w.err.item()) == 0, "fm_ag_gemm reported a timeout"
     ms_step = (t1 - t0) * 1e3 / args.steps
     names = ["ag_gemm", "gemm_rs", "moe_gather_gemm", "moe_gemm_scatter"]
-    durs = {n: sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)) / args.steps
-            for i, n in enumerate(names)}
+    per_step = {n: sorted(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps))
+                for i, n in enumerate(names)}
+    durs = {n: sum(v) / len(v) for n, v in per_step.items()}
     flops = {"ag_gemm": w.flop_ag, "gemm_rs": w.flop_rs,
              "moe_gather_gemm": w.flop_moe / 2, "moe_gemm_scatter": w.flop_moe / 2}
     total_flop = sum(flops.values())
     value = total_flop / (ms_step * 1e-3) / 1e12
     ops = {n: {"ms": round(durs[n], 4),
+               "median_ms": round(per_step[n][len(per_step[n]) // 2], 4),
+               "min_ms": round(per_step[n][0], 4),
                "tflops": round(flops[n] / (durs[n] * 1e-3) / 1e12, 1),
                "frac_peak": round(flops[n] / (durs[n] * 1e-3) / 1e12 / PEAK_TFLOPS, 4)}
            for n in names}
@@ -600,6 +632,8 @@ def main():
                      "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_TFLOPS, 4), **traffic(dom)},
     }
+    if not args.no_cold:
+        out["cold_ms"] = cold_ops(w)
     if not args.no_ect:
         out["ect"] = ect_block(w, args.ect_iters)
     if not args.no_cpu_baseline:
