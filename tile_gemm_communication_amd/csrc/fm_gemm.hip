@@ -124,7 +124,12 @@ __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args)
   // One wave per SIMD has the register room for a two-sub-step read-ahead,
   // or for the 16x16x32 MFMA form.
   using Eng = Engine<E, BM, BN, KTAIL, NW, 4, NW == 4 ? 2 : 1, kMfma16 && NW == 4 && !KTAIL>;
-  __shared__ __attribute__((aligned(16))) char smem[Eng::LDS_BYTES];
+  // The ReduceScatter epilogue of full tiles keeps its destination rows in
+  // LDS (the one-wave-per-SIMD form: with two, its registers would spill).
+  constexpr bool kRsDma = MODE == Mode::RS && NW == 4;
+  constexpr int kSmem =
+      (kRsDma && Eng::EP_RMW_LDS > Eng::LDS_BYTES) ? Eng::EP_RMW_LDS : Eng::LDS_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
   __shared__ int s_abort;
 
   int wg = blockIdx.x, G = gridDim.x;
@@ -148,7 +153,10 @@ __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args)
     const int P = args.pos0 + L / args.sub_n, sub = L % args.sub_n;
     int tm_pos, tn;
     band_coords(P, args.order.tiles_m, args.order.tiles_n, args.order.group_m, tm_pos, tn);
-    const int tm = args.order.has_morder ? (int)args.order.morder[tm_pos] : tm_pos;
+    // uniform, but a table lookup is not always seen as such: the A base
+    // derived from it must sit in scalar registers for the DMA
+    const int tm = __builtin_amdgcn_readfirstlane(
+        args.order.has_morder ? (int)args.order.morder[tm_pos] : tm_pos);
     const int64_t n0 = ((int64_t)tn * args.sub_n + sub) * BN;
     int64_t m0, m_end;       // output rows of the tile
     const char* a_tile;      // its first A row
@@ -198,35 +206,83 @@ __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args)
       // Add the fp32 partial into the owning rank's row slice.
       const int64_t Ms = args.slice_rows;
       const int s_lo = (int)(m0 / Ms), s_hi = (int)((m_end - 1) / Ms);
+      float* const base = args.dst[s_lo] + (m0 - (int64_t)s_lo * Ms) * N + n0;
+      // Element offset of this lane's first value; the empty asm makes it
+      // opaque per tile, so that the addresses derived from it are formed
+      // here rather than hoisted out of the tile loop, where they would stay
+      // live through the K loop.
+      int lane_off = eng.ep_row(0, 0) * (int)N + col;
+      asm volatile("" : "+v"(lane_off));
       if constexpr (MODE == Mode::RS) {
-        // Common case: the tile lies in one slice.  Uniform base, 32-bit lane
-        // offsets (row < BM, N < 2^22), all loads of a block in flight first.
-        float* base = args.dst[s_lo] + (m0 - (int64_t)s_lo * Ms) * N + n0;
-        // rows of block i, run q are valid while i*32 + q*EP_RPI < lim
-        const int lim = col_ok ? (int)(m_end - m0) - eng.ep_row(0, 0) : 0;
-        // at most 8 slice loads in flight per lane (32 VGPRs): the 4-wave
-        // tile has 16 per block, which would crowd out the loop state
-        constexpr int QH = Eng::EP_READS > 8 ? 8 : Eng::EP_READS;
+        if (kRsDma && m_end - m0 == BM && n0 + BN <= N) {
+          // A full tile in one slice: the slice rows come into LDS by DMA,
+          // block i+1's before block i's stores (vmcnt counts loads and stores
+          // in issue order, so loads issued after a store would wait for it),
+          // each block in two halves of H reads.  Every lane is valid, so each
+          // half issues exactly H loads and H stores and the waits count them.
+          // Issue order: D(0) h0, D(0) h1, then per half h of block i:
+          // D(i+1) h, S(i) h.
+          constexpr int H = Eng::EP_READS / 2;
+          auto at = [&](int i, int q) {
+            return base + (uint32_t)(lane_off + (32 * i + q * Eng::EP_RPI) * (int)N);
+          };
 #pragma unroll
-        for (int i = 0; i < Eng::FM; ++i) {
-          float* p0 = base + (uint32_t)(eng.ep_row(i, 0) * (int)N + col);
+          for (int q = 0; q < Eng::EP_READS; ++q) eng.ep_fetch(q, at(0, q));
 #pragma unroll
-          for (int q0 = 0; q0 < Eng::EP_READS; q0 += QH) {
-            // the slice rows are requested first; the accumulators are
-            // staged while the first loads fly
-            f32x4 old[QH];
+          for (int i = 0; i < Eng::FM; ++i) {
+            eng.ep_stage(i);
+            const bool next = i + 1 < Eng::FM;
 #pragma unroll
-            for (int q = q0; q < q0 + QH; ++q)
-              if (i * 32 + q * Eng::EP_RPI < lim)
-                old[q - q0] =
-                    *reinterpret_cast<const f32x4*>(p0 + (uint32_t)(q * Eng::EP_RPI * (int)N));
-            if (q0 == 0) eng.ep_stage(i);
+            for (int h = 0; h < 2; ++h) {
+              // Wait for D(i) h.  Issued after it: block 0: D(0) h1 (h = 0);
+              // D(1) h0, S(0) h0 (h = 1).  Block i > 0: S(i-1) h0, D(i) h1,
+              // S(i-1) h1 (h = 0); S(i-1) h1, D(i+1) h0 if any, S(i) h0 (h = 1).
+              if (i == 0 && h == 0) wait_vm_mem<H>();
+              else if (h == 0) wait_vm_mem<3 * H>();
+              else if (i == 0) { if (next) wait_vm_mem<2 * H>(); else wait_vm_mem<H>(); }
+              else { if (next) wait_vm_mem<3 * H>(); else wait_vm_mem<2 * H>(); }
+              f32x4 o[H];
 #pragma unroll
-            for (int q = q0; q < q0 + QH; ++q) {
-              const f32x4 v = eng.ep_read(q);
-              if (i * 32 + q * Eng::EP_RPI < lim)
-                *reinterpret_cast<f32x4*>(p0 + (uint32_t)(q * Eng::EP_RPI * (int)N)) =
-                    old[q - q0] + v;
+              for (int u = 0; u < H; ++u) o[u] = eng.ep_fetched(h * H + u) + eng.ep_read(h * H + u);
+              wait_lgkm_mem();   // these slots are read: block i+1 may land in them
+              if (next) {
+#pragma unroll
+                for (int u = 0; u < H; ++u) eng.ep_fetch(h * H + u, at(i + 1, h * H + u));
+              }
+#pragma unroll
+              for (int u = 0; u < H; ++u)
+                *reinterpret_cast<f32x4*>(at(i, h * H + u)) = o[u];
+            }
+          }
+        } else {
+          // An edge tile in one slice.  Uniform base, 32-bit lane offsets
+          // (row < BM, N < 2^22), the loads of half a block in flight first.
+          // rows of block i, run q are valid while i*32 + q*EP_RPI < lim
+          const int lim = col_ok ? (int)(m_end - m0) - eng.ep_row(0, 0) : 0;
+          // at most 8 slice loads in flight per lane (32 VGPRs): the 4-wave
+          // tile has 16 per block, which would crowd out the loop state
+          constexpr int QH = Eng::EP_READS > 8 ? 8 : Eng::EP_READS;
+#pragma unroll
+          for (int i = 0; i < Eng::FM; ++i) {
+            float* p0 = base + (uint32_t)(eng.ep_row(i, 0) * (int)N + col);
+#pragma unroll
+            for (int q0 = 0; q0 < Eng::EP_READS; q0 += QH) {
+              // the slice rows are requested first; the accumulators are
+              // staged while the first loads fly
+              f32x4 old[QH];
+#pragma unroll
+              for (int q = q0; q < q0 + QH; ++q)
+                if (i * 32 + q * Eng::EP_RPI < lim)
+                  old[q - q0] =
+                      *reinterpret_cast<const f32x4*>(p0 + (uint32_t)(q * Eng::EP_RPI * (int)N));
+              if (q0 == 0) eng.ep_stage(i);
+#pragma unroll
+              for (int q = q0; q < q0 + QH; ++q) {
+                const f32x4 v = eng.ep_read(q);
+                if (i * 32 + q * Eng::EP_RPI < lim)
+                  *reinterpret_cast<f32x4*>(p0 + (uint32_t)(q * Eng::EP_RPI * (int)N)) =
+                      old[q - q0] + v;
+              }
             }
           }
         }
