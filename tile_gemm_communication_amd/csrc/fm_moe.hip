@@ -199,11 +199,11 @@ __device__ __forceinline__ void wait_token_range(const MoeArgs& a, const int* s_
 
 template <class E, int BM, int BN, int NW, bool SCATTER, bool KTAIL, bool PULL = false>
 __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
-  // One wave per SIMD has the register room for a two-sub-step read-ahead
-  // (not next to the combine's epilogue state).  PULL: the token rows are
-  // gathered from the owners' chunk buffers, one 64-bit address per row.
+  // One wave per SIMD has the register room for a two-sub-step read-ahead.
+  // PULL: the token rows are gathered from the owners' chunk buffers, one
+  // 64-bit address per row.
   static_assert(!(SCATTER && PULL), "pull mode is a layer-0 form");
-  using Eng = Engine<E, BM, BN, KTAIL, NW, 4, (NW == 4 && !SCATTER) ? 2 : 1, false, PULL>;
+  using Eng = Engine<E, BM, BN, KTAIL, NW, 4, NW == 4 ? 2 : 1, false, PULL>;
   // the combine's epilogue also keeps its destination rows in LDS
   constexpr int kSmem =
       (SCATTER && Eng::EP_RMW_LDS > Eng::LDS_BYTES) ? Eng::EP_RMW_LDS : Eng::LDS_BYTES;
@@ -580,12 +580,12 @@ struct MoeTile {
   int bm, bn, nw;
 };
 
-// 256x256 tiles with two waves per SIMD: measured on N(0,1) data, 2% faster
-// than one wave per SIMD for layer 0, and 10% for the combine, whose
-// read-modify-write epilogue the second wave hides.
+// 256x256 tiles.  Layer 0 runs two waves per SIMD: on N(0,1) data 2% faster
+// than one (0.649 vs 0.660 ms at EP=8).  The combine runs one wave per SIMD
+// with the two-sub-step fragment read-ahead, which its DMA-fed epilogue
+// leaves the registers for: 0.769 vs 0.775 ms.
 MoeTile moe_tile(bool scatter) {
-  const int nw_default = 8;
-  (void)scatter;
+  const int nw_default = scatter ? 4 : 8;
   if (const char* env = std::getenv("FM_MOE_TILE")) {
     int bm = 0, bn = 0, nw = 0;
     const int got = std::sscanf(env, "%dx%dw%d", &bm, &bn, &nw);
