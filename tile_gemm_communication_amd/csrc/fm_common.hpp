@@ -77,6 +77,9 @@ constexpr int kRouteN = kEpSink0 - kRoute0;
 // value back, so a launch replayed from a graph still gets a fresh epoch.
 constexpr int kCombineEpoch = kTileCounters - 2;
 constexpr int kCombineDone = kTileCounters - 1;             // finished workgroups
+static_assert(kRoute0 + kRouteN <= kEpSink0 && kEpSink0 + 256 <= kCombineEpoch &&
+                  (kEpSink0 * 4) % 16 == 0,
+              "counter regions overlap, or the sink is not 16-byte aligned");
 
 // Translate the last HIP launch error into a status.
 inline fm_status_t launch_status() {
