@@ -46,12 +46,12 @@ PEAK_TFLOPS = 2516.6          # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 
 # known-size copy (`bench.py --copy-probe 256`) gives: FETCH_SIZE x2.0,
 # WRITE_SIZE x1.0.  Keyed by the digest of the kernel sources they were taken
 # on: after any change to csrc/ they no longer apply and traffic is null.
-TRAFFIC_DIGEST = "cbee61f0302c4f23"
+TRAFFIC_DIGEST = "3c178ea609dcd4b3"
 TRAFFIC_BYTES = {             # op name -> (read bytes, written bytes) per call
-    "ag_gemm": (1113940410, 50328564),
-    "gemm_rs": (1111577112, 201314256),
-    "moe_gather_gemm": (1381487512, 172517205),
-    "moe_gemm_scatter": (1653856636, 504405893),
+    "ag_gemm": (1120582619, 50328564),
+    "gemm_rs": (1137977791, 201314256),
+    "moe_gather_gemm": (1342691779, 172517205),
+    "moe_gemm_scatter": (1660018948, 504405893),
 }
 
 
