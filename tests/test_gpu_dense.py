@@ -188,6 +188,22 @@ def test_rs_slices_vs_tiles(oracle, M, P, rank):
         assert_close(got[r] - seeds[r], ref[r] - seeds[r], f"rs slice {r}")
 
 
+@pytest.mark.parametrize("dt", [F16, BF16])
+@pytest.mark.parametrize("M,N,K,P", [(1024, 512, 256, 2), (768, 520, 200, 3)])
+def test_rs_full_tiles(oracle, monkeypatch, dt, M, N, K, P):
+    """Slices a multiple of the tile height: full 256x256 tiles take the
+    epilogue that fetches the slice rows by DMA, the column-edge tile of
+    N = 520 the register form; K = 200 runs the K-tail kernel."""
+    monkeypatch.setenv("FM_TILE", "256x256")
+    monkeypatch.setenv("FM_SPLIT_TAIL", "0")
+    say(f"fm_gemm_rs full tiles {M}x{N}x{K} P={P} dt={dt}")
+    A, W, seeds = wl.rs_inputs(M, N, K, P, dt, seed=M + N + K)
+    got = _rs(A, W, seeds, dt, rank=P - 1)
+    ref = oracle.gemm_rs(dt, A, W, list(seeds))
+    for r in range(P):
+        assert_close(got[r] - seeds[r], ref[r] - seeds[r], f"rs slice {r}")
+
+
 def test_rs_split_k_emulated_ranks(oracle):
     """P sequential calls with contiguous K shards (the other ranks' partials)
     accumulate into the same slices: seed + the full GEMM."""
