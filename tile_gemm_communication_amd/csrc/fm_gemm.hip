@@ -215,10 +215,11 @@ __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args)
       asm volatile("" : "+v"(lane_off));
       if constexpr (MODE == Mode::RS) {
         if (kRsDma && m_end - m0 == BM && n0 + BN <= N) {
-          // A full tile in one slice: the slice rows come into LDS by DMA,
-          // block i+1's before block i's stores (vmcnt counts loads and stores
-          // in issue order, so loads issued after a store would wait for it),
-          // each block in two halves of H reads.  Every lane is valid, so each
+          // A full tile in one slice: the slice rows come into LDS by DMA
+          // (non-temporal: each is read once), block i+1's before block
+          // i's stores (vmcnt counts loads and stores in issue order, so
+          // loads issued after a store would wait for it), each block in
+          // two halves of H reads.  Every lane is valid, so each
           // half issues exactly H loads and H stores and the waits count them.
           // Issue order: D(0) h0, D(0) h1, then per half h of block i:
           // D(i+1) h, S(i) h.
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args)
             return base + (uint32_t)(lane_off + (32 * i + q * Eng::EP_RPI) * (int)N);
           };
 #pragma unroll
-          for (int q = 0; q < Eng::EP_READS; ++q) eng.ep_fetch(q, at(0, q));
+          for (int q = 0; q < Eng::EP_READS; ++q) eng.ep_fetch_once(q, at(0, q));
 #pragma unroll
           for (int i = 0; i < Eng::FM; ++i) {
             eng.ep_stage(i);
@@ -243,15 +244,16 @@ __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args)
               else { if (next) wait_vm_mem<3 * H>(); else wait_vm_mem<2 * H>(); }
               f32x4 o[H];
 #pragma unroll
-              for (int u = 0; u < H; ++u) o[u] = eng.ep_fetched(h * H + u) + eng.ep_read(h * H + u);
+              for (int u = 0; u < H; ++u)
+                o[u] = eng.ep_fetched(h * H + u) + eng.ep_read(h * H + u);
               wait_lgkm_mem();   // these slots are read: block i+1 may land in them
               if (next) {
 #pragma unroll
-                for (int u = 0; u < H; ++u) eng.ep_fetch(h * H + u, at(i + 1, h * H + u));
+                for (int u = 0; u < H; ++u) eng.ep_fetch_once(h * H + u, at(i + 1, h * H + u));
               }
 #pragma unroll
               for (int u = 0; u < H; ++u)
-                *reinterpret_cast<f32x4*>(at(i, h * H + u)) = o[u];
+                __builtin_nontemporal_store(o[u], reinterpret_cast<f32x4*>(at(i, h * H + u)));
             }
           }
         } else {

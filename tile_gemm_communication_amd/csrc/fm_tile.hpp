@@ -109,6 +109,14 @@ __device__ __forceinline__ void dma16_64(const void* vaddr, uint32_t lds) {
                : "v"(vaddr), "s"(lds)
                : "memory", "m0");
 }
+// The same with the non-temporal hint (data read once: kept out of the way
+// of operands that are reused).
+__device__ __forceinline__ void dma16_64_nt(const void* vaddr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(vaddr), "s"(lds)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1,
@@ -608,6 +616,10 @@ struct Engine {
   static constexpr int EP_RMW_LDS = EP_STAGE_BYTES + NW * EP_READS * 1024;
   __device__ __forceinline__ void ep_fetch(int q, const void* p) const {
     dma16_64(p, lds0 + EP_STAGE_BYTES + (w * EP_READS + q) * 1024);
+  }
+  // The same as a non-temporal load: for destination rows read only once.
+  __device__ __forceinline__ void ep_fetch_once(int q, const void* p) const {
+    dma16_64_nt(p, lds0 + EP_STAGE_BYTES + (w * EP_READS + q) * 1024);
   }
   __device__ __forceinline__ f32x4 ep_fetched(int q) const {
     return *reinterpret_cast<const f32x4*>(smem + EP_STAGE_BYTES + (w * EP_READS + q) * 1024 +
