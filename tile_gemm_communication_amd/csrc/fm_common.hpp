@@ -55,6 +55,21 @@ struct BF16 {
 };
 
 
+// Store 16 bytes written through every cache level (system-scope store):
+// once the wave's vmcnt drains, the data is visible device-wide without an
+// L2 write-back.  Used for data handed to a reader that may run on another
+// XCD (each XCD has its own, non-coherent L2): the reader learns of it from a
+// flag or count published after that drain, and acquires at agent scope.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void store_through(void* p, const u32x4& v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store_through(float* p, const f32x4& v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" ::"v"(p), "v"(v) : "memory");
+}
+#pragma clang diagnostic pop
+
 // Device properties cached once per device (compute-unit count).
 int device_cu_count();
 

@@ -1,9 +1,9 @@
 // fm_push.hip -- producer side of the chunk-arrival protocol.
 //
-// A chunk is copied with coalesced 16-byte loads/stores by a small grid; every
-// workgroup makes its stores visible at device scope and checks in on a
-// counter; the last one to check in resets the counter and publishes the
-// chunk's flag with a release store.  This is the signalled one-sided put of
+// A chunk is copied with coalesced 16-byte loads and write-through stores by a
+// small grid; every workgroup waits until its stores have reached memory
+// (visible to every XCD) and checks in on a counter; the last one to check in
+// resets the counter and publishes the chunk's flag.  This is the signalled one-sided put of
 // the FlagCX guide ("flagcxPutSignal": write the data, then bump the remote
 // signal) and the push mode of the FLUX review ("拉取 vs 推送数据传输"), with
 // the peer's buffer being local HBM on one GPU.
@@ -24,23 +24,24 @@ __global__ __launch_bounds__(256) void push_kernel(const u32x4* __restrict__ src
   int64_t i = begin + threadIdx.x;
   for (; i + 3 * 256 < end; i += 4 * 256) {
     const u32x4 a = src[i], b = src[i + 256], c = src[i + 512], d = src[i + 768];
-    dst[i] = a;
-    dst[i + 256] = b;
-    dst[i + 512] = c;
-    dst[i + 768] = d;
+    store_through(dst + i, a);
+    store_through(dst + i + 256, b);
+    store_through(dst + i + 512, c);
+    store_through(dst + i + 768, d);
   }
-  for (; i < end; i += 256) dst[i] = src[i];
-  // Every wave waits until its stores are acknowledged by L2; after the
-  // barrier one release (a single L2 write-back per workgroup rather than one
-  // per thread) makes the workgroup's stores visible device-wide.
+  for (; i < end; i += 256) store_through(dst + i, src[i]);
+  // Every wave waits until its write-through stores have completed; after the
+  // barrier the workgroup's part of the chunk is in memory, so the count and
+  // the flag need no release (which would write back this XCD's whole L2,
+  // once per workgroup, under the GEMM that runs beside the copy).
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t prev =
-        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (prev == gridDim.x - 1) {
       __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(flag, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

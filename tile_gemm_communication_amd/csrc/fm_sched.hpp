@@ -92,8 +92,9 @@ struct ProducerArgs {
 };
 
 // Producer workgroup p of P: for each chunk in arrival order, copy its p-th
-// share into X, then check in on the chunk's counter; the last of the P
-// workgroups resets the counter and publishes the chunk's flag (release).
+// share into X with write-through stores, wait until they have completed,
+// then check in on the chunk's counter; the last of the P workgroups resets
+// the counter and publishes the chunk's flag.
 // All producers work on the same chunk at a time, so chunks complete in
 // arrival order.  Chunks without a source are published by workgroup 0.
 template <int NT>
@@ -114,20 +115,21 @@ __device__ __forceinline__ void produce_chunks(const ProducerArgs& pa) {
     int64_t i = b0 + t;
     for (; i + 3 * NT < b1; i += 4 * NT) {
       const u32x4 x0 = src[i], x1 = src[i + NT], x2 = src[i + 2 * NT], x3 = src[i + 3 * NT];
-      dst[i] = x0;
-      dst[i + NT] = x1;
-      dst[i + 2 * NT] = x2;
-      dst[i + 3 * NT] = x3;
+      store_through(dst + i, x0);
+      store_through(dst + i + NT, x1);
+      store_through(dst + i + 2 * NT, x2);
+      store_through(dst + i + 3 * NT, x3);
     }
-    for (; i < b1; i += NT) dst[i] = src[i];
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are done
+    for (; i < b1; i += NT) store_through(dst + i, src[i]);
+    // this wave's write-through stores are in memory: no release needed
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
     if (t == 0) {
       const uint32_t prev =
-          __hip_atomic_fetch_add(pa.counters + c, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_add(pa.counters + c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (prev == (uint32_t)P - 1) {
         __hip_atomic_store(pa.counters + c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(pa.flags + c, pa.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(pa.flags + c, pa.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -148,12 +150,5 @@ inline void fill_producers(ProducerArgs& pa, int P, int n_chunks, int64_t chunk_
   for (int a = 0; a < n_chunks; ++a) pa.order[a] = (uint8_t)(order ? order[a] : a);
 }
 
-// Store 16 bytes written through every cache level (system-scope store):
-// once the wave's vmcnt drains, the data is visible device-wide without an
-// L2 write-back.  Used for data that a counted tile hands to a tile that may
-// run on another XCD (each XCD has its own, non-coherent L2).
-__device__ __forceinline__ void store_through(float* p, const f32x4& v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" ::"v"(p), "v"(v) : "memory");
-}
 
 }  // namespace fm
