@@ -560,10 +560,12 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       publish();
     }
     // Every workgroup checks in once its tiles are done; the last one resets
-    // the count and stores this launch's epoch for the next launch.
+    // the count and stores this launch's epoch for the next launch.  Relaxed:
+    // only the next launch reads these words, after the kernel boundary (a
+    // release here would write back this XCD's L2 once per workgroup).
     __syncthreads();
     if (t == 0) {
-      const uint32_t prev = __hip_atomic_fetch_add(a.ctr + kCombineDone, 1u, __ATOMIC_ACQ_REL,
+      const uint32_t prev = __hip_atomic_fetch_add(a.ctr + kCombineDone, 1u, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
       if (prev == (uint32_t)G - 1) {
         __hip_atomic_store(a.ctr + kCombineDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
