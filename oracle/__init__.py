@@ -69,6 +69,7 @@ class Oracle:
         L.or_round_to_bf16.argtypes = [_i64, _p, _p]
         L.or_round_to_f16.argtypes = [_i64, _p, _p]
         L.or_gemm.argtypes = [ctypes.c_int, _i64, _i64, _i64, _p, _p, _p]
+        L.or_activation.argtypes = [ctypes.c_int, _i64, _p]
         L.or_gemm_entries.argtypes = [ctypes.c_int, _i64, _i64, _i64, _p, _p, _i64, _p, _p, _p]
         L.or_ag_gemm.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _p, _p, _p, _p]
         L.or_gemm_rs.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _p, _p, _p, _p]
@@ -189,6 +190,12 @@ class Oracle:
         self._L.or_moe_layer0(dt, T, hidden, ffn, topk, n_local, X.ctypes.data, W1.ctypes.data,
                               sp.ctypes.data, off.ctypes.data, H.ctypes.data)
         return H
+
+    def activation(self, act: int, x: np.ndarray) -> np.ndarray:
+        """O5a: act (0 none, 1 ReLU, 2 tanh-form GELU, 3 SiLU) of x, in fp64."""
+        y = np.array(x, dtype=np.float64, order="C", copy=True)
+        self._L.or_activation(int(act), y.size, y.ctypes.data)
+        return y
 
     def moe_ag_layer0(self, dt, chunks, W1, sorted_pairs, offsets, topk, arrival=None):
         """Layer 0 on the token chunks gathered in `arrival` order (by index)."""

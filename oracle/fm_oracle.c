@@ -309,6 +309,33 @@ void or_moe_layer0(int dt, int64_t T, int64_t hidden, int64_t ffn, int64_t topk,
 }
 
 /* ------------------------------------------------------------------------- */
+/* O5a Activation applied to layer 0's output before it is stored (Flux       */
+/* README: MoE MLP layer 0 is the first GEMM of the expert MLP; the FLUX      */
+/* review's MLP forward pass feeds GEMM 1's output to GEMM 2 as is, which is  */
+/* act = 0).  In place, elementwise, in fp64:                                 */
+/*   1 ReLU        max(x, 0)                                                  */
+/*   2 GELU, tanh  x/2 * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3)))          */
+/*   3 SiLU        x * sigmoid(x) = x / (1 + exp(-x))                         */
+/* ------------------------------------------------------------------------- */
+
+void or_activation(int act, int64_t n, double* x) {
+    const double c = sqrt(2.0 / 3.14159265358979323846);
+    for (int64_t i = 0; i < n; ++i) {
+        double v = x[i];
+        if (act == 1) {
+            v = v > 0.0 ? v : 0.0;
+        } else if (act == 2) {
+            double half = MUTANT(7) ? 1.0 : 0.5;            /* dropped 1/2 */
+            v = half * v * (1.0 + tanh(c * (v + 0.044715 * v * v * v)));
+        } else if (act == 3) {
+            v = MUTANT(8) ? v / (1.0 + exp(v))               /* sigmoid(-x) */
+                          : v / (1.0 + exp(-v));
+        }
+        x[i] = v;
+    }
+}
+
+/* ------------------------------------------------------------------------- */
 /* O5' MoE layer 0 behind a token AllGather (Flux README: all-gather fused    */
 /* with the grouped GEMM of MoE MLP layer 0).  The expert-parallel ranks'     */
 /* token chunks are gathered (arrival order, placed by chunk index: chunk c   */

@@ -298,6 +298,44 @@ def pin_moe_layer0_onehot_is_gemm(o):
     assert np.array_equal(H, o.gemm(BF16, X, W1[0]))
 
 
+# -- O5a activation (closed forms and identities) ---------------------------
+
+_ACT_X = np.concatenate([np.linspace(-8.0, 8.0, 3201), [0.0, -0.0, 1e-300, -1e-300, 40.0, -40.0]])
+
+
+def pin_act_none(o):
+    assert np.array_equal(o.activation(0, _ACT_X), _ACT_X)
+
+
+def pin_act_relu(o):
+    y, yn = o.activation(1, _ACT_X), o.activation(1, -_ACT_X)
+    assert (y >= 0).all()
+    assert np.array_equal(y - yn, _ACT_X)          # relu(x) - relu(-x) = x
+    assert (y * yn == 0).all()                     # one of the two is zero
+
+
+def pin_act_gelu(o):
+    import math
+    y, yn = o.activation(2, _ACT_X), o.activation(2, -_ACT_X)
+    # odd part: g(x) - g(-x) = x, since tanh is odd (checks the 1/2 factor)
+    assert np.abs((y - yn) - _ACT_X).max() <= 1e-12
+    # the tanh form approximates the exact GELU x * Phi(x) (Phi the normal CDF,
+    # through math.erf) to within a few 1e-4: a wrong constant breaks this
+    exact = np.array([x * 0.5 * (1.0 + math.erf(x / math.sqrt(2.0))) for x in _ACT_X])
+    assert np.abs(y - exact).max() <= 1e-3
+    assert o.activation(2, np.array([0.0]))[0] == 0.0
+
+
+def pin_act_silu(o):
+    import math
+    ln3 = math.log(3.0)
+    # sigmoid(ln 3) = 3/4 and sigmoid(-ln 3) = 1/4 exactly
+    y = o.activation(3, np.array([ln3, -ln3, 0.0]))
+    assert abs(y[0] - 0.75 * ln3) <= 1e-15 and abs(y[1] + 0.25 * ln3) <= 1e-15 and y[2] == 0.0
+    d = o.activation(3, _ACT_X) - o.activation(3, -_ACT_X)
+    assert np.abs(d - _ACT_X).max() <= 1e-12      # x*s(x) + x*s(-x) = x
+
+
 def pin_moe_layer1_token_loop(o):
     inp, e0, nl, topk, dt = _tiny_moe(seed=64)
     off, sp = o.moe_route(inp["topk_ids"], e0, nl)
@@ -400,6 +438,7 @@ ALL_PINS = [
     pin_rs_sum_of_slices, pin_rs_split_k_bruteforce, pin_rs_single_rank_is_gemm,
     pin_route_numpy, pin_route_edges, pin_route_routing_workload,
     pin_moe_layer0_bruteforce, pin_moe_ag_layer0_gather, pin_moe_layer0_onehot_is_gemm,
+    pin_act_none, pin_act_relu, pin_act_gelu, pin_act_silu,
     pin_moe_layer1_token_loop,
     pin_moe_identical_experts_chain, pin_moe_ep_ranks_sum,
     pin_golden_mlp, pin_golden_moe,

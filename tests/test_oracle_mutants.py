@@ -2,7 +2,7 @@
 oracle/fm_oracle.c) must be caught by at least one of the pins that guard the
 function it lives in.  This shows the pins are strong enough to notice a
 dropped term, a misplaced chunk, a wrong slice, an unstable sort, a wrong
-gather index and a dropped gate weight."""
+gather index, a dropped gate weight and wrong activation forms."""
 import pytest
 
 import oracle as oracle_pkg
@@ -22,6 +22,8 @@ MUTANTS = {
     5: ("unstable placement inside an expert", [pins.pin_route_numpy, pins.pin_golden_moe]),
     6: ("pair id used as the gathered token", [pins.pin_moe_layer0_bruteforce,
                                                pins.pin_golden_moe]),
+    7: ("GELU without its factor 1/2", [pins.pin_act_gelu]),
+    8: ("SiLU with sigmoid(-x)", [pins.pin_act_silu]),
 }
 
 
