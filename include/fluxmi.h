@@ -63,6 +63,15 @@ typedef enum fm_dtype {
     FM_F32 = 2
 } fm_dtype_t;
 
+/* Activation applied to MoE layer 0's fp32 result before it is rounded and
+ * stored (fm_moe_gather_gemm_act). */
+typedef enum fm_act {
+    FM_ACT_NONE = 0,       /* H = X W1, as fm_moe_gather_gemm */
+    FM_ACT_RELU = 1,       /* max(x, 0) */
+    FM_ACT_GELU_TANH = 2,  /* x/2 * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3))) */
+    FM_ACT_SILU = 3        /* x / (1 + exp(-x)) */
+} fm_act_t;
+
 /* Library version, major*10000 + minor*100 + patch. */
 int fm_version(void);
 
@@ -268,6 +277,22 @@ fm_status_t fm_moe_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t
                                const void* X, const int32_t* topk_ids, const void* W1,
                                void* H, int32_t* sorted_pairs, int32_t* expert_offsets,
                                hipStream_t stream);
+
+/*
+ * fm_moe_gather_gemm_act -- fm_moe_gather_gemm with an activation fused into
+ * the epilogue: H[row, :] = act(X[p / topk, :] * W1[e]), the activation taken
+ * in fp32 on the accumulated value, then rounded (RNE) to dt.  The FLUX
+ * review's MLP forward pass (section 三, "MLP 前向传播") feeds the first GEMM's
+ * output to the second as is, which is FM_ACT_NONE; the other forms cover
+ * expert MLPs that apply an activation between their two GEMMs.  Arguments,
+ * layouts and errors as fm_moe_gather_gemm; an act outside fm_act_t gives
+ * FM_ERR_INVALID_ARG before anything is launched.
+ */
+fm_status_t fm_moe_gather_gemm_act(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn,
+                                   int32_t topk, int32_t expert_begin, int32_t n_local,
+                                   const void* X, const int32_t* topk_ids, const void* W1,
+                                   void* H, int32_t* sorted_pairs, int32_t* expert_offsets,
+                                   fm_act_t act, hipStream_t stream);
 
 /*
  * fm_moe_ag_gather_gemm -- fm_moe_gather_gemm behind a token AllGather (Flux

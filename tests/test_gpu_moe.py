@@ -97,6 +97,55 @@ def test_moe_small(oracle, monkeypatch, tile, dt, T, hidden, ffn, E, nl, e0):
     assert_close(host64(out) - inp["out_seed"], ref - inp["out_seed"], "moe combine")
 
 
+@pytest.mark.parametrize("act", [1, 2, 3])
+@pytest.mark.parametrize("dt", [F16, BF16])
+@pytest.mark.parametrize("T,hidden,ffn,tile", [(300, 136, 264, "256x256"), (1500, 256, 520, "256x256w4"),
+                                               (700, 192, 136, "128x128")])
+def test_moe_layer0_activation(oracle, monkeypatch, act, dt, T, hidden, ffn, tile):
+    """fm_moe_gather_gemm_act: H = act(gathered X @ W1[e]) against the
+    oracle's layer 0 followed by its activation (ragged rows and columns, a
+    K tail, the split last wave of the default tile)."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    monkeypatch.setenv("FM_MOE_TILE", tile)
+    E, nl, e0 = 16, 8, 0
+    say(f"moe layer0 act={act} T={T} hidden={hidden} ffn={ffn} dt={dt} tile={tile}")
+    inp = wl.moe_inputs(T, hidden, ffn, E, nl, 2, dt, seed=T + act, zipf_s=1.2)
+    roff, rsp = oracle.moe_route(inp["topk_ids"], e0, nl)
+    ref = oracle.activation(act, oracle.moe_layer0(dt, inp["X"], inp["W1"], rsp, roff, 2))
+    sp = torch.full((T * 2,), -1, dtype=torch.int32, device="cuda:0")
+    off = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
+    H = torch.zeros((T * 2, ffn), dtype=torch.float16 if dt == F16 else torch.bfloat16,
+                    device="cuda:0")
+    fm.fm_moe_gather_gemm_act(dev16(inp["X"], dt), _i32(inp["topk_ids"]), dev16(inp["W1"], dt),
+                              H, sp, off, e0, act)
+    torch.cuda.synchronize()
+    rows = int(roff[-1])
+    assert np.array_equal(off.cpu().numpy(), roff)
+    assert_close(host64(H[:rows]), ref, f"layer0 act {act}")
+
+
+def test_moe_layer0_no_activation_is_plain():
+    """FM_ACT_NONE gives the bits of fm_moe_gather_gemm."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    T, hidden, ffn, nl = 900, 256, 264, 8
+    inp = wl.moe_inputs(T, hidden, ffn, 16, nl, 2, BF16, seed=5, zipf_s=1.2)
+    outs = []
+    for fn in ("plain", "act"):
+        sp = torch.full((T * 2,), -1, dtype=torch.int32, device="cuda:0")
+        off = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
+        H = torch.zeros((T * 2, ffn), dtype=torch.bfloat16, device="cuda:0")
+        args = (dev16(inp["X"], BF16), _i32(inp["topk_ids"]), dev16(inp["W1"], BF16), H, sp, off, 0)
+        if fn == "plain":
+            fm.fm_moe_gather_gemm(*args)
+        else:
+            fm.fm_moe_gather_gemm_act(*args, fm.FM_ACT_NONE)
+        torch.cuda.synchronize()
+        outs.append(bits16(H))
+    assert np.array_equal(outs[0], outs[1])
+
+
 def test_moe_one_hot_expert(oracle):
     """All tokens routed to one local expert with weight 1 (top-1): the layer
     reduces to seed + (X W1) W2 for that expert."""

@@ -104,6 +104,13 @@ def test_moe_validation():
         fm.FM_ERR_UNSUPPORTED
     assert L.fm_moe_gather_gemm(1, 16, 60, 64, 2, 0, 8, P, P, P, P, P, P, None) == \
         fm.FM_ERR_INVALID_ARG
+    # the activation is checked first; a valid one still meets the dtype check
+    for bad_act in (-1, 4, 100):
+        assert L.fm_moe_gather_gemm_act(1, 16, 64, 64, 2, 0, 8, P, P, P, P, P, P, bad_act,
+                                        None) == fm.FM_ERR_INVALID_ARG
+    for act in (fm.FM_ACT_NONE, fm.FM_ACT_RELU, fm.FM_ACT_GELU_TANH, fm.FM_ACT_SILU):
+        assert L.fm_moe_gather_gemm_act(2, 16, 64, 64, 2, 0, 8, P, P, P, P, P, P, act,
+                                        None) == fm.FM_ERR_UNSUPPORTED
     assert L.fm_moe_gemm_scatter(1, 16, 64, 64, 2, 8, ODD, P, P, P, P, P3, None) == \
         fm.FM_ERR_INVALID_ARG
     assert L.fm_moe_gemm_scatter(1, 16, 64, 64, 2, 0, P, P, P, P, P, P3, None) == \

@@ -22,9 +22,13 @@ FM_F16, FM_BF16, FM_F32 = 0, 1, 2
 
 EXPORTS = ("fm_version", "fm_status_str", "fm_gemm", "fm_ag_gemm", "fm_ag_gemm_pull", "fm_ag_gemm_producers",
            "fm_chunk_push", "fm_chunk_push_dma", "fm_chunk_signal_paced",
-           "fm_gemm_rs", "fm_moe_route", "fm_moe_gather_gemm", "fm_moe_ag_gather_gemm",
+           "fm_gemm_rs", "fm_moe_route", "fm_moe_gather_gemm", "fm_moe_gather_gemm_act",
+           "fm_moe_ag_gather_gemm",
            "fm_moe_ag_gather_gemm_producers", "fm_moe_ag_gather_gemm_pull",
            "fm_moe_gemm_scatter")
+
+# fm_act_t: activation of MoE layer 0's result (fm_moe_gather_gemm_act)
+FM_ACT_NONE, FM_ACT_RELU, FM_ACT_GELU_TANH, FM_ACT_SILU = 0, 1, 2, 3
 
 
 class FluxMIError(RuntimeError):
@@ -74,6 +78,9 @@ def lib() -> ctypes.CDLL:
     L.fm_moe_gather_gemm.restype = ctypes.c_int
     L.fm_moe_gather_gemm.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32, p, p, p, p, p,
                                      p, p]
+    L.fm_moe_gather_gemm_act.restype = ctypes.c_int
+    L.fm_moe_gather_gemm_act.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32, p, p, p, p,
+                                         p, p, ctypes.c_int, p]
     L.fm_moe_ag_gather_gemm.restype = ctypes.c_int
     L.fm_moe_ag_gather_gemm.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32, p, p, p, p,
                                         p, p, i32, p, u32, p, p, i64, p]
@@ -284,6 +291,20 @@ def fm_moe_gather_gemm(X, topk_ids, W1, H, sorted_pairs, expert_offsets, expert_
     _check("fm_moe_gather_gemm", lib().fm_moe_gather_gemm(
         _dt(X), T, hidden, ffn, topk, int(expert_begin), n_local, _ptr(X), _ptr(topk_ids),
         _ptr(W1), _ptr(H), _ptr(sorted_pairs), _ptr(expert_offsets), _stream(stream)))
+
+
+def fm_moe_gather_gemm_act(X, topk_ids, W1, H, sorted_pairs, expert_offsets, expert_begin: int,
+                           act: int, stream=None) -> None:
+    """fm_moe_gather_gemm with act (FM_ACT_*) applied to the fp32 result
+    before it is rounded into H."""
+    T, hidden = X.shape
+    n_local, h2, ffn = W1.shape
+    topk = topk_ids.shape[1]
+    if h2 != hidden or H.shape[1] != ffn or H.shape[0] < T * topk or W1.dtype != X.dtype:
+        raise ValueError("fm_moe_gather_gemm_act: shape or dtype mismatch")
+    _check("fm_moe_gather_gemm_act", lib().fm_moe_gather_gemm_act(
+        _dt(X), T, hidden, ffn, topk, int(expert_begin), n_local, _ptr(X), _ptr(topk_ids),
+        _ptr(W1), _ptr(H), _ptr(sorted_pairs), _ptr(expert_offsets), int(act), _stream(stream)))
 
 
 def fm_moe_ag_gather_gemm(X, topk_ids, W1, H, sorted_pairs, expert_offsets, expert_begin: int,

@@ -138,6 +138,7 @@ struct MoeArgs {
   int64_t K, N;
   int64_t spin_limit;
   int topk, n_local, tiles_n, group_m;
+  int act;                    // layer 0: activation of the fp32 result (fm_act_t)
   // Tail split (layer 0): when the last wave of 256x256 tiles would fill at
   // most half of g_ref CUs, part 0 runs the full waves and part 1 the
   // remaining tiles as 256x128 halves.  tiles_n always counts 256-wide tiles.
@@ -161,6 +162,29 @@ struct MoeArgs {
   const char* pull_src[64];
 };
 
+
+// Activation of layer 0's fp32 result (fm_act_t), from the definitions:
+// ReLU max(x, 0); GELU in its tanh form x/2 (1 + tanh(u)) with u =
+// sqrt(2/pi) (x + 0.044715 x^3); SiLU x / (1 + exp(-x)).  The exponentials
+// use the hardware exp (__expf) and tanh(u) = 1 - 2 / (exp(2u) + 1), so the
+// epilogue makes no library calls (which would spill the accumulators around
+// them); both stay exact in the limits (exp overflowing to inf gives tanh 1
+// and SiLU -0).  Their fp32 error is far below the 16-bit rounding of H.
+__device__ __forceinline__ float apply_act(int act, float x) {
+  switch (act) {
+    case FM_ACT_RELU:
+      return fmaxf(x, 0.f);
+    case FM_ACT_GELU_TANH: {
+      const float u = 0.7978845608028654f * (x + 0.044715f * x * x * x);
+      const float th = 1.f - 2.f / (__expf(2.f * u) + 1.f);
+      return 0.5f * x * (1.f + th);
+    }
+    case FM_ACT_SILU:
+      return x / (1.f + __expf(-x));
+    default:
+      return x;
+  }
+}
 
 // Called by one thread: wait until every tile of an expert before e in
 // column tn whose token range overlaps that of global M-tile gm has published
@@ -197,12 +221,16 @@ __device__ __forceinline__ void wait_token_range(const MoeArgs& a, const int* s_
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-template <class E, int BM, int BN, int NW, bool SCATTER, bool KTAIL, bool PULL = false>
+template <class E, int BM, int BN, int NW, bool SCATTER, bool KTAIL, bool PULL = false,
+          bool ACT = false>
 __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   // One wave per SIMD has the register room for a two-sub-step read-ahead.
   // PULL: the token rows are gathered from the owners' chunk buffers, one
   // 64-bit address per row.
   static_assert(!(SCATTER && PULL), "pull mode is a layer-0 form");
+  // ACT: layer 0 with an activation (a.act); a separate instantiation, so
+  // the plain form carries none of its code.
+  static_assert(!(ACT && (SCATTER || PULL)), "the activation is a plain layer-0 form");
   using Eng = Engine<E, BM, BN, KTAIL, NW, 4, NW == 4 ? 2 : 1, false, PULL>;
   // the combine's epilogue also keeps its destination rows in LDS
   constexpr int kSmem =
@@ -537,19 +565,26 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       // H rows in expert-sorted order, 16-bit.
       const int col = eng.ep_col();
       const bool col_ok = n0 + col < N;
-#pragma unroll
-      for (int i = 0; i < Eng::FM; ++i) {
+      // Blocks by compile-time index: with the activation's code the body
+      // is too large for the unroller, and a runtime block index would move
+      // the accumulators to scratch.
+      static_for<Eng::FM>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
         eng.ep_stage(i);
 #pragma unroll
         for (int q = 0; q < Eng::EP_READS; ++q) {
           const int lr = m0 + eng.ep_row(i, q);
-          const f32x4 v = eng.ep_read(q);
+          f32x4 v = eng.ep_read(q);
+          if constexpr (ACT) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[k] = apply_act(a.act, v[k]);
+          }
           if (lr < rows_e && col_ok) {
             const u32x2 pk = {E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
             *reinterpret_cast<u32x2*>(a.out + ((int64_t)(row_base + lr) * N + n0 + col) * 2) = pk;
           }
         }
-      }
+      });
     }
     eng.ep_end();
   }
@@ -627,7 +662,7 @@ int moe_ag_group() {
   return 2;
 }
 
-template <bool SCATTER, bool PULL = false>
+template <bool SCATTER, bool PULL = false, bool ACT = false>
 void launch_moe_part(fm_dtype_t dt, MoeTile cfg, const MoeArgs& a, hipStream_t stream);
 
 // Layer 0 splits a half-empty last wave into 256x128 halves (part 1, a second
@@ -655,26 +690,33 @@ fm_status_t launch_moe(fm_dtype_t dt, MoeTile cfg, MoeArgs& a, hipStream_t strea
     if (!a.ctr) return FM_ERR_HIP;
     a.tile_done = a.ctr + kColDone0;
   }
-  if (!SCATTER && a.pull_src[0]) launch_moe_part<false, true>(dt, cfg, a, stream);
-  else launch_moe_part<SCATTER>(dt, cfg, a, stream);
+  auto launch_part = [&](MoeTile c) {
+    if constexpr (SCATTER) {
+      launch_moe_part<true>(dt, c, a, stream);
+    } else {
+      if (a.pull_src[0]) launch_moe_part<false, true>(dt, c, a, stream);
+      else if (a.act != FM_ACT_NONE) launch_moe_part<false, false, true>(dt, c, a, stream);
+      else launch_moe_part<false>(dt, c, a, stream);
+    }
+  };
+  launch_part(cfg);
   if (a.split) {
     a.part = 1;
-    if (!SCATTER && a.pull_src[0]) launch_moe_part<false, true>(dt, MoeTile{256, 128, 4}, a, stream);
-    else launch_moe_part<SCATTER>(dt, MoeTile{256, 128, 4}, a, stream);
+    launch_part(MoeTile{256, 128, 4});
   }
   return launch_status();
 }
 
-template <bool SCATTER, bool PULL>
+template <bool SCATTER, bool PULL, bool ACT>
 void launch_moe_part(fm_dtype_t dt, MoeTile cfg, const MoeArgs& a, hipStream_t stream) {
   const dim3 grid(device_cu_count());
 #define FM_LAUNCH(E, BM, BN, NW)                                                              \
   do {                                                                                        \
     if (a.K % kBK) /* ragged K: the 4-wave form keeps the tail path spill-free */             \
-      hipLaunchKernelGGL((moe_kernel<E, BM, BN, 4, SCATTER, true, PULL>), grid, dim3(256), 0,  \
-                         stream, a);                                                          \
+      hipLaunchKernelGGL((moe_kernel<E, BM, BN, 4, SCATTER, true, PULL, ACT>), grid,          \
+                         dim3(256), 0, stream, a);                                            \
     else                                                                                      \
-      hipLaunchKernelGGL((moe_kernel<E, BM, BN, NW, SCATTER, false, PULL>), grid,             \
+      hipLaunchKernelGGL((moe_kernel<E, BM, BN, NW, SCATTER, false, PULL, ACT>), grid,        \
                          dim3(64 * NW), 0, stream, a);                                        \
   } while (0)
 #define FM_LAUNCH_E(E)                                                                       \
@@ -737,7 +779,8 @@ fm_status_t moe_gather_impl(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ff
                             const uint32_t* flags, uint32_t epoch, const int32_t* order,
                             int32_t* err_word, int64_t spin_limit, hipStream_t stream,
                             const void* const* src = nullptr, uint32_t* counters = nullptr,
-                            int32_t n_producers = 0, const void* const* pull = nullptr) {
+                            int32_t n_producers = 0, const void* const* pull = nullptr,
+                            int act = FM_ACT_NONE) {
   if (dt != FM_F16 && dt != FM_BF16) return FM_ERR_UNSUPPORTED;
   fm_status_t st = check_route_args(T, topk, n_local, topk_ids, sorted_pairs, expert_offsets);
   if (st != FM_OK) return st;
@@ -813,6 +856,7 @@ fm_status_t moe_gather_impl(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ff
                    const_cast<uint32_t*>(flags), counters, epoch);
   }
   a.ag_group = moe_ag_group();
+  a.act = act;
   return launch_moe<false>(dt, moe_tile(false), a, stream);
 }
 
@@ -828,6 +872,18 @@ extern "C" fm_status_t fm_moe_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidd
   return moe_gather_impl(dt, T, hidden, ffn, topk, expert_begin, n_local, X, topk_ids, W1, H,
                          sorted_pairs, expert_offsets, 0, nullptr, 0, nullptr, nullptr, 0,
                          stream);
+}
+
+extern "C" fm_status_t fm_moe_gather_gemm_act(fm_dtype_t dt, int64_t T, int64_t hidden,
+                                              int64_t ffn, int32_t topk, int32_t expert_begin,
+                                              int32_t n_local, const void* X,
+                                              const int32_t* topk_ids, const void* W1, void* H,
+                                              int32_t* sorted_pairs, int32_t* expert_offsets,
+                                              fm_act_t act, hipStream_t stream) {
+  if ((int)act < FM_ACT_NONE || (int)act > FM_ACT_SILU) return FM_ERR_INVALID_ARG;
+  return moe_gather_impl(dt, T, hidden, ffn, topk, expert_begin, n_local, X, topk_ids, W1, H,
+                         sorted_pairs, expert_offsets, 0, nullptr, 0, nullptr, nullptr, 0,
+                         stream, nullptr, nullptr, 0, nullptr, (int)act);
 }
 
 extern "C" fm_status_t fm_moe_ag_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidden,
