@@ -33,10 +33,12 @@ def _capture(body):
     return g
 
 
-def test_graph_moe_layer_replays():
-    """Route + layer 0 + the combine in one graph.  The combine's ordering
-    epoch advances on the device, so each replay (and the eager calls between
-    replays, which advance it too) orders its tiles correctly."""
+@pytest.mark.parametrize("act", [None, 2])
+def test_graph_moe_layer_replays(act):
+    """Route + layer 0 (plain, or with the tanh-form GELU fused) + the combine
+    in one graph.  The combine's ordering epoch advances on the device, so
+    each replay (and the eager calls between replays, which advance it too)
+    orders its tiles correctly."""
     import torch
     import tile_gemm_communication_amd as fm
     T, hidden, ffn, E, nl, e0 = 3072, 256, 264, 16, 8, 0
@@ -52,7 +54,10 @@ def test_graph_moe_layer_replays():
 
     def body():
         out.copy_(seed)
-        fm.fm_moe_gather_gemm(X, ids, W1, H, sp, off, e0)
+        if act is None:
+            fm.fm_moe_gather_gemm(X, ids, W1, H, sp, off, e0)
+        else:
+            fm.fm_moe_gather_gemm_act(X, ids, W1, H, sp, off, e0, act)
         fm.fm_moe_gemm_scatter(H, W2, sp, off, wts, out)
 
     body()
@@ -64,7 +69,7 @@ def test_graph_moe_layer_replays():
         out.fill_(float("nan"))
         g.replay()
         torch.cuda.synchronize()
-        say(f"moe graph replay {r}")
+        say(f"moe graph replay {r} act={act}")
         assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), f"replay {r}"
         # eager combine calls between replays move the device epoch on
         other.copy_(seed)
