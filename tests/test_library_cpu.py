@@ -117,6 +117,15 @@ def test_moe_validation():
         fm.FM_ERR_INVALID_ARG
 
 
+def test_combine_flag_capacity_limit():
+    """More (M-tile, N-tile) completion flags than the counter buffer holds
+    is refused before anything is allocated or launched."""
+    L = fm.lib()
+    # 2^20 rows -> 4104 M-tiles (with 8 ragged experts) x 16 N-tiles > 16384
+    assert L.fm_moe_gemm_scatter(1, 1 << 19, 4096, 8, 2, 8, P, P, P, P, P, P3, None) == \
+        fm.FM_ERR_UNSUPPORTED
+
+
 def test_chunk_push_validation():
     L = fm.lib()
     assert L.fm_chunk_push(P, P2, 100, P3, P3, 1, 0, None) == fm.FM_ERR_INVALID_ARG   # 16 B
