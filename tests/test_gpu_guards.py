@@ -87,3 +87,25 @@ def test_rs_epilogue_stays_in_bounds(monkeypatch, M, N, K, P, tile):
     for r in range(P):
         assert _guards_intact(bigs[r], rows * N, 0x7FC0BEEF), f"slice {r}"
         assert torch.isfinite(dst[r]).all()
+
+
+@pytest.mark.parametrize("out32", [False, True])
+@pytest.mark.parametrize("M,N,K,tile", [(200, 136, 72, "256x256"), (300, 264, 1000, "256x128"),
+                                        (130, 520, 64, "128x128")])
+def test_gemm_store_stays_in_bounds(monkeypatch, out32, M, N, K, tile):
+    import torch
+    import tile_gemm_communication_amd as fm
+    monkeypatch.setenv("FM_TILE", tile)
+    say(f"guards gemm {M}x{N}x{K} tile={tile} out32={out32}")
+    A = dev16(wl.normal_bits((M, K), M + 1, F16), F16)
+    B = dev16(wl.normal_bits((K, N), N + 2, F16, 1.0 / np.sqrt(K)), F16)
+    if out32:
+        big, flat = _guarded(M * N, torch.int32, 0x7FC0F00D)
+        C = flat.view(torch.float32).view(M, N)
+    else:
+        big, flat = _guarded(M * N, torch.int16, 0x7ABC)
+        C = flat.view(torch.float16).view(M, N)
+    fm.fm_gemm(A, B, C)
+    torch.cuda.synchronize()
+    assert _guards_intact(big, M * N, 0x7FC0F00D if out32 else 0x7ABC)
+    assert torch.isfinite(C.float()).all()
