@@ -159,6 +159,8 @@ class Workload:
         self.H = torch.empty((self.T * self.topk, self.ffn), dtype=bf16, device=dev)
         self.sp = torch.empty(self.T * self.topk, dtype=torch.int32, device=dev)
         self.off = torch.zeros(self.n_local + 1, dtype=torch.int32, device=dev)
+        import tile_gemm_communication_amd as fm
+        self.mws = fm.moe_workspace(self.T, self.topk, self.hidden, self.n_local)
 
         # three side streams: with the compute stream that is the four hardware
         # queues a process gets by default
@@ -214,17 +216,19 @@ class Workload:
 
     def moe0(self):
         import tile_gemm_communication_amd as fm
-        fm.fm_moe_gather_gemm(self.mX, self.ids, self.mW1, self.H, self.sp, self.off, self.e0)
+        fm.fm_moe_gather_gemm(self.mX, self.ids, self.mW1, self.H, self.sp, self.off, self.e0,
+                              self.mws)
 
     def moe0_ag(self, epoch):
         import tile_gemm_communication_amd as fm
         fm.fm_moe_ag_gather_gemm(self.mXg, self.ids, self.mW1, self.H, self.sp, self.off, self.e0,
-                                 self.mflags, epoch, self.n, order=self.order,
+                                 self.mflags, epoch, self.n, self.mws, order=self.order,
                                  err_word=self.err)
 
     def moe1(self):
         import tile_gemm_communication_amd as fm
-        fm.fm_moe_gemm_scatter(self.H, self.mW2, self.sp, self.off, self.wts, self.mout)
+        fm.fm_moe_gemm_scatter(self.H, self.mW2, self.sp, self.off, self.wts, self.mout, self.mws,
+                               err_word=self.err)
 
     def step(self, evs=None):
         """One full step on the current stream (+ the side streams for arrival).
@@ -442,13 +446,13 @@ def ect_block(w, iters):
         w.epoch += 1
         w.push_all(w.epoch, moe=True)
         w.join_sides()
-        fm.fm_moe_gather_gemm(w.mXg, w.ids, w.mW1, w.H, w.sp, w.off, w.e0)
+        fm.fm_moe_gather_gemm(w.mXg, w.ids, w.mW1, w.H, w.sp, w.off, w.e0, w.mws)
 
     def moe_producers():
         # the token copies run on producer workgroups of layer 0's own launch
         w.epoch += 1
         fm.fm_moe_ag_gather_gemm_producers([None] + w.mpeers[1:], w.mXg, w.ids, w.mW1, w.H, w.sp,
-                                           w.off, w.e0, w.mflags, w.mcounters, w.epoch,
+                                           w.off, w.e0, w.mflags, w.mcounters, w.epoch, w.mws,
                                            order=w.order, err_word=w.err)
 
     # pull mode: layer 0 reads each owner's 16 MiB chunk in place, signals
@@ -462,7 +466,8 @@ def ect_block(w, iters):
             s.wait_stream(cs)
             fm.fm_chunk_signal_paced(w.mflags, times, w.epoch, order=w.order, stream=s)
             fm.fm_moe_ag_gather_gemm_pull(w.mpeers, w.ids, w.mW1, w.H, w.sp, w.off, w.e0,
-                                          w.mflags, w.epoch, order=w.order, err_word=w.err)
+                                          w.mflags, w.epoch, w.mws, order=w.order,
+                                          err_word=w.err)
             cs.wait_stream(s)
         return fn
 
@@ -584,7 +589,7 @@ def main():
         w.step(evs[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    assert int(w.err.item()) == 0, "fm_ag_gemm reported a timeout"
+    assert int(w.err.item()) == 0, f"a kernel reported {fm.status_str(int(w.err.item()))}"
     ms_step = (t1 - t0) * 1e3 / args.steps
     names = ["ag_gemm", "gemm_rs", "moe_gather_gemm", "moe_gemm_scatter"]
     per_step = {n: sorted(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps))

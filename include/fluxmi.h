@@ -20,11 +20,15 @@
  *
  * Conventions for every call:
  *  - All matrices are dense and row-major.  A / X are [M, K]; B / W are [K, N].
- *  - Every pointer argument that names a matrix, flag or index buffer is a
- *    device pointer to memory owned by the caller; the library allocates
- *    nothing, keeps no state between calls beyond cached device properties,
- *    and never synchronizes the host.  Calls are enqueued on `stream` (NULL =
- *    the null stream) and return before the work runs.
+ *  - Every pointer argument that names a matrix, flag, index buffer or
+ *    workspace is a device pointer to memory owned by the caller; the library
+ *    allocates nothing, keeps no state of its own between calls beyond cached
+ *    device properties (the compute-unit count), and never synchronizes the
+ *    host.  State that must outlive one call (the MoE operators' counters and
+ *    completion flags) lives in a caller-owned workspace whose size
+ *    fm_moe_workspace_bytes gives.  Calls are enqueued on `stream` (NULL =
+ *    the null stream) and return before the work runs; every call is
+ *    re-entrant for disjoint buffers.
  *  - 16-bit operands are IEEE binary16 (FM_F16) or bfloat16 (FM_BF16); every
  *    product is accumulated in fp32; narrowing to 16 bits rounds to nearest
  *    even.
@@ -38,10 +42,37 @@
  *    (see fm_ag_gemm).  No C++ exception crosses this interface.
  *  - Calls that write the same output on one stream are ordered; calls on
  *    different streams that write the same buffer race.
+ *
+ * Chunk-arrival protocol (fm_ag_gemm and its variants, fm_moe_ag_gather_gemm):
+ *  - A producer makes a chunk's bytes visible device-wide before it publishes
+ *    the chunk's flag.  The portable form is a store of the flag with release
+ *    semantics at device (agent) scope, as fm_chunk_signal_paced does.  The
+ *    library's own copy producers (fm_chunk_push, the producer workgroups of
+ *    fm_ag_gemm_producers / fm_moe_ag_gather_gemm_producers) use an equivalent
+ *    form that is cheaper on a GPU whose L2 caches are per XCD and not
+ *    coherent with each other: each wave writes the chunk with write-through
+ *    (system-scope) stores, waits until those stores have completed, passes a
+ *    workgroup barrier, and only then updates the counter and the flag with
+ *    relaxed atomics.  A release at agent scope would instead write back the
+ *    whole L2 of the producer's XCD, once per workgroup.  Any producer must
+ *    follow one of these two forms.  Consumers poll with relaxed loads and
+ *    acquire at agent scope after the flag is seen.
+ *  - The consumers of one launch may occupy every compute unit while they
+ *    wait.  A producer kernel that runs on another stream (emulated arrival
+ *    on one GPU) must therefore be enqueued on a stream that HIP maps to a
+ *    different hardware queue than the consumer's, and before the consumer,
+ *    so that its workgroups are dispatched first; with the default four
+ *    hardware queues per process, streams created in a row take queues in
+ *    turn.  A producer stream that shares the consumer's queue runs after
+ *    the consumer, which then waits until spin_limit and reports
+ *    FM_ERR_TIMEOUT.  Producers on the copy engines (fm_chunk_push_dma) and
+ *    the producer workgroups of the *_producers forms (lowest workgroup ids,
+ *    dispatched first) do not depend on this.
  */
 #ifndef FLUXMI_H
 #define FLUXMI_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -191,15 +222,17 @@ fm_status_t fm_chunk_signal_paced(uint32_t* flags, int32_t n_chunks, const int32
 
 /*
  * fm_chunk_push -- producer side of the chunk-arrival protocol: copy `bytes`
- * from src to dst, then publish *flag = epoch (release, device scope) once
- * every byte is visible.  This is what a peer rank's push (the review's
+ * from src to dst, then publish *flag = epoch once every byte is visible
+ * device-wide (the write-through form of the protocol above: every
+ * workgroup's stores have completed before the last one to check in on
+ * `counter` stores the flag).  This is what a peer rank's push (the review's
  * "推送模式" in "拉取 vs 推送数据传输") does to this rank's gathered buffer; on
  * one GPU src and dst are both local.
  *   bytes    multiple of 16 (0 = publish the flag only); src/dst 16-byte aligned
  *            and non-overlapping.
  *   counter  device uint32 scratch owned by the caller, zero before the
  *            first call and left zero after every call; one per flag in use.
- *   n_workgroups  copy workgroups, 0 = default (one per 192 KiB, at most
+ *   n_workgroups  copy workgroups, 0 = default (one per 96 KiB, at most
  *                 two per compute unit).
  */
 fm_status_t fm_chunk_push(const void* src, void* dst, int64_t bytes, uint32_t* flag,
@@ -241,6 +274,25 @@ fm_status_t fm_gemm_rs(fm_dtype_t dt, int64_t M, int64_t N, int64_t K, int32_t n
                        int32_t atomic, hipStream_t stream);
 
 /*
+ * fm_moe_workspace_bytes -- bytes of device workspace that the MoE operators
+ * (fm_moe_route, fm_moe_gather_gemm and its variants, fm_moe_gemm_scatter)
+ * need for T tokens with topk pairs each, a hidden size `hidden` and n_local
+ * local experts; 0 if the arguments are out of range (T < 0, topk < 1,
+ * hidden < 0, n_local outside 1..64).  A workspace of this size serves every
+ * call of one MoE layer with these (or smaller) sizes.
+ * The workspace is 16-byte aligned device memory owned by the caller.  Fill
+ * it with zeros once, before its first use; every call leaves it ready for
+ * the next (calls keep an epoch and a few counters in it, so that nothing
+ * needs resetting between calls, also when a call is replayed from a HIP
+ * graph).  One workspace must not be used by two routes (or two combines) at
+ * the same time: issue such calls on one stream, or order their streams.  A
+ * route (or layer 0) and a combine may share one workspace concurrently.
+ * Separate MoE layers (for instance two expert-parallel ranks emulated on one
+ * GPU) that run at the same time need one workspace each.
+ */
+size_t fm_moe_workspace_bytes(int64_t T, int32_t topk, int64_t hidden, int32_t n_local);
+
+/*
  * fm_moe_route -- expert-sorted row index of this rank's local experts
  * (COMET article, "COMET 的技术原理": the tensor shared between the MoE
  * layers is decomposed along the token dimension).
@@ -253,15 +305,15 @@ fm_status_t fm_gemm_rs(fm_dtype_t dt, int64_t M, int64_t N, int64_t K, int32_t n
  *                 [0, expert_offsets[n_local]) hold the local pair ids stably
  *                 sorted by expert (increasing pair id within an expert); the
  *                 rest is left untouched.
- * Deterministic: identical bits on every call.  The per-chunk histograms of
- * the counting sort use the library's per-device counter buffer (see
- * fm_moe_gemm_scatter; FM_ERR_HIP if its first allocation fails): route
- * calls (also those inside fm_moe_gather_gemm) on one device must not
- * overlap in time.
+ *   ws, ws_bytes  the MoE workspace (fm_moe_workspace_bytes); the per-chunk
+ *                 histograms of the counting sort live there.  A null,
+ *                 misaligned or too small workspace gives FM_ERR_INVALID_ARG.
+ * Deterministic: identical bits on every call.
  */
 fm_status_t fm_moe_route(int64_t T, int32_t topk, int32_t expert_begin, int32_t n_local,
                          const int32_t* topk_ids, int32_t* sorted_pairs,
-                         int32_t* expert_offsets, hipStream_t stream);
+                         int32_t* expert_offsets, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
 
 /*
  * fm_moe_gather_gemm -- MoE layer 0 on this rank: route (as fm_moe_route),
@@ -271,12 +323,13 @@ fm_status_t fm_moe_route(int64_t T, int32_t topk, int32_t expert_begin, int32_t 
  * into the GEMM's A loads).  Row counts stay on the device: no host sync.
  *   X   [T, hidden]; W1 [n_local, hidden, ffn]; H [T*topk, ffn] (rows past
  *       expert_offsets[n_local] are left untouched).  dt FM_F16 or FM_BF16.
+ *   ws, ws_bytes  the MoE workspace, as fm_moe_route.
  */
 fm_status_t fm_moe_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn,
                                int32_t topk, int32_t expert_begin, int32_t n_local,
                                const void* X, const int32_t* topk_ids, const void* W1,
                                void* H, int32_t* sorted_pairs, int32_t* expert_offsets,
-                               hipStream_t stream);
+                               void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * fm_moe_gather_gemm_act -- fm_moe_gather_gemm with an activation fused into
@@ -292,7 +345,7 @@ fm_status_t fm_moe_gather_gemm_act(fm_dtype_t dt, int64_t T, int64_t hidden, int
                                    int32_t topk, int32_t expert_begin, int32_t n_local,
                                    const void* X, const int32_t* topk_ids, const void* W1,
                                    void* H, int32_t* sorted_pairs, int32_t* expert_offsets,
-                                   fm_act_t act, hipStream_t stream);
+                                   fm_act_t act, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * fm_moe_ag_gather_gemm -- fm_moe_gather_gemm behind a token AllGather (Flux
@@ -312,6 +365,7 @@ fm_status_t fm_moe_gather_gemm_act(fm_dtype_t dt, int64_t T, int64_t hidden, int
  *             the tiles).
  *   err_word, spin_limit  as fm_ag_gemm (a wait past the limit writes
  *             FM_ERR_TIMEOUT there; H is then undefined).
+ *   ws, ws_bytes  the MoE workspace, as fm_moe_route.
  * The result equals fm_moe_gather_gemm on the fully gathered X, bit for bit.
  */
 fm_status_t fm_moe_ag_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn,
@@ -320,7 +374,7 @@ fm_status_t fm_moe_ag_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidden, int6
                                   void* H, int32_t* sorted_pairs, int32_t* expert_offsets,
                                   int32_t n_chunks, const uint32_t* flags, uint32_t epoch,
                                   const int32_t* order, int32_t* err_word, int64_t spin_limit,
-                                  hipStream_t stream);
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * fm_moe_ag_gather_gemm_producers -- fm_moe_ag_gather_gemm with the token
@@ -348,7 +402,8 @@ fm_status_t fm_moe_ag_gather_gemm_producers(
     int32_t n_local, void* X, const int32_t* topk_ids, const void* W1, void* H,
     int32_t* sorted_pairs, int32_t* expert_offsets, int32_t n_chunks, const void* const* src,
     uint32_t* flags, uint32_t* counters, uint32_t epoch, const int32_t* order,
-    int32_t n_producers, int32_t* err_word, int64_t spin_limit, hipStream_t stream);
+    int32_t n_producers, int32_t* err_word, int64_t spin_limit, void* ws, size_t ws_bytes,
+    hipStream_t stream);
 
 /*
  * fm_moe_ag_gather_gemm_pull -- fm_moe_ag_gather_gemm in pull mode (FLUX
@@ -360,7 +415,7 @@ fm_status_t fm_moe_ag_gather_gemm_producers(
  *           16-byte aligned [T/n_chunks, hidden] block of tokens
  *           [c*T/n_chunks, (c+1)*T/n_chunks).
  *   the rest  as fm_moe_ag_gather_gemm (flags, epoch, order, err_word,
- *           spin_limit; signals from fm_chunk_signal_paced or a peer).
+ *           spin_limit, ws; signals from fm_chunk_signal_paced or a peer).
  * The result equals fm_moe_gather_gemm on the concatenated chunks, bit for
  * bit.
  */
@@ -368,35 +423,51 @@ fm_status_t fm_moe_ag_gather_gemm_pull(
     fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn, int32_t topk, int32_t expert_begin,
     int32_t n_local, const void* const* chunks, const int32_t* topk_ids, const void* W1, void* H,
     int32_t* sorted_pairs, int32_t* expert_offsets, int32_t n_chunks, const uint32_t* flags,
-    uint32_t epoch, const int32_t* order, int32_t* err_word, int64_t spin_limit,
-    hipStream_t stream);
+    uint32_t epoch, const int32_t* order, int32_t* err_word, int64_t spin_limit, void* ws,
+    size_t ws_bytes, hipStream_t stream);
 
 /*
  * fm_moe_gemm_scatter -- MoE layer 1 on this rank with the top-k weighted
  * combine fused into the GEMM epilogue (Flux README: grouped GEMM fused with
- * the reduce-scatter of MoE MLP layer 1):
+ * the reduce-scatter of MoE MLP layer 1; COMET article, "COMET 的技术原理":
+ * the per-token combine over the experts):
  *   out[t, :] += sum over local pairs p = t*topk + k of
  *                topk_weights[p] * (H[row(p), :] * W2[e(p)])
  * where row(p) is p's position in sorted_pairs (from fm_moe_gather_gemm /
  * fm_moe_route with the same arguments).
  *   H [rows, ffn] with rows = expert_offsets[n_local]; W2 [n_local, ffn, hidden];
  *   topk_weights device fp32 [T, topk]; out device fp32 [T, hidden].
+ *   Precondition: the local pairs of one token lie in different experts (a
+ *   top-k choice never picks one expert twice).  A token with two pairs in
+ *   one local expert is reported as FM_ERR_INVALID_ARG in err_word; the
+ *   adds of the row tiles that hold the repeated pair are skipped, and out
+ *   is then undefined.
+ *   err_word  device int32 or NULL: receives FM_ERR_TIMEOUT if an ordering
+ *             wait exceeds spin_limit polls (the launch then abandons its
+ *             remaining tiles, out is undefined, the call never hangs), or
+ *             FM_ERR_INVALID_ARG as above.  Left untouched otherwise.
+ *   spin_limit  polls of one completion flag before giving up (each poll
+ *             sleeps ~0.1 us); 0 selects the default of 2^24.
+ *   ws, ws_bytes  the MoE workspace (fm_moe_workspace_bytes with the same T,
+ *             topk, hidden and n_local or larger); FM_ERR_INVALID_ARG if it
+ *             is null, misaligned or too small.
  * The additions into a token row are applied in local-expert order with plain
- * fp32 loads and stores (no atomics), so the result is deterministic.  The
- * ordering uses per-(row tile, column tile) completion flags in a per-device
- * buffer that the library allocates on the first call (128 KiB, kept until
- * the process ends; FM_ERR_HIP if that allocation fails), stamped with an
- * epoch that the kernel itself advances in that buffer, so the call may be
- * captured in a HIP graph and replayed (make the first call outside the
- * capture: it allocates).  Calls of this function on one device must not
- * overlap in time (issue them on one stream, or order the streams).  Requires
- * (ceil(T*topk/256) + n_local) * ceil(hidden/256) <= 16384, else
- * FM_ERR_UNSUPPORTED.
+ * fp32 loads and stores (no atomics), so the result is deterministic.  Each
+ * row tile of one expert waits for the tiles of earlier experts in its column
+ * whose token ranges overlap its own, through per-(row tile, column tile)
+ * completion flags in the workspace, stamped with an epoch that the kernel
+ * itself advances there (so the call may be captured in a HIP graph and
+ * replayed).  Tiles are handed out by an atomic ticket in expert order, so a
+ * tile only ever waits for tiles that running workgroups hold: the call
+ * completes whatever share of the GPU it gets (another kernel, or another
+ * combine on another stream with its own workspace, may run beside it).
  */
 fm_status_t fm_moe_gemm_scatter(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn,
                                 int32_t topk, int32_t n_local, const void* H, const void* W2,
                                 const int32_t* sorted_pairs, const int32_t* expert_offsets,
-                                const float* topk_weights, float* out, hipStream_t stream);
+                                const float* topk_weights, float* out, int32_t* err_word,
+                                int64_t spin_limit, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
 
 #ifdef __cplusplus
 }

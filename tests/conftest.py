@@ -14,6 +14,17 @@ def pytest_configure(config):
 
 
 @pytest.fixture(scope="session")
+def built_library():
+    """libfluxmi.so, compiled first (hipcc, gfx950; no GPU needed) when a fresh
+    checkout has none yet."""
+    import tile_gemm_communication_amd as fm
+    if not os.path.exists(fm.LIB_PATH):
+        from tile_gemm_communication_amd import build
+        build.build(verbose=False)
+    return fm.lib()
+
+
+@pytest.fixture(scope="session")
 def oracle():
     import oracle as _oracle
     return _oracle.load()

@@ -51,14 +51,16 @@ def test_graph_moe_layer_replays(act):
     sp = torch.full((T * 2,), -1, dtype=torch.int32, device="cuda:0")
     off = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
     out = torch.empty_like(seed)
+    ws = fm.moe_workspace(T, 2, hidden, nl)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
 
     def body():
         out.copy_(seed)
         if act is None:
-            fm.fm_moe_gather_gemm(X, ids, W1, H, sp, off, e0)
+            fm.fm_moe_gather_gemm(X, ids, W1, H, sp, off, e0, ws)
         else:
-            fm.fm_moe_gather_gemm_act(X, ids, W1, H, sp, off, e0, act)
-        fm.fm_moe_gemm_scatter(H, W2, sp, off, wts, out)
+            fm.fm_moe_gather_gemm_act(X, ids, W1, H, sp, off, e0, act, ws)
+        fm.fm_moe_gemm_scatter(H, W2, sp, off, wts, out, ws, err_word=err)
 
     body()
     torch.cuda.synchronize()
@@ -73,9 +75,10 @@ def test_graph_moe_layer_replays(act):
         assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), f"replay {r}"
         # eager combine calls between replays move the device epoch on
         other.copy_(seed)
-        fm.fm_moe_gemm_scatter(H, W2, sp, off, wts, other)
+        fm.fm_moe_gemm_scatter(H, W2, sp, off, wts, other, ws, err_word=err)
         torch.cuda.synchronize()
         assert torch.equal(other.view(torch.int32), ref.view(torch.int32))
+        assert err.item() == 0
 
 
 def test_graph_ag_rs_replays():

@@ -51,7 +51,8 @@ def test_moe_epilogues_stay_in_bounds(monkeypatch, T, hidden, ffn, tile):
     H = Hflat.view(torch.bfloat16).view(T * topk, ffn)
     sp = torch.full((T * topk,), -1, dtype=torch.int32, device="cuda:0")
     off = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
-    fm.fm_moe_gather_gemm(X, ids, W1, H, sp, off, e0)
+    ws = fm.moe_workspace(T, topk, hidden, nl)
+    fm.fm_moe_gather_gemm(X, ids, W1, H, sp, off, e0, ws)
     torch.cuda.synchronize()
     rows = int(off[-1].item())
     assert _guards_intact(Hbig, h_words, 0x7ABC)
@@ -61,7 +62,7 @@ def test_moe_epilogues_stay_in_bounds(monkeypatch, T, hidden, ffn, tile):
     Obig, Oflat = _guarded(o_words, torch.int32, 0x7FC0DEAD)
     Oflat.view(torch.float32).copy_(devf32(inp["out_seed"]).view(-1))
     fm.fm_moe_gemm_scatter(H, W2, sp, off, devf32(inp["topk_weights"]),
-                           Oflat.view(torch.float32).view(T, hidden))
+                           Oflat.view(torch.float32).view(T, hidden), ws)
     torch.cuda.synchronize()
     assert _guards_intact(Obig, o_words, 0x7FC0DEAD)
     assert torch.isfinite(Oflat.view(torch.float32)).all()

@@ -29,7 +29,7 @@ def _route(ids, e0, nl):
     T, k = ids.shape
     sp = torch.full((T * k,), -1, dtype=torch.int32, device="cuda:0")
     off = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
-    fm.fm_moe_route(_i32(ids), e0, nl, sp, off)
+    fm.fm_moe_route(_i32(ids), e0, nl, sp, off, fm.moe_workspace(T, k, 8, nl))
     torch.cuda.synchronize()
     off_h = off.cpu().numpy()
     return off_h, sp.cpu().numpy()[:off_h[-1]]
@@ -67,10 +67,16 @@ def _moe_run(inp, e0, nl, dt, H_in=None):
     off = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
     H = torch.zeros((T * topk, ffn), dtype=torch.float16 if dt == F16 else torch.bfloat16,
                     device="cuda:0")
-    fm.fm_moe_gather_gemm(dev16(inp["X"], dt), _i32(ids), dev16(inp["W1"], dt), H, sp, off, e0)
+    ws = fm.moe_workspace(T, topk, hidden, nl)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    fm.fm_moe_gather_gemm(dev16(inp["X"], dt), _i32(ids), dev16(inp["W1"], dt), H, sp, off, e0,
+                          ws)
     out = devf32(inp["out_seed"])
     Hsrc = H if H_in is None else dev16(H_in, dt)
-    fm.fm_moe_gemm_scatter(Hsrc, dev16(inp["W2"], dt), sp, off, devf32(wts), out)
+    fm.fm_moe_gemm_scatter(Hsrc, dev16(inp["W2"], dt), sp, off, devf32(wts), out, ws,
+                           err_word=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0, fm.status_str(err.item())
     torch.cuda.synchronize()
     return off.cpu().numpy(), sp.cpu().numpy(), H, out
 
@@ -118,7 +124,7 @@ def test_moe_layer0_activation(oracle, monkeypatch, act, dt, T, hidden, ffn, til
     H = torch.zeros((T * 2, ffn), dtype=torch.float16 if dt == F16 else torch.bfloat16,
                     device="cuda:0")
     fm.fm_moe_gather_gemm_act(dev16(inp["X"], dt), _i32(inp["topk_ids"]), dev16(inp["W1"], dt),
-                              H, sp, off, e0, act)
+                              H, sp, off, e0, act, fm.moe_workspace(T, 2, hidden, nl))
     torch.cuda.synchronize()
     rows = int(roff[-1])
     assert np.array_equal(off.cpu().numpy(), roff)
@@ -137,10 +143,11 @@ def test_moe_layer0_no_activation_is_plain():
         off = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
         H = torch.zeros((T * 2, ffn), dtype=torch.bfloat16, device="cuda:0")
         args = (dev16(inp["X"], BF16), _i32(inp["topk_ids"]), dev16(inp["W1"], BF16), H, sp, off, 0)
+        ws = fm.moe_workspace(T, 2, hidden, nl)
         if fn == "plain":
-            fm.fm_moe_gather_gemm(*args)
+            fm.fm_moe_gather_gemm(*args, ws)
         else:
-            fm.fm_moe_gather_gemm_act(*args, fm.FM_ACT_NONE)
+            fm.fm_moe_gather_gemm_act(*args, fm.FM_ACT_NONE, ws)
         torch.cuda.synchronize()
         outs.append(bits16(H))
     assert np.array_equal(outs[0], outs[1])
@@ -218,11 +225,14 @@ def test_moe_combine_deterministic(oracle, T, hidden, ffn, E, nl, topk):
     W2 = dev16(inp["W2"], BF16)
     wts = devf32(inp["topk_weights"])
     outs = []
+    ws = fm.moe_workspace(T, topk, hidden, nl)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
     for _ in range(3):
         out = devf32(inp["out_seed"])
-        fm.fm_moe_gemm_scatter(Hd, W2, sp, off, wts, out)
+        fm.fm_moe_gemm_scatter(Hd, W2, sp, off, wts, out, ws, err_word=err)
         torch.cuda.synchronize()
         outs.append(out.cpu().numpy())
+    assert err.item() == 0
     assert all(np.array_equal(outs[0].view(np.uint32), o.view(np.uint32)) for o in outs[1:])
     ref = oracle.moe_layer1(BF16, Hb, inp["W2"], inp["topk_ids"], inp["topk_weights"], rsp, roff,
                             inp["out_seed"], 0)
@@ -252,7 +262,7 @@ def test_moe_gather_split_tail_bit_identical(oracle, monkeypatch, T, ffn):
         H = torch.zeros((T * 2, ffn), dtype=torch.bfloat16, device="cuda:0")
         sp = torch.full((T * 2,), -1, dtype=torch.int32, device="cuda:0")
         off = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
-        fm.fm_moe_gather_gemm(X, ids, W1, H, sp, off, 0)
+        fm.fm_moe_gather_gemm(X, ids, W1, H, sp, off, 0, fm.moe_workspace(T, 2, hidden, nl))
         torch.cuda.synchronize()
         outs.append(H)
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), "split changed H"
@@ -276,8 +286,11 @@ def test_moe_nothing_local_leaves_buffers():
     sp = torch.full((T * 2,), -1, dtype=torch.int32, device="cuda:0")
     off = torch.full((nl + 1,), 99, dtype=torch.int32, device="cuda:0")
     out = devf32(inp["out_seed"])
-    fm.fm_moe_gather_gemm(dev16(inp["X"], BF16), _i32(ids), dev16(inp["W1"], BF16), H, sp, off, 0)
-    fm.fm_moe_gemm_scatter(H, dev16(inp["W2"], BF16), sp, off, devf32(inp["topk_weights"]), out)
+    ws = fm.moe_workspace(T, 2, hidden, nl)
+    fm.fm_moe_gather_gemm(dev16(inp["X"], BF16), _i32(ids), dev16(inp["W1"], BF16), H, sp, off, 0,
+                          ws)
+    fm.fm_moe_gemm_scatter(H, dev16(inp["W2"], BF16), sp, off, devf32(inp["topk_weights"]), out,
+                           ws)
     torch.cuda.synchronize()
     assert off.cpu().numpy().tolist() == [0] * (nl + 1)
     assert bool((H.float() == 7.0).all()) and bool((sp == -1).all())
@@ -318,8 +331,10 @@ def _moe_ag_run(arr, inp, e0, nl, order, epoch, dt=BF16, spin=0, hint=None, **pu
     off = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
     arr.err.zero_()
     arr.push(order, epoch, **push_kw)
+    hidden = inp["X"].shape[1]
     fm.fm_moe_ag_gather_gemm(arr.X, _i32(ids), dev16(inp["W1"], dt), H, sp, off, e0, arr.flags,
-                             epoch, arr.n, order=hint, err_word=arr.err, spin_limit=spin)
+                             epoch, arr.n, fm.moe_workspace(T, topk, hidden, nl), order=hint,
+                             err_word=arr.err, spin_limit=spin)
     arr.join()
     torch.cuda.synchronize()
     return off.cpu().numpy(), sp.cpu().numpy(), H
@@ -358,7 +373,7 @@ def test_moe_ag_gather_random_arrival(oracle, monkeypatch, T, n, delay, hint):
     sp2 = torch.full_like(torch.from_numpy(sp).to("cuda:0"), -1)
     off2 = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
     fm.fm_moe_gather_gemm(arr.X, _i32(inp["topk_ids"]), dev16(inp["W1"], BF16), H2, sp2, off2,
-                          e0)
+                          e0, fm.moe_workspace(T, 2, hidden, nl))
     torch.cuda.synchronize()
     assert torch.equal(H[:rows].view(torch.int16), H2[:rows].view(torch.int16))
 
@@ -388,7 +403,8 @@ def test_moe_ag_f16_layouts(oracle, T, n, topk, nl, e0):
     H2 = torch.zeros_like(H)
     sp2 = torch.full((T * topk,), -1, dtype=torch.int32, device="cuda:0")
     off2 = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
-    fm.fm_moe_gather_gemm(arr.X, _i32(inp["topk_ids"]), dev16(inp["W1"], F16), H2, sp2, off2, e0)
+    fm.fm_moe_gather_gemm(arr.X, _i32(inp["topk_ids"]), dev16(inp["W1"], F16), H2, sp2, off2, e0,
+                          fm.moe_workspace(T, topk, hidden, nl))
     torch.cuda.synchronize()
     assert torch.equal(H[:rows].view(torch.int16), H2[:rows].view(torch.int16))
 
@@ -427,9 +443,12 @@ def test_moe_layer_end_to_end(oracle):
     off, sp, H = _moe_ag_run(arr, inp, e0, nl, order, arr.next_epoch(), hint=order.tolist())
     assert arr.err.item() == 0
     out = devf32(inp["out_seed"])
+    err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
     fm.fm_moe_gemm_scatter(H, dev16(inp["W2"], BF16), _i32(sp), _i32(off),
-                           devf32(inp["topk_weights"]), out)
+                           devf32(inp["topk_weights"]), out, fm.moe_workspace(T, 2, hidden, nl),
+                           err_word=err)
     torch.cuda.synchronize()
+    assert err.item() == 0
     roff, rsp = oracle.moe_route(inp["topk_ids"], e0, nl)
     assert np.array_equal(off, roff)
     Href = oracle.moe_ag_layer0(BF16, list(chunks), inp["W1"], rsp, roff, 2, arrival=order)
@@ -460,7 +479,8 @@ def _moe_prod_run(inp, chunks, e0, nl, order, local, n_prod, dt=BF16, counters=N
         counters = torch.zeros(n, dtype=torch.int32, device="cuda:0")
     err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
     fm.fm_moe_ag_gather_gemm_producers(src, X, _i32(inp["topk_ids"]), dev16(inp["W1"], dt), H,
-                                       sp, off, e0, flags, counters, 7, order=order,
+                                       sp, off, e0, flags, counters, 7,
+                                       fm.moe_workspace(T, topk, hidden, nl), order=order,
                                        n_producers=n_prod, err_word=err)
     torch.cuda.synchronize()
     assert err.item() == 0
@@ -491,7 +511,8 @@ def test_moe_ag_producers(oracle, T, n, n_prod, local):
     H2 = torch.zeros_like(H)
     sp2 = torch.full_like(H2[:, 0], 0, dtype=torch.int32)
     off2 = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
-    fm.fm_moe_gather_gemm(X, _i32(inp["topk_ids"]), dev16(inp["W1"], BF16), H2, sp2, off2, e0)
+    fm.fm_moe_gather_gemm(X, _i32(inp["topk_ids"]), dev16(inp["W1"], BF16), H2, sp2, off2, e0,
+                          fm.moe_workspace(T, 2, hidden, nl))
     torch.cuda.synchronize()
     assert torch.equal(H[:rows].view(torch.int16), H2[:rows].view(torch.int16))
 
@@ -523,7 +544,8 @@ def test_full_moe_ag_producers_rank0(oracle):
     H2 = torch.zeros_like(H)
     sp2 = torch.full((c["T"] * 2,), -1, dtype=torch.int32, device="cuda:0")
     off2 = torch.zeros(c["n_local"] + 1, dtype=torch.int32, device="cuda:0")
-    fm.fm_moe_gather_gemm(X, _i32(inp["topk_ids"]), dev16(inp["W1"], BF16), H2, sp2, off2, e0)
+    fm.fm_moe_gather_gemm(X, _i32(inp["topk_ids"]), dev16(inp["W1"], BF16), H2, sp2, off2, e0,
+                          fm.moe_workspace(c["T"], 2, c["hidden"], c["n_local"]))
     torch.cuda.synchronize()
     assert torch.equal(H[:rows].view(torch.int16), H2[:rows].view(torch.int16))
     _, _, H3, _ = _moe_prod_run(inp, chunks, e0, c["n_local"], list(range(n)), (0,), 0,
@@ -553,7 +575,8 @@ def _moe_pull_run(inp, chunks, e0, nl, order, times_ns, dt=BF16, spin=0, signal=
     fm.fm_chunk_signal_paced(flags, times_ns, 5, order=order if signal is None else signal,
                              stream=side)
     fm.fm_moe_ag_gather_gemm_pull(src, _i32(inp["topk_ids"]), dev16(inp["W1"], dt), H, sp, off,
-                                  e0, flags, 5, order=order, err_word=err, spin_limit=spin)
+                                  e0, flags, 5, fm.moe_workspace(T, topk, hidden, nl),
+                                  order=order, err_word=err, spin_limit=spin)
     cs.wait_stream(side)
     torch.cuda.synchronize()
     return off.cpu().numpy(), sp.cpu().numpy(), H, err.item()
@@ -583,7 +606,7 @@ def test_moe_ag_pull(oracle, T, n, gap_us):
     sp2 = torch.full((T * 2,), -1, dtype=torch.int32, device="cuda:0")
     off2 = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
     fm.fm_moe_gather_gemm(dev16(inp["X"], BF16), _i32(inp["topk_ids"]), dev16(inp["W1"], BF16),
-                          H2, sp2, off2, e0)
+                          H2, sp2, off2, e0, fm.moe_workspace(T, 2, hidden, nl))
     torch.cuda.synchronize()
     assert torch.equal(H[:rows].view(torch.int16), H2[:rows].view(torch.int16))
 
@@ -655,7 +678,7 @@ def test_full_moe_ag_pull_link_paced(oracle):
     sp2 = torch.full((c["T"] * 2,), -1, dtype=torch.int32, device="cuda:0")
     off2 = torch.zeros(c["n_local"] + 1, dtype=torch.int32, device="cuda:0")
     fm.fm_moe_gather_gemm(dev16(inp["X"], BF16), _i32(inp["topk_ids"]), dev16(inp["W1"], BF16),
-                          H2, sp2, off2, e0)
+                          H2, sp2, off2, e0, fm.moe_workspace(c["T"], 2, c["hidden"], c["n_local"]))
     torch.cuda.synchronize()
     assert torch.equal(H[:rows].view(torch.int16), H2[:rows].view(torch.int16))
 
@@ -703,6 +726,6 @@ def test_full_moe_ag_rank0(oracle):
     sp2 = torch.full((c["T"] * 2,), -1, dtype=torch.int32, device="cuda:0")
     off2 = torch.zeros(c["n_local"] + 1, dtype=torch.int32, device="cuda:0")
     fm.fm_moe_gather_gemm(arr.X, _i32(inp["topk_ids"]), dev16(inp["W1"], BF16), H2, sp2, off2,
-                          e0)
+                          e0, fm.moe_workspace(c["T"], 2, c["hidden"], c["n_local"]))
     torch.cuda.synchronize()
     assert torch.equal(H[:rows].view(torch.int16), H2[:rows].view(torch.int16))

@@ -9,6 +9,8 @@ import pytest
 
 import tile_gemm_communication_amd as fm
 
+pytestmark = pytest.mark.usefixtures("built_library")
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
@@ -95,35 +97,71 @@ def test_gemm_rs_validation():
     assert L.fm_gemm_rs(0, 256, 64, 64, 4, 0, P, P2, None, 0, None) == fm.FM_ERR_INVALID_ARG
 
 
+# a fake workspace: aligned, and reported large enough for the small shapes
+WS = ctypes.c_void_p(0x800000)
+WS_BYTES = 1 << 24
+
+
 def test_moe_validation():
     L = fm.lib()
-    assert L.fm_moe_route(16, 2, 0, 65, P, P2, P3, None) == fm.FM_ERR_INVALID_ARG
-    assert L.fm_moe_route(16, 0, 0, 8, P, P2, P3, None) == fm.FM_ERR_INVALID_ARG
-    assert L.fm_moe_route(16, 2, 0, 8, P, P2, None, None) == fm.FM_ERR_INVALID_ARG
-    assert L.fm_moe_gather_gemm(2, 16, 64, 64, 2, 0, 8, P, P, P, P, P, P, None) == \
-        fm.FM_ERR_UNSUPPORTED
-    assert L.fm_moe_gather_gemm(1, 16, 60, 64, 2, 0, 8, P, P, P, P, P, P, None) == \
-        fm.FM_ERR_INVALID_ARG
+    assert L.fm_moe_route(16, 2, 0, 65, P, P2, P3, WS, WS_BYTES, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_moe_route(16, 0, 0, 8, P, P2, P3, WS, WS_BYTES, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_moe_route(16, 2, 0, 8, P, P2, None, WS, WS_BYTES, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_moe_gather_gemm(2, 16, 64, 64, 2, 0, 8, P, P, P, P, P, P, WS, WS_BYTES,
+                                None) == fm.FM_ERR_UNSUPPORTED
+    assert L.fm_moe_gather_gemm(1, 16, 60, 64, 2, 0, 8, P, P, P, P, P, P, WS, WS_BYTES,
+                                None) == fm.FM_ERR_INVALID_ARG
     # the activation is checked first; a valid one still meets the dtype check
     for bad_act in (-1, 4, 100):
         assert L.fm_moe_gather_gemm_act(1, 16, 64, 64, 2, 0, 8, P, P, P, P, P, P, bad_act,
-                                        None) == fm.FM_ERR_INVALID_ARG
+                                        WS, WS_BYTES, None) == fm.FM_ERR_INVALID_ARG
     for act in (fm.FM_ACT_NONE, fm.FM_ACT_RELU, fm.FM_ACT_GELU_TANH, fm.FM_ACT_SILU):
         assert L.fm_moe_gather_gemm_act(2, 16, 64, 64, 2, 0, 8, P, P, P, P, P, P, act,
-                                        None) == fm.FM_ERR_UNSUPPORTED
-    assert L.fm_moe_gemm_scatter(1, 16, 64, 64, 2, 8, ODD, P, P, P, P, P3, None) == \
-        fm.FM_ERR_INVALID_ARG
-    assert L.fm_moe_gemm_scatter(1, 16, 64, 64, 2, 0, P, P, P, P, P, P3, None) == \
-        fm.FM_ERR_INVALID_ARG
+                                        WS, WS_BYTES, None) == fm.FM_ERR_UNSUPPORTED
+    assert L.fm_moe_gemm_scatter(1, 16, 64, 64, 2, 8, ODD, P, P, P, P, P3, None, 0, WS,
+                                 WS_BYTES, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_moe_gemm_scatter(1, 16, 64, 64, 2, 0, P, P, P, P, P, P3, None, 0, WS,
+                                 WS_BYTES, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_moe_gemm_scatter(1, 16, 64, 64, 2, 8, P, P, P, P, P, P3, None, -1, WS,
+                                 WS_BYTES, None) == fm.FM_ERR_INVALID_ARG   # spin_limit < 0
 
 
-def test_combine_flag_capacity_limit():
-    """More (M-tile, N-tile) completion flags than the counter buffer holds
-    is refused before anything is allocated or launched."""
+def test_moe_workspace_size_query():
+    """The size query grows with the tokens and the hidden size, covers the
+    fixed regions, and rejects out-of-range arguments with 0."""
     L = fm.lib()
-    # 2^20 rows -> 4104 M-tiles (with 8 ragged experts) x 16 N-tiles > 16384
-    assert L.fm_moe_gemm_scatter(1, 1 << 19, 4096, 8, 2, 8, P, P, P, P, P, P3, None) == \
-        fm.FM_ERR_UNSUPPORTED
+    q = L.fm_moe_workspace_bytes
+    small = q(16, 2, 64, 8)
+    assert small > 0 and small % 256 == 0
+    assert q(16384, 2, 4096, 8) > q(1024, 2, 4096, 8) > small
+    assert q(16384, 2, 4096, 8) > q(16384, 2, 1024, 8)
+    assert q(16384, 4, 4096, 8) > q(16384, 2, 4096, 8)
+    assert q(16384, 2, 4096, 64) > q(16384, 2, 4096, 8)
+    # the EP=8 workload: fixed regions (control, sink, route histograms) plus
+    # one flag per (128-row tile, 128-column tile) of up to 32768 + 8 x 128 rows
+    assert q(16384, 2, 4096, 8) >= 4 * (16704 + (256 + 8) * 32)
+    for bad in [(-1, 2, 64, 8), (16, 0, 64, 8), (16, 2, -8, 8), (16, 2, 64, 0), (16, 2, 64, 65)]:
+        assert q(*bad) == 0, bad
+    assert fm.fm_moe_workspace_bytes(16, 2, 64, 8) == small
+
+
+def test_moe_workspace_too_small_or_missing():
+    """A missing, misaligned or too small workspace is refused before any
+    launch, by the route, every layer-0 form and the combine."""
+    L = fm.lib()
+    T, topk, hidden, ffn, nl = 1024, 2, 512, 256, 8
+    need = L.fm_moe_workspace_bytes(T, topk, hidden, nl)
+    route_need = 4 * (320 + 16384)          # the route uses the fixed regions only
+    odd_ws = ctypes.c_void_p(0x800008)
+    for ws, nb in [(None, need), (odd_ws, need), (WS, route_need - 4)]:
+        assert L.fm_moe_route(T, topk, 0, nl, P, P2, P3, ws, nb, None) == fm.FM_ERR_INVALID_ARG
+        assert L.fm_moe_gather_gemm(1, T, hidden, ffn, topk, 0, nl, P, P, P, P, P, P, ws, nb,
+                                    None) == fm.FM_ERR_INVALID_ARG
+        assert L.fm_moe_ag_gather_gemm(1, T, hidden, ffn, topk, 0, nl, P, P, P, P, P, P, 4, P3,
+                                       1, None, None, 0, ws, nb, None) == fm.FM_ERR_INVALID_ARG
+    for ws, nb in [(None, need), (odd_ws, need), (WS, need - 256), (WS, route_need)]:
+        assert L.fm_moe_gemm_scatter(1, T, hidden, ffn, topk, nl, P, P, P, P, P, P3, None, 0,
+                                     ws, nb, None) == fm.FM_ERR_INVALID_ARG, (ws, nb)
 
 
 def test_chunk_push_validation():
@@ -200,7 +238,8 @@ def test_moe_ag_producers_validation():
 
     def call(n=4, src=src4, flags=P3, counters=P2, nprod=0, order=None):
         return L.fm_moe_ag_gather_gemm_producers(1, 64, 64, 64, 2, 0, 8, X, P, P, P, P, P, n, src,
-                                                 flags, counters, 1, order, nprod, None, 0, None)
+                                                 flags, counters, 1, order, nprod, None, 0, WS,
+                                                 WS_BYTES, None)
     assert call(src=None) == fm.FM_ERR_INVALID_ARG
     assert call(flags=None) == fm.FM_ERR_INVALID_ARG
     assert call(counters=None) == fm.FM_ERR_INVALID_ARG
@@ -218,7 +257,7 @@ def test_moe_ag_pull_validation():
 
     def call(n=4, chunks=ch4, flags=P3, order=None):
         return L.fm_moe_ag_gather_gemm_pull(1, 64, 64, 64, 2, 0, 8, chunks, P, P, P, P, P, n,
-                                            flags, 1, order, None, 0, None)
+                                            flags, 1, order, None, 0, WS, WS_BYTES, None)
     assert call(chunks=None) == fm.FM_ERR_INVALID_ARG
     assert call(flags=None) == fm.FM_ERR_INVALID_ARG
     assert call(n=3) == fm.FM_ERR_INVALID_ARG                          # T % n_chunks
@@ -255,7 +294,7 @@ def test_moe_ag_gather_validation():
     def call(n, flags, order=None, spin=0):
         o = None if order is None else ctypes.cast((ctypes.c_int32 * len(order))(*order),
                                                    ctypes.c_void_p)
-        return L.fm_moe_ag_gather_gemm(*args, n, flags, 1, o, None, spin, None)
+        return L.fm_moe_ag_gather_gemm(*args, n, flags, 1, o, None, spin, WS, WS_BYTES, None)
     assert call(4, None) == fm.FM_ERR_INVALID_ARG                 # flags required
     assert call(0, P3) == fm.FM_ERR_INVALID_ARG
     assert call(3, P3) == fm.FM_ERR_INVALID_ARG                   # T % n_chunks

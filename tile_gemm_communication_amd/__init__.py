@@ -22,7 +22,8 @@ FM_F16, FM_BF16, FM_F32 = 0, 1, 2
 
 EXPORTS = ("fm_version", "fm_status_str", "fm_gemm", "fm_ag_gemm", "fm_ag_gemm_pull", "fm_ag_gemm_producers",
            "fm_chunk_push", "fm_chunk_push_dma", "fm_chunk_signal_paced",
-           "fm_gemm_rs", "fm_moe_route", "fm_moe_gather_gemm", "fm_moe_gather_gemm_act",
+           "fm_gemm_rs", "fm_moe_workspace_bytes", "fm_moe_route", "fm_moe_gather_gemm",
+           "fm_moe_gather_gemm_act",
            "fm_moe_ag_gather_gemm",
            "fm_moe_ag_gather_gemm_producers", "fm_moe_ag_gather_gemm_pull",
            "fm_moe_gemm_scatter")
@@ -73,26 +74,30 @@ def lib() -> ctypes.CDLL:
     L.fm_chunk_push_dma.argtypes = [p, p, i64, p, u32, p]
     L.fm_gemm_rs.restype = ctypes.c_int
     L.fm_gemm_rs.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, p, p, p, i32, p]
+    sz = ctypes.c_size_t
+    L.fm_moe_workspace_bytes.restype = sz
+    L.fm_moe_workspace_bytes.argtypes = [i64, i32, i64, i32]
     L.fm_moe_route.restype = ctypes.c_int
-    L.fm_moe_route.argtypes = [i64, i32, i32, i32, p, p, p, p]
+    L.fm_moe_route.argtypes = [i64, i32, i32, i32, p, p, p, p, sz, p]
     L.fm_moe_gather_gemm.restype = ctypes.c_int
     L.fm_moe_gather_gemm.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32, p, p, p, p, p,
-                                     p, p]
+                                     p, p, sz, p]
     L.fm_moe_gather_gemm_act.restype = ctypes.c_int
     L.fm_moe_gather_gemm_act.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32, p, p, p, p,
-                                         p, p, ctypes.c_int, p]
+                                         p, p, ctypes.c_int, p, sz, p]
     L.fm_moe_ag_gather_gemm.restype = ctypes.c_int
     L.fm_moe_ag_gather_gemm.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32, p, p, p, p,
-                                        p, p, i32, p, u32, p, p, i64, p]
+                                        p, p, i32, p, u32, p, p, i64, p, sz, p]
     L.fm_moe_ag_gather_gemm_producers.restype = ctypes.c_int
     L.fm_moe_ag_gather_gemm_producers.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32, p,
                                                   p, p, p, p, p, i32, p, p, p, u32, p, i32, p,
-                                                  i64, p]
+                                                  i64, p, sz, p]
     L.fm_moe_ag_gather_gemm_pull.restype = ctypes.c_int
     L.fm_moe_ag_gather_gemm_pull.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32, p, p, p,
-                                             p, p, p, i32, p, u32, p, p, i64, p]
+                                             p, p, p, i32, p, u32, p, p, i64, p, sz, p]
     L.fm_moe_gemm_scatter.restype = ctypes.c_int
-    L.fm_moe_gemm_scatter.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, p, p, p, p, p, p, p]
+    L.fm_moe_gemm_scatter.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, p, p, p, p, p, p, p,
+                                      i64, p, sz, p]
     _lib = L
     return L
 
@@ -272,29 +277,52 @@ def fm_gemm_rs(A, W, dst, rank: int, atomic: bool = False, stream=None) -> None:
                                           _stream(stream)))
 
 
-def fm_moe_route(topk_ids, expert_begin: int, n_local: int, sorted_pairs, expert_offsets,
+def fm_moe_workspace_bytes(T: int, topk: int, hidden: int, n_local: int) -> int:
+    """Bytes of MoE workspace for T tokens, top-k, hidden size and local experts."""
+    return int(lib().fm_moe_workspace_bytes(int(T), int(topk), int(hidden), int(n_local)))
+
+
+def moe_workspace(T: int, topk: int, hidden: int, n_local: int, device="cuda:0"):
+    """A zero-filled uint8 device tensor of fm_moe_workspace_bytes bytes."""
+    torch = _torch()
+    n = fm_moe_workspace_bytes(T, topk, hidden, n_local)
+    if n <= 0:
+        raise ValueError("fm_moe_workspace_bytes: arguments out of range")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def _ws(ws):
+    """(pointer, bytes) of a workspace tensor."""
+    if ws is None:
+        return None, 0
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
+def fm_moe_route(topk_ids, expert_begin: int, n_local: int, sorted_pairs, expert_offsets, ws,
                  stream=None) -> None:
     T, topk = topk_ids.shape
+    wp, wn = _ws(ws)
     _check("fm_moe_route", lib().fm_moe_route(T, topk, int(expert_begin), int(n_local),
                                               _ptr(topk_ids), _ptr(sorted_pairs),
-                                              _ptr(expert_offsets), _stream(stream)))
+                                              _ptr(expert_offsets), wp, wn, _stream(stream)))
 
 
 def fm_moe_gather_gemm(X, topk_ids, W1, H, sorted_pairs, expert_offsets, expert_begin: int,
-                       stream=None) -> None:
+                       ws, stream=None) -> None:
     """Route, then H[rows of expert e] = X[gathered tokens] @ W1[e]."""
     T, hidden = X.shape
     n_local, h2, ffn = W1.shape
     topk = topk_ids.shape[1]
     if h2 != hidden or H.shape[1] != ffn or H.shape[0] < T * topk or W1.dtype != X.dtype:
         raise ValueError("fm_moe_gather_gemm: shape or dtype mismatch")
+    wp, wn = _ws(ws)
     _check("fm_moe_gather_gemm", lib().fm_moe_gather_gemm(
         _dt(X), T, hidden, ffn, topk, int(expert_begin), n_local, _ptr(X), _ptr(topk_ids),
-        _ptr(W1), _ptr(H), _ptr(sorted_pairs), _ptr(expert_offsets), _stream(stream)))
+        _ptr(W1), _ptr(H), _ptr(sorted_pairs), _ptr(expert_offsets), wp, wn, _stream(stream)))
 
 
 def fm_moe_gather_gemm_act(X, topk_ids, W1, H, sorted_pairs, expert_offsets, expert_begin: int,
-                           act: int, stream=None) -> None:
+                           act: int, ws, stream=None) -> None:
     """fm_moe_gather_gemm with act (FM_ACT_*) applied to the fp32 result
     before it is rounded into H."""
     T, hidden = X.shape
@@ -302,13 +330,15 @@ def fm_moe_gather_gemm_act(X, topk_ids, W1, H, sorted_pairs, expert_offsets, exp
     topk = topk_ids.shape[1]
     if h2 != hidden or H.shape[1] != ffn or H.shape[0] < T * topk or W1.dtype != X.dtype:
         raise ValueError("fm_moe_gather_gemm_act: shape or dtype mismatch")
+    wp, wn = _ws(ws)
     _check("fm_moe_gather_gemm_act", lib().fm_moe_gather_gemm_act(
         _dt(X), T, hidden, ffn, topk, int(expert_begin), n_local, _ptr(X), _ptr(topk_ids),
-        _ptr(W1), _ptr(H), _ptr(sorted_pairs), _ptr(expert_offsets), int(act), _stream(stream)))
+        _ptr(W1), _ptr(H), _ptr(sorted_pairs), _ptr(expert_offsets), int(act), wp, wn,
+        _stream(stream)))
 
 
 def fm_moe_ag_gather_gemm(X, topk_ids, W1, H, sorted_pairs, expert_offsets, expert_begin: int,
-                          flags, epoch: int, n_chunks: int, order=None, err_word=None,
+                          flags, epoch: int, n_chunks: int, ws, order=None, err_word=None,
                           spin_limit: int = 0, stream=None) -> None:
     """fm_moe_gather_gemm behind a token AllGather: token chunk c of X is read
     after flags[c] >= epoch; `order` is the expected arrival order."""
@@ -326,13 +356,13 @@ def fm_moe_ag_gather_gemm(X, topk_ids, W1, H, sorted_pairs, expert_offsets, expe
         _ptr(W1), _ptr(H), _ptr(sorted_pairs), _ptr(expert_offsets), int(n_chunks), _ptr(flags),
         ctypes.c_uint32(epoch & 0xFFFFFFFF),
         ctypes.cast(order_arr, ctypes.c_void_p) if order_arr is not None else None,
-        _ptr(err_word), int(spin_limit), _stream(stream)))
+        _ptr(err_word), int(spin_limit), *_ws(ws), _stream(stream)))
 
 
 def fm_moe_ag_gather_gemm_producers(src, X, topk_ids, W1, H, sorted_pairs, expert_offsets,
-                                    expert_begin: int, flags, counters, epoch: int, order=None,
-                                    n_producers: int = 0, err_word=None, spin_limit: int = 0,
-                                    stream=None) -> None:
+                                    expert_begin: int, flags, counters, epoch: int, ws,
+                                    order=None, n_producers: int = 0, err_word=None,
+                                    spin_limit: int = 0, stream=None) -> None:
     """fm_moe_ag_gather_gemm whose own producer workgroups copy token chunk c
     from src[c] (None: already in X) into X and publish flags[c] = epoch."""
     T, hidden = X.shape
@@ -351,12 +381,12 @@ def fm_moe_ag_gather_gemm_producers(src, X, topk_ids, W1, H, sorted_pairs, exper
         ctypes.cast(ptrs, ctypes.c_void_p), _ptr(flags), _ptr(counters),
         ctypes.c_uint32(epoch & 0xFFFFFFFF),
         ctypes.cast(o, ctypes.c_void_p) if o is not None else None, int(n_producers),
-        _ptr(err_word), int(spin_limit), _stream(stream)))
+        _ptr(err_word), int(spin_limit), *_ws(ws), _stream(stream)))
 
 
 def fm_moe_ag_gather_gemm_pull(chunks, topk_ids, W1, H, sorted_pairs, expert_offsets,
-                               expert_begin: int, flags, epoch: int, order=None, err_word=None,
-                               spin_limit: int = 0, stream=None) -> None:
+                               expert_begin: int, flags, epoch: int, ws, order=None,
+                               err_word=None, spin_limit: int = 0, stream=None) -> None:
     """MoE layer 0 reading token chunk c in place from chunks[c] after
     flags[c] >= epoch (no gathered buffer)."""
     n = len(chunks)
@@ -374,11 +404,11 @@ def fm_moe_ag_gather_gemm_pull(chunks, topk_ids, W1, H, sorted_pairs, expert_off
         ctypes.cast(ptrs, ctypes.c_void_p), _ptr(topk_ids), _ptr(W1), _ptr(H), _ptr(sorted_pairs),
         _ptr(expert_offsets), n, _ptr(flags), ctypes.c_uint32(epoch & 0xFFFFFFFF),
         ctypes.cast(o, ctypes.c_void_p) if o is not None else None, _ptr(err_word),
-        int(spin_limit), _stream(stream)))
+        int(spin_limit), *_ws(ws), _stream(stream)))
 
 
-def fm_moe_gemm_scatter(H, W2, sorted_pairs, expert_offsets, topk_weights, out,
-                        stream=None) -> None:
+def fm_moe_gemm_scatter(H, W2, sorted_pairs, expert_offsets, topk_weights, out, ws,
+                        err_word=None, spin_limit: int = 0, stream=None) -> None:
     """out[t] += sum_k w[t,k] * (H[row(t,k)] @ W2[e(t,k)]) over local pairs."""
     T, topk = topk_weights.shape
     n_local, ffn, hidden = W2.shape
@@ -386,4 +416,5 @@ def fm_moe_gemm_scatter(H, W2, sorted_pairs, expert_offsets, topk_weights, out,
         raise ValueError("fm_moe_gemm_scatter: shape or dtype mismatch")
     _check("fm_moe_gemm_scatter", lib().fm_moe_gemm_scatter(
         _dt(H), T, hidden, ffn, topk, n_local, _ptr(H), _ptr(W2), _ptr(sorted_pairs),
-        _ptr(expert_offsets), _ptr(topk_weights), _ptr(out), _stream(stream)))
+        _ptr(expert_offsets), _ptr(topk_weights), _ptr(out), _ptr(err_word), int(spin_limit),
+        *_ws(ws), _stream(stream)))

@@ -23,25 +23,6 @@ int device_cu_count() {
   return cached[dev];
 }
 
-uint32_t* device_tile_counters() {
-  static std::mutex mu;
-  static uint32_t* cached[64] = {nullptr};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!cached[dev]) {
-    void* p = nullptr;
-    if (hipMalloc(&p, kTileCounters * sizeof(uint32_t)) != hipSuccess) return nullptr;
-    if (hipMemset(p, 0, kTileCounters * sizeof(uint32_t)) != hipSuccess ||
-        hipDeviceSynchronize() != hipSuccess) {
-      (void)hipFree(p);
-      return nullptr;
-    }
-    cached[dev] = static_cast<uint32_t*>(p);
-  }
-  return cached[dev];
-}
-
 }  // namespace fm
 
 extern "C" int fm_version(void) { return 100; }

@@ -73,29 +73,6 @@ __device__ __forceinline__ void store_through(float* p, const f32x4& v) {
 // Device properties cached once per device (compute-unit count).
 int device_cu_count();
 
-// Per-device counter buffer of the MoE operators: kTileCounters uint32
-// words, zeroed when allocated on first use and kept until the process ends.
-// NULL if the allocation fails.
-constexpr int kTileCounters = 32768;
-uint32_t* device_tile_counters();
-// Layout, one region per user so that different operators may overlap in
-// time (calls of one operator on one device may not):
-constexpr int kColDone0 = 0, kColDoneN = 16384;            // combine tile flags (epochs)
-constexpr int kRoute0 = kColDoneN;                          // route chunk histograms
-// 1 KiB the combine's epilogue reads and writes in place of rows it does not
-// own (lanes past the last row or column), so that every wave issues the same
-// number of memory instructions per block.  Its contents are meaningless.
-constexpr int kEpSink0 = kTileCounters - 512;
-constexpr int kRouteN = kEpSink0 - kRoute0;
-// The combine's epoch lives on the device: each launch stamps its tile flags
-// with the stored epoch + 1, and its last workgroup to finish stores that
-// value back, so a launch replayed from a graph still gets a fresh epoch.
-constexpr int kCombineEpoch = kTileCounters - 2;
-constexpr int kCombineDone = kTileCounters - 1;             // finished workgroups
-static_assert(kRoute0 + kRouteN <= kEpSink0 && kEpSink0 + 256 <= kCombineEpoch &&
-                  (kEpSink0 * 4) % 16 == 0,
-              "counter regions overlap, or the sink is not 16-byte aligned");
-
 // Translate the last HIP launch error into a status.
 inline fm_status_t launch_status() {
   return hipGetLastError() == hipSuccess ? FM_OK : FM_ERR_HIP;

@@ -24,10 +24,52 @@ constexpr int kMaxMTiles = 1024;                      // token ranges cached in 
 constexpr int kMaxBands = 256;                        // bands ordered by arrival in LDS
 constexpr int kRouteThreads = 256;
 constexpr int kRouteWaves = kRouteThreads / 64;
-// Per-chunk expert counts live in the route region of the library's
-// tile-counter buffer.
-constexpr int kRouteScratch0 = kRoute0;
-constexpr int kRouteScratchN = kRouteN;
+
+// ---------------------------------------------------------------------------
+// Workspace of the MoE operators: caller-owned device memory, zero-filled once
+// before its first use; every call leaves it ready for the next.  Layout, in
+// uint32 words (every region at a fixed offset, so a workspace may serve
+// calls of different shapes one after another):
+//   [0, 64)       control words of the combine (below)
+//   [64, 320)     1 KiB the combine's epilogue reads and writes in place of
+//                 rows it does not own (lanes past the last row or column),
+//                 so that every wave issues the same number of memory
+//                 instructions per block; its contents are meaningless
+//   [320, +16384) route: per-chunk expert histograms of the counting sort
+//   [16704, ...)  combine: one completion epoch per (M-tile, N-tile)
+// The route region and the combine regions are disjoint: a route (or MoE
+// layer 0) and a combine may use one workspace at the same time; two routes,
+// or two combines, may not.
+// ---------------------------------------------------------------------------
+constexpr int kCtlEpoch = 0;     // the last combine launch's epoch
+constexpr int kCtlDone = 1;      // workgroups of the running combine that finished
+constexpr int kCtlTicket = 2;    // next tile ticket of the running combine
+constexpr int kCtlAbort = 3;     // = epoch once a wait of that launch gave up
+constexpr int64_t kWsSink = 64;
+constexpr int64_t kWsRoute = kWsSink + 256;
+constexpr int64_t kRouteWords = 16384;
+constexpr int64_t kWsFlags = kWsRoute + kRouteWords;
+constexpr int kMinTileEdge = 128;   // the smallest BM and BN of any combine tile
+static_assert((kWsSink * 4) % 16 == 0, "the sink must be 16-byte aligned");
+
+// Pairs per route workgroup: 2048, doubled until the per-chunk histograms fit
+// the route region.
+inline int64_t route_chunk_pairs(int64_t P, int n_local) {
+  int64_t ch = 2048;
+  while (std::max<int64_t>(1, cdiv(P, ch)) * n_local > kRouteWords) ch *= 2;
+  return ch;
+}
+
+// Completion flags the combine needs: one per (M-tile, N-tile) for the
+// smallest tile, with M-tiles <= pairs / BM + one partial tile per expert.
+inline int64_t combine_flag_words(int64_t pairs, int64_t hidden, int n_local) {
+  return (cdiv(pairs, kMinTileEdge) + n_local) * cdiv(hidden, kMinTileEdge);
+}
+
+inline size_t moe_ws_bytes(int64_t pairs, int64_t hidden, int n_local) {
+  const int64_t words = kWsFlags + combine_flag_words(pairs, hidden, n_local);
+  return (size_t)cdiv(words * 4, 256) * 256;
+}
 
 // ---------------------------------------------------------------------------
 // Route: a counting sort over chunks of `ch` consecutive pairs, one
@@ -134,7 +176,7 @@ struct MoeArgs {
   const int32_t* offsets;
   const float* weights;       // [T * topk] (layer 1)
   uint32_t* tile_done;        // layer 1: per (M-tile, N-tile) completion epoch
-  uint32_t* ctr;              // layer 1: the counter buffer (epoch and finish count)
+  uint32_t* ws;               // layer 1: the workspace (control words, sink)
   int64_t K, N;
   int64_t spin_limit;
   int topk, n_local, tiles_n, group_m;
@@ -190,13 +232,17 @@ __device__ __forceinline__ float apply_act(int act, float x) {
 // column tn whose token range overlaps that of global M-tile gm has published
 // this call's epoch, then acquire.  Beyond kMaxMTiles tiles the ranges are not
 // cached and every earlier tile of the column is waited for.
-__device__ __forceinline__ void wait_token_range(const MoeArgs& a, const int* s_tile0,
+// Returns false if the wait gave up: after spin_limit polls of one flag (this
+// thread then writes FM_ERR_TIMEOUT to err_word and marks the launch aborted
+// in the workspace), or once another workgroup has marked it aborted.
+__device__ __forceinline__ bool wait_token_range(const MoeArgs& a, const int* s_tile0,
                                                  const int* s_ftok, const int* s_ltok,
                                                  int total_m, int e, int gm, int tn,
                                                  uint32_t epoch) {
   const bool cached = total_m <= kMaxMTiles;
   const int lo_tok = cached ? s_ftok[gm] : 0;
   const int hi_tok = cached ? s_ltok[gm] : 0x7FFFFFFF;
+  uint32_t* const abort_word = a.ws + kCtlAbort;
   for (int ep = 0; ep < e; ++ep) {
     const int g0 = s_tile0[ep] / a.tiles_n, g1 = s_tile0[ep + 1] / a.tiles_n;
     int m = g0;
@@ -214,11 +260,44 @@ __device__ __forceinline__ void wait_token_range(const MoeArgs& a, const int* s_
       while (!flag_reached(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
                            epoch)) {
         __builtin_amdgcn_s_sleep(2);
-        if (++polls > a.spin_limit) break;   // safeguard only: see the deadlock note
+        ++polls;
+        if ((polls & 63) == 0 &&
+            __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch)
+          return false;
+        if (polls > a.spin_limit) {
+          if (a.err_word)
+            __hip_atomic_store(a.err_word, (int32_t)FM_ERR_TIMEOUT, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(abort_word, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          return false;
+        }
       }
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return true;
+}
+
+// Combine: the tile of ticket L.  Tickets count tiles in expert order (all
+// of expert 0's tiles, then expert 1's, ...), so a tile only ever waits for
+// tiles of smaller tickets.  Within one expert (whose tiles never wait for
+// each other) the tiles are permuted in windows of G tickets so that the
+// tickets an XCD takes together, which in the first round are those of
+// workgroups w, w+8, w+16, ..., cover a compact block of tiles (see
+// xcd_slot and band_coords).
+__device__ __forceinline__ void combine_tile(const MoeArgs& a, const int* s_off,
+                                             const int* s_tile0, int L, int G, int BM, int& e,
+                                             int& tm, int& tn) {
+  e = 0;
+  while (e + 1 < a.n_local && s_tile0[e + 1] <= L) ++e;
+  const int tiles_e = (int)cdiv(s_off[e + 1] - s_off[e], BM);
+  const int n_e = tiles_e * a.tiles_n;
+  const int i = L - s_tile0[e];
+  const int w0 = i - i % G;
+  const int wsz = min(G, n_e - w0);
+  const int r = i - w0;
+  const int j = w0 + ((wsz & 7) == 0 ? xcd_slot(r, wsz) : r);
+  band_coords(j, tiles_e, a.tiles_n, min(a.group_m, tiles_e), tm, tn);
 }
 
 template <class E, int BM, int BN, int NW, bool SCATTER, bool KTAIL, bool PULL = false,
@@ -244,6 +323,10 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   __shared__ int s_ftok[SCATTER ? kMaxMTiles : 1];
   __shared__ int s_ltok[SCATTER ? kMaxMTiles : 1];
   __shared__ int s_abort;
+  // combine: this tile has a row whose token also has the previous row (two
+  // pairs of one token in one expert), and the next ticket (by tile parity)
+  __shared__ int s_dup;
+  __shared__ int s_next[2];
   // token AllGather: bands of M-tiles sorted by the arrival of their chunks
   __shared__ int s_band0[SCATTER ? 1 : kMaxLocalExperts + 1];
   __shared__ uint8_t s_blvl[SCATTER ? 1 : kMaxBands];
@@ -264,11 +347,17 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   }
   const int t = threadIdx.x;
   const int gmb = SCATTER ? 1 : a.ag_group;
-  // Combine: this launch's epoch (never 0, the flags' initial value).
+  // Combine: this launch's epoch (never 0, the flags' initial value), and
+  // the first tile ticket.
   uint32_t epoch = 0;
   if constexpr (SCATTER) {
-    epoch = __hip_atomic_load(a.ctr + kCombineEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+    epoch = __hip_atomic_load(a.ws + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
     if (epoch == 0) epoch = 1;
+    if (t == 0) {
+      s_next[1] = (int)__hip_atomic_fetch_add(a.ws + kCtlTicket, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+      s_dup = 0;
+    }
   }
   if (t <= a.n_local) s_off[t] = a.offsets[t];
   __syncthreads();
@@ -379,10 +468,16 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
     pending = -1;
   };
 
-  for (int L2 = slot; L2 < n_items; L2 += G) {
+  // Layer 0: static positions slot, slot + G, ...  Combine: tickets, one
+  // taken ahead (during the previous tile's K loop), so that a tile only ever
+  // waits for tiles that running workgroups hold.
+  int L2 = SCATTER ? s_next[1] : slot;
+  for (int it = 0; L2 < n_items; ++it) {
     const int L = pos0 + L2 / sub_n, sub = L2 % sub_n;
     int e = 0, tm, tn;
-    if (by_arrival) {
+    if constexpr (SCATTER) {
+      combine_tile(a, s_off, s_tile0, L, G, BM, e, tm, tn);
+    } else if (by_arrival) {
       int lo = 0, hi = n_bands - 1;   // last band starting at or before L
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -404,7 +499,10 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
     const int rows_e = s_off[e + 1] - row_base;
     const int m0 = tm * BM;
     const int64_t n0 = ((int64_t)tn * sub_n + sub) * BN;
-    if (n0 >= N) continue;   // the right half of an edge tile that lies past N
+    if (!SCATTER && n0 >= N) {   // the right half of an edge tile that lies past N
+      L2 += G;
+      continue;
+    }
 
     if constexpr (!SCATTER) {
       if (a.flags) {
@@ -446,12 +544,23 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
     eng.set_b(a.W + (int64_t)e * K * N * 2, N * 2, n0, N);
     // Combine: fetch each tile row's pair id now, so that the load overlaps
     // the K loop (the K loop's first wait drains it with the stage-0 DMA).
-    int my_p = -1;
+    int my_p = -1, prev_p = -1;
+    uint32_t next_ticket = 0;
     if constexpr (SCATTER) {
-      if (t < BM && m0 + t < rows_e) my_p = a.sorted_pairs[row_base + m0 + t];
+      if (t < BM && m0 + t < rows_e) {
+        my_p = a.sorted_pairs[row_base + m0 + t];
+        if (m0 + t > 0) prev_p = a.sorted_pairs[row_base + m0 + t - 1];
+      }
     }
     eng.run([&] {
-      if constexpr (SCATTER) publish();
+      if constexpr (SCATTER) {
+        publish();
+        // the next ticket, taken now and kept in a register until the
+        // epilogue (its return drains with the K loop's first wait)
+        if (t == 0)
+          next_ticket = __hip_atomic_fetch_add(a.ws + kCtlTicket, 1u, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+      }
     });
 
     // Epilogue through the LDS staging regions (whole-line global accesses).
@@ -464,18 +573,32 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       // (count per column, in expert order).  The adds are plain fp32 loads
       // and stores, in a fixed order: the combine is deterministic.
       // Row metadata into LDS (token, gate weight; token -1 past the rows).
+      // Rows of an expert are sorted by pair id, so two pairs of one token in
+      // one expert (an input the combine does not accept) are neighbours.
+      if (t == 0) s_next[it & 1] = (int)next_ticket;
       if (t < BM) {
         s_tok[t] = my_p >= 0 ? my_p / a.topk : -1;
         s_wt[t] = my_p >= 0 ? a.weights[my_p] : 0.f;
+        if (my_p >= 0 && prev_p >= 0 && my_p / a.topk == prev_p / a.topk) s_dup = 1;
       }
       // Wait for the tiles of earlier experts in this N column whose token
       // ranges overlap this tile's: they hold every earlier contribution to
       // this tile's tokens, and are usually long finished (each expert walks
       // its tokens in order, about one expert's worth of tiles earlier).
       const int gm = s_tile0[e] / a.tiles_n + tm;   // this tile's global M-tile
-      if (e > 0 && t == 0)
-        wait_token_range(a, s_tile0, s_ftok, s_ltok, total_m, e, gm, tn, epoch);
+      if (t == 0)
+        s_abort = (e > 0 && !wait_token_range(a, s_tile0, s_ftok, s_ltok, total_m, e, gm, tn,
+                                               epoch))
+                      ? 1
+                      : 0;
       __syncthreads();
+      // A wait that gave up ends this workgroup's work (err_word is set, out
+      // is undefined); a duplicated token skips the tile's adds and is
+      // reported, and its flag still goes out.
+      const bool skip = s_abort != 0 || s_dup != 0;
+      if (t == 0 && s_dup && a.err_word)
+        __hip_atomic_store(a.err_word, (int32_t)FM_ERR_INVALID_ARG, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       // Per wave and 32-row block i: the destination rows come into LDS by
       // DMA, the accumulators are staged, and weight * row is added and
       // stored through.  Block i+1's rows are requested before block i's
@@ -490,9 +613,9 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       constexpr int H = Eng::EP_READS / 2;
       const int col = eng.ep_col();
       const bool col_ok = n0 + col < N;
-      float* const sink = reinterpret_cast<float*>(a.ctr + kEpSink0) + 4 * (t & 63);
+      float* const sink = reinterpret_cast<float*>(a.ws + kWsSink) + 4 * (t & 63);
       const int row_w = m0 + eng.ep_row0();
-      const int live = (n0 + eng.ep_col0() < N && row_w < rows_e)
+      const int live = (!skip && n0 + eng.ep_col0() < N && row_w < rows_e)
                            ? min(Eng::FM, (int)cdiv(rows_e - row_w, 32))
                            : 0;
       // destinations of half h of block i (the token reads go out together)
@@ -560,7 +683,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       // The tile's flag goes out once every wave's stores have completed:
       // at the next tile's first K-step wait (which drains them while that
       // tile's first stage loads), or after the last tile.
-      pending = (int)(gm * a.tiles_n + tn);
+      if (s_abort == 0) pending = (int)(gm * a.tiles_n + tn);
     } else {
       // H rows in expert-sorted order, 16-bit.
       const int col = eng.ep_col();
@@ -592,6 +715,13 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       });
     }
     eng.ep_end();
+    if constexpr (SCATTER) {
+      if (s_abort) break;
+      if (t == 0) s_dup = 0;   // read by every thread before ep_end's barrier
+      L2 = s_next[it & 1];
+    } else {
+      L2 += G;
+    }
   }
   if constexpr (SCATTER) {
     if (pending >= 0) {
@@ -599,18 +729,20 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       __syncthreads();
       publish();
     }
-    // Every workgroup checks in once its tiles are done; the last one resets
-    // the count and stores this launch's epoch for the next launch.  Relaxed:
-    // only the next launch reads these words, after the kernel boundary (a
-    // release here would write back this XCD's L2 once per workgroup).
+    // Every workgroup checks in once its tiles are done (or abandoned); the
+    // last one resets the count and the ticket counter (every ticket fetch
+    // has returned by then) and stores this launch's epoch for the next
+    // launch.  Relaxed: only the next launch reads these words, after the
+    // kernel boundary (a release here would write back this XCD's L2 once
+    // per workgroup).
     __syncthreads();
     if (t == 0) {
-      const uint32_t prev = __hip_atomic_fetch_add(a.ctr + kCombineDone, 1u, __ATOMIC_RELAXED,
+      const uint32_t prev = __hip_atomic_fetch_add(a.ws + kCtlDone, 1u, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
       if (prev == (uint32_t)G - 1) {
-        __hip_atomic_store(a.ctr + kCombineDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(a.ctr + kCombineEpoch, epoch, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.ws + kCtlDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.ws + kCtlTicket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.ws + kCtlEpoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -678,7 +810,6 @@ template <bool SCATTER>
 fm_status_t launch_moe(fm_dtype_t dt, MoeTile cfg, MoeArgs& a, hipStream_t stream) {
   a.tiles_n = (int)cdiv(a.N, cfg.bn);
   a.group_m = 8;
-  a.spin_limit = 1ll << 26;
   a.g_ref = device_cu_count();
   const char* env = std::getenv("FM_SPLIT_TAIL");
   // (no split with producer workgroups: producers and consumers share one launch)
@@ -687,14 +818,7 @@ fm_status_t launch_moe(fm_dtype_t dt, MoeTile cfg, MoeArgs& a, hipStream_t strea
                 ? 1
                 : 0;
   a.part = 0;
-  if (SCATTER) {
-    // one completion flag per (M-tile, N-tile); M-tiles <= pairs/BM + experts
-    const int64_t m_tiles = cdiv(a.rows_cap, (int64_t)cfg.bm) + a.n_local;
-    if (m_tiles * a.tiles_n > kColDoneN) return FM_ERR_UNSUPPORTED;
-    a.ctr = device_tile_counters();
-    if (!a.ctr) return FM_ERR_HIP;
-    a.tile_done = a.ctr + kColDone0;
-  }
+  if (SCATTER) a.tile_done = a.ws + kWsFlags;   // sized for the smallest tile
   auto launch_part = [&](MoeTile c) {
     if constexpr (SCATTER) {
       launch_moe_part<true>(dt, c, a, stream);
@@ -712,9 +836,20 @@ fm_status_t launch_moe(fm_dtype_t dt, MoeTile cfg, MoeArgs& a, hipStream_t strea
   return launch_status();
 }
 
+// Grid of the combine: one workgroup per CU.  Its tiles are handed out by
+// ticket, so any grid size is correct; FM_COMBINE_GRID (1..4096) overrides the
+// size, which the tests use to run more workgroups than can be resident.
+int combine_grid() {
+  if (const char* env = std::getenv("FM_COMBINE_GRID")) {
+    const int g = std::atoi(env);
+    if (g >= 1 && g <= 4096) return g;
+  }
+  return device_cu_count();
+}
+
 template <bool SCATTER, bool PULL, bool ACT>
 void launch_moe_part(fm_dtype_t dt, MoeTile cfg, const MoeArgs& a, hipStream_t stream) {
-  const dim3 grid(device_cu_count());
+  const dim3 grid(SCATTER ? combine_grid() : device_cu_count());
 #define FM_LAUNCH(E, BM, BN, NW)                                                              \
   do {                                                                                        \
     if (a.K % kBK) /* ragged K: the 4-wave form keeps the tail path spill-free */             \
@@ -740,10 +875,13 @@ void launch_moe_part(fm_dtype_t dt, MoeTile cfg, const MoeArgs& a, hipStream_t s
 }
 
 fm_status_t check_route_args(int64_t T, int32_t topk, int32_t n_local, const int32_t* topk_ids,
-                             const int32_t* sorted_pairs, const int32_t* expert_offsets) {
+                             const int32_t* sorted_pairs, const int32_t* expert_offsets,
+                             const void* ws, size_t ws_bytes) {
   if (T < 0 || topk < 1 || n_local < 1 || n_local > kMaxLocalExperts) return FM_ERR_INVALID_ARG;
   if (T * topk >= (1ll << 31)) return FM_ERR_UNSUPPORTED;
   if (!expert_offsets || (T > 0 && (!topk_ids || !sorted_pairs))) return FM_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws) || ws_bytes < (size_t)(kWsRoute + kRouteWords) * 4)
+    return FM_ERR_INVALID_ARG;
   return FM_OK;
 }
 
@@ -752,20 +890,23 @@ fm_status_t check_route_args(int64_t T, int32_t topk, int32_t n_local, const int
 
 using namespace fm;
 
+extern "C" size_t fm_moe_workspace_bytes(int64_t T, int32_t topk, int64_t hidden,
+                                         int32_t n_local) {
+  if (T < 0 || topk < 1 || hidden < 0 || n_local < 1 || n_local > kMaxLocalExperts) return 0;
+  return moe_ws_bytes(T * topk, hidden, n_local);
+}
+
 extern "C" fm_status_t fm_moe_route(int64_t T, int32_t topk, int32_t expert_begin,
                                     int32_t n_local, const int32_t* topk_ids,
-                                    int32_t* sorted_pairs, int32_t* expert_offsets,
-                                    hipStream_t stream) {
-  const fm_status_t st =
-      check_route_args(T, topk, n_local, topk_ids, sorted_pairs, expert_offsets);
+                                    int32_t* sorted_pairs, int32_t* expert_offsets, void* ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+  const fm_status_t st = check_route_args(T, topk, n_local, topk_ids, sorted_pairs,
+                                          expert_offsets, ws, ws_bytes);
   if (st != FM_OK) return st;
   const int64_t P = T * topk;
-  int64_t ch = 2048;   // pairs per workgroup; the chunk histograms must fit the scratch
-  while (std::max<int64_t>(1, cdiv(P, ch)) * n_local > kRouteScratchN) ch *= 2;
+  const int64_t ch = route_chunk_pairs(P, n_local);
   const int n_chunks = (int)std::max<int64_t>(1, cdiv(P, ch));
-  uint32_t* counts = device_tile_counters();
-  if (!counts) return FM_ERR_HIP;
-  counts += kRouteScratch0;
+  uint32_t* counts = static_cast<uint32_t*>(ws) + kWsRoute;
   hipLaunchKernelGGL(route_count_kernel, dim3(n_chunks), dim3(kRouteThreads), 0, stream,
                      topk_ids, P, (int)expert_begin, (int)n_local, ch, counts);
   hipLaunchKernelGGL(route_place_kernel, dim3(n_chunks), dim3(kRouteThreads), 0, stream,
@@ -782,12 +923,14 @@ fm_status_t moe_gather_impl(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ff
                             const int32_t* topk_ids, const void* W1, void* H,
                             int32_t* sorted_pairs, int32_t* expert_offsets, int32_t n_chunks,
                             const uint32_t* flags, uint32_t epoch, const int32_t* order,
-                            int32_t* err_word, int64_t spin_limit, hipStream_t stream,
+                            int32_t* err_word, int64_t spin_limit, void* ws, size_t ws_bytes,
+                            hipStream_t stream,
                             const void* const* src = nullptr, uint32_t* counters = nullptr,
                             int32_t n_producers = 0, const void* const* pull = nullptr,
                             int act = FM_ACT_NONE) {
   if (dt != FM_F16 && dt != FM_BF16) return FM_ERR_UNSUPPORTED;
-  fm_status_t st = check_route_args(T, topk, n_local, topk_ids, sorted_pairs, expert_offsets);
+  fm_status_t st = check_route_args(T, topk, n_local, topk_ids, sorted_pairs, expert_offsets,
+                                    ws, ws_bytes);
   if (st != FM_OK) return st;
   if (hidden < 0 || ffn < 0 || hidden % 8 || ffn % 8) return FM_ERR_INVALID_ARG;
   // pull mode reads the chunks in place: no gathered X
@@ -830,8 +973,8 @@ fm_status_t moe_gather_impl(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ff
   // gathered-row byte offsets are 32-bit
   if (hidden >= (1ll << 22) || ffn >= (1ll << 22) || T * hidden >= (1ll << 31))
     return FM_ERR_UNSUPPORTED;
-  st = fm_moe_route(T, topk, expert_begin, n_local, topk_ids, sorted_pairs, expert_offsets,
-                    stream);
+  st = fm_moe_route(T, topk, expert_begin, n_local, topk_ids, sorted_pairs, expert_offsets, ws,
+                    ws_bytes, stream);
   if (st != FM_OK || T == 0 || ffn == 0) return st;
   MoeArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -873,10 +1016,10 @@ extern "C" fm_status_t fm_moe_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidd
                                           int32_t n_local, const void* X,
                                           const int32_t* topk_ids, const void* W1, void* H,
                                           int32_t* sorted_pairs, int32_t* expert_offsets,
-                                          hipStream_t stream) {
+                                          void* ws, size_t ws_bytes, hipStream_t stream) {
   return moe_gather_impl(dt, T, hidden, ffn, topk, expert_begin, n_local, X, topk_ids, W1, H,
-                         sorted_pairs, expert_offsets, 0, nullptr, 0, nullptr, nullptr, 0,
-                         stream);
+                         sorted_pairs, expert_offsets, 0, nullptr, 0, nullptr, nullptr, 0, ws,
+                         ws_bytes, stream);
 }
 
 extern "C" fm_status_t fm_moe_gather_gemm_act(fm_dtype_t dt, int64_t T, int64_t hidden,
@@ -884,11 +1027,12 @@ extern "C" fm_status_t fm_moe_gather_gemm_act(fm_dtype_t dt, int64_t T, int64_t 
                                               int32_t n_local, const void* X,
                                               const int32_t* topk_ids, const void* W1, void* H,
                                               int32_t* sorted_pairs, int32_t* expert_offsets,
-                                              fm_act_t act, hipStream_t stream) {
+                                              fm_act_t act, void* ws, size_t ws_bytes,
+                                              hipStream_t stream) {
   if ((int)act < FM_ACT_NONE || (int)act > FM_ACT_SILU) return FM_ERR_INVALID_ARG;
   return moe_gather_impl(dt, T, hidden, ffn, topk, expert_begin, n_local, X, topk_ids, W1, H,
-                         sorted_pairs, expert_offsets, 0, nullptr, 0, nullptr, nullptr, 0,
-                         stream, nullptr, nullptr, 0, nullptr, (int)act);
+                         sorted_pairs, expert_offsets, 0, nullptr, 0, nullptr, nullptr, 0, ws,
+                         ws_bytes, stream, nullptr, nullptr, 0, nullptr, (int)act);
 }
 
 extern "C" fm_status_t fm_moe_ag_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidden,
@@ -898,12 +1042,12 @@ extern "C" fm_status_t fm_moe_ag_gather_gemm(fm_dtype_t dt, int64_t T, int64_t h
                                              int32_t* sorted_pairs, int32_t* expert_offsets,
                                              int32_t n_chunks, const uint32_t* flags,
                                              uint32_t epoch, const int32_t* order,
-                                             int32_t* err_word, int64_t spin_limit,
-                                             hipStream_t stream) {
+                                             int32_t* err_word, int64_t spin_limit, void* ws,
+                                             size_t ws_bytes, hipStream_t stream) {
   if (!flags) return FM_ERR_INVALID_ARG;
   return moe_gather_impl(dt, T, hidden, ffn, topk, expert_begin, n_local, X, topk_ids, W1, H,
                          sorted_pairs, expert_offsets, n_chunks, flags, epoch, order, err_word,
-                         spin_limit, stream);
+                         spin_limit, ws, ws_bytes, stream);
 }
 
 extern "C" fm_status_t fm_moe_ag_gather_gemm_producers(
@@ -911,23 +1055,24 @@ extern "C" fm_status_t fm_moe_ag_gather_gemm_producers(
     int32_t n_local, void* X, const int32_t* topk_ids, const void* W1, void* H,
     int32_t* sorted_pairs, int32_t* expert_offsets, int32_t n_chunks, const void* const* src,
     uint32_t* flags, uint32_t* counters, uint32_t epoch, const int32_t* order,
-    int32_t n_producers, int32_t* err_word, int64_t spin_limit, hipStream_t stream) {
+    int32_t n_producers, int32_t* err_word, int64_t spin_limit, void* ws, size_t ws_bytes,
+    hipStream_t stream) {
   if (!flags || !src) return FM_ERR_INVALID_ARG;
   return moe_gather_impl(dt, T, hidden, ffn, topk, expert_begin, n_local, X, topk_ids, W1, H,
                          sorted_pairs, expert_offsets, n_chunks, flags, epoch, order, err_word,
-                         spin_limit, stream, src, counters, n_producers);
+                         spin_limit, ws, ws_bytes, stream, src, counters, n_producers);
 }
 
 extern "C" fm_status_t fm_moe_ag_gather_gemm_pull(
     fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn, int32_t topk, int32_t expert_begin,
     int32_t n_local, const void* const* chunks, const int32_t* topk_ids, const void* W1, void* H,
     int32_t* sorted_pairs, int32_t* expert_offsets, int32_t n_chunks, const uint32_t* flags,
-    uint32_t epoch, const int32_t* order, int32_t* err_word, int64_t spin_limit,
-    hipStream_t stream) {
+    uint32_t epoch, const int32_t* order, int32_t* err_word, int64_t spin_limit, void* ws,
+    size_t ws_bytes, hipStream_t stream) {
   if (!flags || !chunks) return FM_ERR_INVALID_ARG;
   return moe_gather_impl(dt, T, hidden, ffn, topk, expert_begin, n_local, nullptr, topk_ids, W1,
                          H, sorted_pairs, expert_offsets, n_chunks, flags, epoch, order,
-                         err_word, spin_limit, stream, nullptr, nullptr, 0, chunks);
+                         err_word, spin_limit, ws, ws_bytes, stream, nullptr, nullptr, 0, chunks);
 }
 
 extern "C" fm_status_t fm_moe_gemm_scatter(fm_dtype_t dt, int64_t T, int64_t hidden,
@@ -936,11 +1081,14 @@ extern "C" fm_status_t fm_moe_gemm_scatter(fm_dtype_t dt, int64_t T, int64_t hid
                                            const int32_t* sorted_pairs,
                                            const int32_t* expert_offsets,
                                            const float* topk_weights, float* out,
-                                           hipStream_t stream) {
+                                           int32_t* err_word, int64_t spin_limit, void* ws,
+                                           size_t ws_bytes, hipStream_t stream) {
   if (dt != FM_F16 && dt != FM_BF16) return FM_ERR_UNSUPPORTED;
   if (T < 0 || topk < 1 || n_local < 1 || n_local > kMaxLocalExperts) return FM_ERR_INVALID_ARG;
-  if (hidden < 0 || ffn < 0 || hidden % 8 || ffn % 8) return FM_ERR_INVALID_ARG;
-  if (!expert_offsets) return FM_ERR_INVALID_ARG;
+  if (hidden < 0 || ffn < 0 || hidden % 8 || ffn % 8 || spin_limit < 0) return FM_ERR_INVALID_ARG;
+  if (!expert_offsets || !ws || !aligned16(ws) ||
+      ws_bytes < moe_ws_bytes(T * topk, hidden, n_local))
+    return FM_ERR_INVALID_ARG;
   if (T == 0 || hidden == 0) return FM_OK;
   if (!H || !W2 || !sorted_pairs || !topk_weights || !out || !aligned16(H) || !aligned16(W2) ||
       !aligned16(out))
@@ -960,5 +1108,8 @@ extern "C" fm_status_t fm_moe_gemm_scatter(fm_dtype_t dt, int64_t T, int64_t hid
   a.topk = topk;
   a.rows_cap = T * topk;
   a.n_local = n_local;
+  a.ws = static_cast<uint32_t*>(ws);
+  a.err_word = err_word;
+  a.spin_limit = spin_limit ? spin_limit : (1ll << 24);
   return launch_moe<true>(dt, moe_tile(true), a, stream);
 }
