@@ -309,3 +309,34 @@ def test_split_tail_bit_identical(oracle, monkeypatch, extra_tiles, K):
     rows, cols = sample_coords(M, N, 2000, seed=5, tile=(256, 128))
     assert_close(_at(C1, rows, cols), oracle.gemm_entries(F16, A, B, rows, cols),
                  "split tail samples")
+
+
+def test_more_row_tiles_than_the_ordered_table(oracle):
+    """65792 rows: 514 row tiles of the chosen 128-row tile, more than the
+    256 entries of the M-tile order table, so the AllGather-GEMM and the
+    GEMM-ReduceScatter fall back to the plain row order.  Both element by
+    element against the oracle (the AllGather with a reversed arrival)."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    M, N, K, n, P = 65792, 64, 64, 4, 2
+    chunks, W, _ = wl.ag_inputs(n, M // n, N, K, F16, seed=65)
+    order = list(range(n))[::-1]
+    say(f"row tiles beyond the order table: {M}x{N}x{K}")
+    arr = Arrival(chunks, F16, K)
+    arr.poison()
+    C = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+    ep = arr.next_epoch()
+    arr.push(order, ep)
+    fm.fm_ag_gemm(arr.X, dev16(W, F16), C, arr.flags, ep, n, order=order, err_word=arr.err)
+    arr.join()
+    torch.cuda.synchronize()
+    assert arr.err.item() == 0
+    X = np.concatenate(list(chunks), axis=0)
+    assert_close(host64(C), oracle.gemm(F16, X, W), "ag beyond the order table")
+    A, W2, seeds = wl.rs_inputs(M, N, K, P, F16, seed=66)
+    dst = [devf32(s) for s in seeds]
+    fm.fm_gemm_rs(dev16(A, F16), dev16(W2, F16), dst, rank=1)
+    torch.cuda.synchronize()
+    ref = oracle.gemm_rs(F16, A, W2, list(seeds))
+    for r in range(P):
+        assert_close(host64(dst[r]) - seeds[r], ref[r] - seeds[r], f"rs slice {r}")

@@ -170,16 +170,19 @@ def test_moe_one_hot_expert(oracle):
 
 def test_full_moe_rank0(oracle):
     """EP=8 rank 0: 16384 tokens x 4096, 64 experts top-2 (log-Zipf bias), 8
-    local experts, ffn 2816, bf16.  Routing bit-exact; layer 0 on sampled rows;
-    layer 1 on sampled tokens fed by the oracle's own layer 0."""
+    local experts, ffn 2816, bf16, chained on the GPU: layer 0, then the
+    combine on the GPU's own H.  Routing bit-exact; layer 0 on sampled rows;
+    the combine on every token of each expert's first and last row tile, at
+    least 100 tokens with both pairs local and random tokens (over 512 in
+    all), against the oracle's combine run on the GPU's H bits."""
     import torch
     c = wl.MOE_EP8
     say("full moe EP=8 rank 0")
     inp = wl.moe_inputs(c["T"], c["hidden"], c["ffn"], c["n_experts"], c["n_local"], c["topk"],
                         BF16, seed=c["seed"], zipf_s=c["zipf_s"])
-    e0 = c["rank"] * c["n_local"]
-    roff, rsp = oracle.moe_route(inp["topk_ids"], e0, c["n_local"])
-    off, sp, H, out = _moe_run(inp, e0, c["n_local"], BF16)
+    e0, nl = c["rank"] * c["n_local"], c["n_local"]
+    roff, rsp = oracle.moe_route(inp["topk_ids"], e0, nl)
+    off, sp, H, out = _moe_run(inp, e0, nl, BF16)
     rows = int(roff[-1])
     assert np.array_equal(off, roff) and np.array_equal(sp[:rows], rsp)
     rng = np.random.default_rng(7)
@@ -188,17 +191,24 @@ def test_full_moe_rank0(oracle):
     Hs = oracle.moe_layer0_rows(BF16, inp["X"], inp["W1"], rsp, roff, 2, srows)
     idx = torch.from_numpy(srows).to("cuda:0")
     assert_close(host64(H[idx]), Hs, "full layer0 rows")
-    # End-to-end tokens: every local row of each sampled token comes from the
-    # oracle's layer 0 (rounded to bf16), then the oracle's combine.
-    toks = np.unique(rng.integers(0, c["T"], 24))
-    pos = {int(p): r for r, p in enumerate(rsp)}
-    need = sorted({pos[t * 2 + k] for t in toks for k in range(2) if (t * 2 + k) in pos})
-    Hfull = np.zeros((rows, c["ffn"]), dtype=np.uint16)
-    if need:
-        Hfull[need] = oracle.round_bf16(
-            oracle.moe_layer0_rows(BF16, inp["X"], inp["W1"], rsp, roff, 2, np.array(need)))
-    ref = oracle.moe_layer1_tokens(BF16, Hfull, inp["W2"], inp["topk_ids"], inp["topk_weights"],
-                                   rsp, roff, inp["out_seed"], e0, toks)
+    # tokens of every expert's first and last 256-row tile
+    edge = []
+    for e in range(nl):
+        r0, r1 = int(roff[e]), int(roff[e + 1])
+        if r1 > r0:
+            last0 = r0 + (r1 - r0 - 1) // 256 * 256
+            edge.append(rsp[r0:min(r0 + 256, r1)] // 2)
+            edge.append(rsp[last0:r1] // 2)
+    ids = inp["topk_ids"]
+    local = (ids >= e0) & (ids < e0 + nl)
+    both = np.nonzero(local.all(axis=1))[0]
+    toks = np.unique(np.concatenate(edge + [rng.choice(both, 128, replace=False),
+                                            rng.integers(0, c["T"], 64)]))
+    assert toks.size >= 512 and np.isin(toks, both).sum() >= 100
+    say(f"full moe combine: {toks.size} tokens checked")
+    Hbits = H[:rows].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = oracle.moe_layer1_tokens(BF16, Hbits, inp["W2"], ids, inp["topk_weights"], rsp, roff,
+                                   inp["out_seed"], e0, toks)
     tidx = torch.from_numpy(toks).to("cuda:0")
     assert_close(host64(out[tidx]) - inp["out_seed"][toks], ref - inp["out_seed"][toks],
                  "full combine tokens")
