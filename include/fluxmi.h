@@ -469,6 +469,32 @@ fm_status_t fm_moe_gemm_scatter(fm_dtype_t dt, int64_t T, int64_t hidden, int64_
                                 int64_t spin_limit, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
 
+/*
+ * fm_moe_gemm_scatter_noalloc -- fm_moe_gemm_scatter for callers that cannot
+ * allocate or own a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid device allocation).  The combine's control
+ * words and completion flags live in a static device array of the library,
+ * 256 KiB per GPU, held until the process ends (its address is looked up, and
+ * the array zero-filled by a kernel on `stream`, on the first call on each
+ * GPU); the call itself allocates nothing.
+ *   Arguments, results and errors as fm_moe_gemm_scatter without (ws,
+ *   ws_bytes); the result is bit-identical to it.
+ *   Limit: (ceil(T*topk/128) + n_local) * ceil(hidden/128) <= 65216, else
+ *   FM_ERR_UNSUPPORTED (the EP=8 workload, T = 16384, top-2, hidden 4096,
+ *   8 local experts, needs 8448).  FM_ERR_HIP if the array's address cannot
+ *   be obtained.
+ *   Every call on one GPU shares that GPU's array: calls that overlap in time
+ *   on one GPU (two streams) race and give undefined results; issue them on
+ *   one stream, or order the streams.
+ */
+fm_status_t fm_moe_gemm_scatter_noalloc(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn,
+                                        int32_t topk, int32_t n_local, const void* H,
+                                        const void* W2, const int32_t* sorted_pairs,
+                                        const int32_t* expert_offsets,
+                                        const float* topk_weights, float* out,
+                                        int32_t* err_word, int64_t spin_limit,
+                                        hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -311,3 +311,18 @@ def test_oracle_is_not_reachable_from_the_product():
             if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
                 txt = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "import oracle" not in txt and "fm_oracle" not in txt, f
+
+
+def test_noalloc_combine_limit_and_validation():
+    """The no-alloc combine refuses shapes beyond its static scratch and
+    invalid arguments before touching the GPU."""
+    L = fm.lib()
+    # (2^20/128 + 8) x 32 column tiles: beyond the 65216 flags of the scratch
+    assert L.fm_moe_gemm_scatter_noalloc(1, 1 << 19, 4096, 8, 2, 8, P, P, P, P, P, P3, None, 0,
+                                         None) == fm.FM_ERR_UNSUPPORTED
+    assert L.fm_moe_gemm_scatter_noalloc(1, 16, 64, 64, 2, 8, ODD, P, P, P, P, P3, None, 0,
+                                         None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_moe_gemm_scatter_noalloc(0, 16, 64, 60, 2, 8, P, P, P, P, P, P3, None, 0,
+                                         None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_moe_gemm_scatter_noalloc(2, 16, 64, 64, 2, 8, P, P, P, P, P, P3, None, 0,
+                                         None) == fm.FM_ERR_UNSUPPORTED

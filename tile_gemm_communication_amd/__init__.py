@@ -26,7 +26,7 @@ EXPORTS = ("fm_version", "fm_status_str", "fm_gemm", "fm_ag_gemm", "fm_ag_gemm_p
            "fm_moe_gather_gemm_act",
            "fm_moe_ag_gather_gemm",
            "fm_moe_ag_gather_gemm_producers", "fm_moe_ag_gather_gemm_pull",
-           "fm_moe_gemm_scatter")
+           "fm_moe_gemm_scatter", "fm_moe_gemm_scatter_noalloc")
 
 # fm_act_t: activation of MoE layer 0's result (fm_moe_gather_gemm_act)
 FM_ACT_NONE, FM_ACT_RELU, FM_ACT_GELU_TANH, FM_ACT_SILU = 0, 1, 2, 3
@@ -98,6 +98,9 @@ def lib() -> ctypes.CDLL:
     L.fm_moe_gemm_scatter.restype = ctypes.c_int
     L.fm_moe_gemm_scatter.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, p, p, p, p, p, p, p,
                                       i64, p, sz, p]
+    L.fm_moe_gemm_scatter_noalloc.restype = ctypes.c_int
+    L.fm_moe_gemm_scatter_noalloc.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, p, p, p, p,
+                                              p, p, p, i64, p]
     _lib = L
     return L
 
@@ -418,3 +421,17 @@ def fm_moe_gemm_scatter(H, W2, sorted_pairs, expert_offsets, topk_weights, out, 
         _dt(H), T, hidden, ffn, topk, n_local, _ptr(H), _ptr(W2), _ptr(sorted_pairs),
         _ptr(expert_offsets), _ptr(topk_weights), _ptr(out), _ptr(err_word), int(spin_limit),
         *_ws(ws), _stream(stream)))
+
+
+def fm_moe_gemm_scatter_noalloc(H, W2, sorted_pairs, expert_offsets, topk_weights, out,
+                                err_word=None, spin_limit: int = 0, stream=None) -> None:
+    """fm_moe_gemm_scatter with the library's static per-GPU scratch instead of
+    a workspace (for callers that cannot allocate)."""
+    T, topk = topk_weights.shape
+    n_local, ffn, hidden = W2.shape
+    if H.shape[1] != ffn or tuple(out.shape) != (T, hidden) or W2.dtype != H.dtype:
+        raise ValueError("fm_moe_gemm_scatter_noalloc: shape or dtype mismatch")
+    _check("fm_moe_gemm_scatter_noalloc", lib().fm_moe_gemm_scatter_noalloc(
+        _dt(H), T, hidden, ffn, topk, n_local, _ptr(H), _ptr(W2), _ptr(sorted_pairs),
+        _ptr(expert_offsets), _ptr(topk_weights), _ptr(out), _ptr(err_word), int(spin_limit),
+        _stream(stream)))

@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "fm_sched.hpp"
 #include "fm_tile.hpp"
@@ -818,7 +819,6 @@ fm_status_t launch_moe(fm_dtype_t dt, MoeTile cfg, MoeArgs& a, hipStream_t strea
                 ? 1
                 : 0;
   a.part = 0;
-  if (SCATTER) a.tile_done = a.ws + kWsFlags;   // sized for the smallest tile
   auto launch_part = [&](MoeTile c) {
     if constexpr (SCATTER) {
       launch_moe_part<true>(dt, c, a, stream);
@@ -1075,26 +1075,69 @@ extern "C" fm_status_t fm_moe_ag_gather_gemm_pull(
                          err_word, spin_limit, ws, ws_bytes, stream, nullptr, nullptr, 0, chunks);
 }
 
-extern "C" fm_status_t fm_moe_gemm_scatter(fm_dtype_t dt, int64_t T, int64_t hidden,
-                                           int64_t ffn, int32_t topk, int32_t n_local,
-                                           const void* H, const void* W2,
-                                           const int32_t* sorted_pairs,
-                                           const int32_t* expert_offsets,
-                                           const float* topk_weights, float* out,
-                                           int32_t* err_word, int64_t spin_limit, void* ws,
-                                           size_t ws_bytes, hipStream_t stream) {
+namespace fm {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Scratch of fm_moe_gemm_scatter_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  Layout as the workspace's control
+// words and sink ([0, 320)), then the completion flags.  Host code never uses
+// the array's name as an address: the per-device address comes from
+// hipGetSymbolAddress.
+// ---------------------------------------------------------------------------
+constexpr int64_t kNoAllocWords = 65536;                 // 256 KiB
+constexpr int64_t kNoAllocFlags0 = kWsRoute;             // flags follow the sink
+static __device__ __align__(256) uint32_t scratch[kNoAllocWords];
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0u;
+}
+
+// The device address of this device's `scratch`, looked up (and the array
+// zero-filled on `stream`, by a kernel) on the first call on each device;
+// nullptr if the lookup fails.
+uint32_t* noalloc_scratch(hipStream_t stream) {
+  static std::mutex mu;
+  static uint32_t* addr[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(64), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(p), kNoAllocWords);
+    if (hipGetLastError() != hipSuccess) return nullptr;
+    addr[dev] = static_cast<uint32_t*>(p);
+  }
+  return addr[dev];
+}
+
+// Arguments of the combine, shared by both entry points.
+fm_status_t check_combine_args(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn,
+                               int32_t topk, int32_t n_local, const void* H, const void* W2,
+                               const int32_t* sorted_pairs, const int32_t* expert_offsets,
+                               const float* topk_weights, float* out, int64_t spin_limit) {
   if (dt != FM_F16 && dt != FM_BF16) return FM_ERR_UNSUPPORTED;
   if (T < 0 || topk < 1 || n_local < 1 || n_local > kMaxLocalExperts) return FM_ERR_INVALID_ARG;
   if (hidden < 0 || ffn < 0 || hidden % 8 || ffn % 8 || spin_limit < 0) return FM_ERR_INVALID_ARG;
-  if (!expert_offsets || !ws || !aligned16(ws) ||
-      ws_bytes < moe_ws_bytes(T * topk, hidden, n_local))
-    return FM_ERR_INVALID_ARG;
+  if (!expert_offsets) return FM_ERR_INVALID_ARG;
   if (T == 0 || hidden == 0) return FM_OK;
   if (!H || !W2 || !sorted_pairs || !topk_weights || !out || !aligned16(H) || !aligned16(W2) ||
       !aligned16(out))
     return FM_ERR_INVALID_ARG;
   if (hidden >= (1ll << 22) || ffn >= (1ll << 22) || T * topk * ffn >= (1ll << 31))
     return FM_ERR_UNSUPPORTED;
+  return FM_OK;
+}
+
+fm_status_t launch_combine(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn, int32_t topk,
+                           int32_t n_local, const void* H, const void* W2,
+                           const int32_t* sorted_pairs, const int32_t* expert_offsets,
+                           const float* topk_weights, float* out, int32_t* err_word,
+                           int64_t spin_limit, uint32_t* ctl, uint32_t* flags,
+                           hipStream_t stream) {
   MoeArgs a;
   std::memset(&a, 0, sizeof(a));
   a.A = (const char*)H;
@@ -1108,8 +1151,53 @@ extern "C" fm_status_t fm_moe_gemm_scatter(fm_dtype_t dt, int64_t T, int64_t hid
   a.topk = topk;
   a.rows_cap = T * topk;
   a.n_local = n_local;
-  a.ws = static_cast<uint32_t*>(ws);
+  a.ws = ctl;
+  a.tile_done = flags;   // sized for the smallest tile
   a.err_word = err_word;
   a.spin_limit = spin_limit ? spin_limit : (1ll << 24);
   return launch_moe<true>(dt, moe_tile(true), a, stream);
+}
+
+}  // namespace
+}  // namespace fm
+
+extern "C" fm_status_t fm_moe_gemm_scatter_noalloc(fm_dtype_t dt, int64_t T, int64_t hidden,
+                                                   int64_t ffn, int32_t topk, int32_t n_local,
+                                                   const void* H, const void* W2,
+                                                   const int32_t* sorted_pairs,
+                                                   const int32_t* expert_offsets,
+                                                   const float* topk_weights, float* out,
+                                                   int32_t* err_word, int64_t spin_limit,
+                                                   hipStream_t stream) {
+  const fm_status_t st = check_combine_args(dt, T, hidden, ffn, topk, n_local, H, W2,
+                                            sorted_pairs, expert_offsets, topk_weights, out,
+                                            spin_limit);
+  if (st != FM_OK || T == 0 || hidden == 0) return st;
+  if (kNoAllocFlags0 + combine_flag_words(T * topk, hidden, n_local) > kNoAllocWords)
+    return FM_ERR_UNSUPPORTED;
+  uint32_t* ctl = noalloc_scratch(stream);
+  if (!ctl) return FM_ERR_HIP;
+  return launch_combine(dt, T, hidden, ffn, topk, n_local, H, W2, sorted_pairs, expert_offsets,
+                        topk_weights, out, err_word, spin_limit, ctl, ctl + kNoAllocFlags0,
+                        stream);
+}
+
+extern "C" fm_status_t fm_moe_gemm_scatter(fm_dtype_t dt, int64_t T, int64_t hidden,
+                                           int64_t ffn, int32_t topk, int32_t n_local,
+                                           const void* H, const void* W2,
+                                           const int32_t* sorted_pairs,
+                                           const int32_t* expert_offsets,
+                                           const float* topk_weights, float* out,
+                                           int32_t* err_word, int64_t spin_limit, void* ws,
+                                           size_t ws_bytes, hipStream_t stream) {
+  const fm_status_t st = check_combine_args(dt, T, hidden, ffn, topk, n_local, H, W2,
+                                            sorted_pairs, expert_offsets, topk_weights, out,
+                                            spin_limit);
+  if (st != FM_OK) return st;
+  if (!ws || !aligned16(ws) || ws_bytes < moe_ws_bytes(T * topk, hidden, n_local))
+    return FM_ERR_INVALID_ARG;
+  if (T == 0 || hidden == 0) return FM_OK;
+  uint32_t* w = static_cast<uint32_t*>(ws);
+  return launch_combine(dt, T, hidden, ffn, topk, n_local, H, W2, sorted_pairs, expert_offsets,
+                        topk_weights, out, err_word, spin_limit, w, w + kWsFlags, stream);
 }
