@@ -90,6 +90,9 @@ def parse():
     ap.add_argument("--arrival", choices=("kernel", "dma"), default="kernel",
                     help="emulated peer push: fm_chunk_push (copy kernel) or "
                          "fm_chunk_push_dma (copy engines, no compute units)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only run the register-only MFMA loop (fm_probe_mfma) in each form "
+                         "and print its TFLOP/s and the shader clock it held")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run fm_chunk_push over MIB MiB three times and exit: the "
                          "known-size copy that calibrates the HBM byte counters")
@@ -557,6 +560,53 @@ def copy_probe(mib):
                       "dispatches": 3}), flush=True)
 
 
+def mfma_ceiling():
+    """The matrix-core rate with no memory traffic (fm_probe_mfma): bf16 and
+    fp16, the 32x32x16 and 16x16x32 forms, one and two waves per SIMD,
+    N(0,1)-like and all-zero operands.  Each form runs ~0.2 s after a warm-up
+    launch; the clock is the median over workgroups of shader cycles per
+    100 MHz tick."""
+    import torch
+
+    import tile_gemm_communication_amd as fm
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.zeros(4 * cus, dtype=torch.int64, device="cuda:0")
+    rows = []
+    for dt in (torch.bfloat16, torch.float16):
+        for mf16 in (False, True):
+            for waves in (1, 2):
+                for zero in (False, True):
+                    flop_per = (16384 if mf16 else 32768) * 8
+                    per_iter = cus * 4 * waves * flop_per
+                    iters = 2000
+                    fm.fm_probe_mfma(dt, mf16, waves, iters, zero, out)   # warm-up
+                    torch.cuda.synchronize()
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    fm.fm_probe_mfma(dt, mf16, waves, iters, zero, out)
+                    b.record()
+                    torch.cuda.synchronize()
+                    ms = a.elapsed_time(b)
+                    iters = max(1, int(iters * 200.0 / max(ms, 1e-3)))   # ~0.2 s
+                    a.record()
+                    fm.fm_probe_mfma(dt, mf16, waves, iters, zero, out)
+                    b.record()
+                    torch.cuda.synchronize()
+                    ms = a.elapsed_time(b)
+                    o = out.view(cus, 4).cpu().numpy()
+                    ghz = float(sorted(o[:, 0] / o[:, 1])[cus // 2]) * 0.1
+                    tf = per_iter * iters / (ms * 1e-3) / 1e12
+                    rows.append({"dtype": "bf16" if dt == torch.bfloat16 else "f16",
+                                 "mfma": "16x16x32" if mf16 else "32x32x16",
+                                 "waves_per_simd": waves, "operands": "zero" if zero else "N(0,1)",
+                                 "tflops": round(tf, 1), "clock_ghz": round(ghz, 3),
+                                 "frac_of_2516.6": round(tf / PEAK_TFLOPS, 4),
+                                 "frac_at_clock": round(tf / (cus * 4096 * ghz * 1e-3), 4)})
+                    log(f"mfma ceiling {rows[-1]}")
+    print(json.dumps({"mfma_ceiling": rows}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -571,6 +621,9 @@ def main():
     log(f"libfluxmi {fm.version()} on {torch.cuda.get_device_name(0)}")
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.mfma_ceiling:
+        mfma_ceiling()
         return
     w = Workload()
     w.serial_arrival = args.serial_arrival

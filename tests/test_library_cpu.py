@@ -15,9 +15,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared():
-    src = open(os.path.join(ROOT, "include", "fluxmi.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(fm_[a-z0-9_]+)\s*\(", src)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", h)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(fm_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -326,3 +330,17 @@ def test_noalloc_combine_limit_and_validation():
                                          None) == fm.FM_ERR_INVALID_ARG
     assert L.fm_moe_gemm_scatter_noalloc(2, 16, 64, 64, 2, 8, P, P, P, P, P, P3, None, 0,
                                          None) == fm.FM_ERR_UNSUPPORTED
+
+
+def test_probe_validation():
+    L = fm.lib()
+    out = ctypes.c_void_p(0x40000)
+    n = 1 << 16
+    assert L.fm_probe_mfma(2, 0, 1, 10, 0, out, n, None) == fm.FM_ERR_UNSUPPORTED
+    assert L.fm_probe_mfma(1, 2, 1, 10, 0, out, n, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_probe_mfma(1, 0, 3, 10, 0, out, n, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_probe_mfma(1, 0, 1, 0, 0, out, n, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_probe_mfma(1, 0, 1, 10, 0, None, n, None) == fm.FM_ERR_INVALID_ARG
+    assert L.fm_probe_mfma(1, 0, 1, 10, 0, ctypes.c_void_p(0x40004), n, None) == \
+        fm.FM_ERR_INVALID_ARG
+    assert L.fm_probe_mfma(1, 0, 1, 10, 0, out, 4, None) == fm.FM_ERR_INVALID_ARG   # too small

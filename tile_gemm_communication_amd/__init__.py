@@ -26,7 +26,7 @@ EXPORTS = ("fm_version", "fm_status_str", "fm_gemm", "fm_ag_gemm", "fm_ag_gemm_p
            "fm_moe_gather_gemm_act",
            "fm_moe_ag_gather_gemm",
            "fm_moe_ag_gather_gemm_producers", "fm_moe_ag_gather_gemm_pull",
-           "fm_moe_gemm_scatter", "fm_moe_gemm_scatter_noalloc")
+           "fm_moe_gemm_scatter", "fm_moe_gemm_scatter_noalloc", "fm_probe_mfma")
 
 # fm_act_t: activation of MoE layer 0's result (fm_moe_gather_gemm_act)
 FM_ACT_NONE, FM_ACT_RELU, FM_ACT_GELU_TANH, FM_ACT_SILU = 0, 1, 2, 3
@@ -98,6 +98,8 @@ def lib() -> ctypes.CDLL:
     L.fm_moe_gemm_scatter.restype = ctypes.c_int
     L.fm_moe_gemm_scatter.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, p, p, p, p, p, p, p,
                                       i64, p, sz, p]
+    L.fm_probe_mfma.restype = ctypes.c_int
+    L.fm_probe_mfma.argtypes = [ctypes.c_int, i32, i32, i64, i32, p, i64, p]
     L.fm_moe_gemm_scatter_noalloc.restype = ctypes.c_int
     L.fm_moe_gemm_scatter_noalloc.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, p, p, p, p,
                                               p, p, p, i64, p]
@@ -435,3 +437,15 @@ def fm_moe_gemm_scatter_noalloc(H, W2, sorted_pairs, expert_offsets, topk_weight
         _dt(H), T, hidden, ffn, topk, n_local, _ptr(H), _ptr(W2), _ptr(sorted_pairs),
         _ptr(expert_offsets), _ptr(topk_weights), _ptr(out), _ptr(err_word), int(spin_limit),
         _stream(stream)))
+
+
+def fm_probe_mfma(dtype, mfma16: bool, waves_per_simd: int, iters: int, zero: bool, out,
+                  stream=None) -> None:
+    """The register-only MFMA ceiling loop (include/fluxmi_probe.h); `out` is a
+    device int64 tensor of at least 4 x CU-count words."""
+    torch = _torch()
+    dt = FM_F16 if dtype == torch.float16 else FM_BF16
+    _check("fm_probe_mfma", lib().fm_probe_mfma(dt, int(bool(mfma16)), int(waves_per_simd),
+                                                int(iters), int(bool(zero)), _ptr(out),
+                                                out.numel() * out.element_size() // 8,
+                                                _stream(stream)))
