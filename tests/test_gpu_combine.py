@@ -252,4 +252,5 @@ def test_combine_and_layer0_beyond_the_cached_tile_ranges(oracle):
     arr.join()
     torch.cuda.synchronize()
     assert arr.err.item() == 0
+    assert np.array_equal(off2.cpu().numpy(), roff)
     assert torch.equal(H2[:rows].view(torch.int16), lay.H[:rows].view(torch.int16))

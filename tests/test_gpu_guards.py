@@ -34,7 +34,7 @@ def _guards_intact(big, n_words, sentinel):
 
 
 @pytest.mark.parametrize("T,hidden,ffn,tile", [(700, 200, 136, "256x256"), (1100, 328, 264, "256x256w8"),
-                                               (300, 72, 520, "128x128")])
+                                               (300, 72, 520, "128x128"), (9000, 128, 200, "256x256")])
 def test_moe_epilogues_stay_in_bounds(monkeypatch, T, hidden, ffn, tile):
     import torch
     import tile_gemm_communication_amd as fm

@@ -250,14 +250,14 @@ def test_moe_combine_deterministic(oracle, T, hidden, ffn, E, nl, topk):
                  "deterministic combine")
 
 
-@pytest.mark.parametrize("T,ffn", [(20000, 504), (600, 264)])
-def test_moe_gather_split_tail_bit_identical(oracle, monkeypatch, T, ffn):
+@pytest.mark.parametrize("T,ffn", [(20000, 504), (600, 264), (9000, 256)])
+def test_moe_gather_split_tail(oracle, monkeypatch, T, ffn):
     """Layer 0 runs a half-empty last wave of 256x256 tiles as 256x128 halves
     (a second launch).  Each H element is still summed over K by one
     workgroup in the same order, so H is bit-identical to the unsplit run,
-    and meets the parity bar on sampled rows.  Shapes: about 330 tiles (one
-    full wave plus a tail) with a ragged last column, and a few tiles only
-    (halves alone)."""
+    and every row of H meets the parity bar.  Shapes: about 330 tiles (one
+    full wave plus a tail) with a ragged last column, a few tiles only
+    (halves alone), and a tail of about a third of a wave."""
     import torch
     import tile_gemm_communication_amd as fm
     hidden, E, nl = 64, 8, 8
@@ -266,22 +266,41 @@ def test_moe_gather_split_tail_bit_identical(oracle, monkeypatch, T, ffn):
     roff, rsp = oracle.moe_route(inp["topk_ids"], 0, nl)
     rows = int(roff[-1])
     X, W1, ids = dev16(inp["X"], BF16), dev16(inp["W1"], BF16), _i32(inp["topk_ids"])
-    outs = []
-    for split in ("1", "0"):
-        monkeypatch.setenv("FM_SPLIT_TAIL", split)
+    ws = fm.moe_workspace(T, 2, hidden, nl)
+    outs = {}
+    for mode, env in (("halves", "1"), ("none", "0")):
+        monkeypatch.setenv("FM_SPLIT_TAIL", env)
         H = torch.zeros((T * 2, ffn), dtype=torch.bfloat16, device="cuda:0")
         sp = torch.full((T * 2,), -1, dtype=torch.int32, device="cuda:0")
         off = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
-        fm.fm_moe_gather_gemm(X, ids, W1, H, sp, off, 0, fm.moe_workspace(T, 2, hidden, nl))
+        fm.fm_moe_gather_gemm(X, ids, W1, H, sp, off, 0, ws)
         torch.cuda.synchronize()
-        outs.append(H)
-    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), "split changed H"
-    rng = np.random.default_rng(3)
-    srows = np.unique(np.concatenate([rng.integers(0, rows, 64), roff[:-1], roff[1:] - 1]))
-    srows = srows[(srows >= 0) & (srows < rows)]
-    Hs = oracle.moe_layer0_rows(BF16, inp["X"], inp["W1"], rsp, roff, 2, srows)
-    idx = torch.from_numpy(srows).to("cuda:0")
-    assert_close(host64(outs[0][idx]), Hs, "split-tail layer0 rows")
+        outs[mode] = H
+    assert torch.equal(outs["halves"].view(torch.int16), outs["none"].view(torch.int16))
+    Href = oracle.moe_layer0(BF16, inp["X"], inp["W1"], rsp, roff, 2)
+    assert_close(host64(outs["halves"][:rows]), Href, "layer0 split tail")
+
+
+@pytest.mark.parametrize("act", [1, 2])
+def test_moe_gather_split_tail_activation(oracle, act):
+    """The split tail with an activation: the 256x128 halves apply it in
+    their epilogue as the full tiles do (T = 9000 gives a tail of about a
+    third of a wave)."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    T, hidden, ffn, E, nl = 9000, 128, 256, 8, 8
+    inp = wl.moe_inputs(T, hidden, ffn, E, nl, 2, BF16, seed=T + act, zipf_s=1.2)
+    roff, rsp = oracle.moe_route(inp["topk_ids"], 0, nl)
+    rows = int(roff[-1])
+    ref = oracle.activation(act, oracle.moe_layer0(BF16, inp["X"], inp["W1"], rsp, roff, 2))
+    H = torch.zeros((T * 2, ffn), dtype=torch.bfloat16, device="cuda:0")
+    sp = torch.full((T * 2,), -1, dtype=torch.int32, device="cuda:0")
+    off = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
+    fm.fm_moe_gather_gemm_act(dev16(inp["X"], BF16), _i32(inp["topk_ids"]),
+                              dev16(inp["W1"], BF16), H, sp, off, 0, act,
+                              fm.moe_workspace(T, 2, hidden, nl))
+    torch.cuda.synchronize()
+    assert_close(host64(H[:rows]), ref, f"split tail act {act}")
 
 
 def test_moe_nothing_local_leaves_buffers():
@@ -739,3 +758,4 @@ def test_full_moe_ag_rank0(oracle):
                           e0, fm.moe_workspace(c["T"], 2, c["hidden"], c["n_local"]))
     torch.cuda.synchronize()
     assert torch.equal(H[:rows].view(torch.int16), H2[:rows].view(torch.int16))
+

@@ -123,7 +123,10 @@ template <class E, int BM, int BN, int NW, Mode MODE, bool OUT32, bool KTAIL>
 __global__ __launch_bounds__(64 * NW, 1) void dense_kernel(const DenseArgs args) {
   // One wave per SIMD has the register room for a two-sub-step read-ahead,
   // or for the 16x16x32 MFMA form.
-  using Eng = Engine<E, BM, BN, KTAIL, NW, 4, NW == 4 ? 2 : 1, kMfma16 && NW == 4 && !KTAIL>;
+  // 256x128 and 128x128 tiles keep three LDS stages in flight (their K steps
+  // are short); 256x256 tiles have room for two.
+  using Eng = Engine<E, BM, BN, KTAIL, NW, 4, NW == 4 ? 2 : 1, kMfma16 && NW == 4 && !KTAIL, false,
+                     BN == 128 ? 3 : 2>;
   // The ReduceScatter epilogue of full tiles keeps its destination rows in
   // LDS (the one-wave-per-SIMD form: with two, its registers would spill).
   constexpr bool kRsDma = MODE == Mode::RS && NW == 4;

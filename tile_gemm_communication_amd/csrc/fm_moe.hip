@@ -311,7 +311,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   // ACT: layer 0 with an activation (a.act); a separate instantiation, so
   // the plain form carries none of its code.
   static_assert(!(ACT && (SCATTER || PULL)), "the activation is a plain layer-0 form");
-  using Eng = Engine<E, BM, BN, KTAIL, NW, 4, NW == 4 ? 2 : 1, false, PULL>;
+  using Eng = Engine<E, BM, BN, KTAIL, NW, 4, NW == 4 ? 2 : 1, false, PULL, BN == 128 ? 3 : 2>;
   // the combine's epilogue also keeps its destination rows in LDS
   constexpr int kSmem =
       (SCATTER && Eng::EP_RMW_LDS > Eng::LDS_BYTES) ? Eng::EP_RMW_LDS : Eng::LDS_BYTES;

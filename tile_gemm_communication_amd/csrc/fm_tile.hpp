@@ -144,8 +144,14 @@ __device__ __forceinline__ void interleave() {
 }
 
 template <class E, int BM, int BN, bool KTAIL, int NW = 4, int BSWZ = 4, int DEPTH_ = 1,
-          bool MF16 = false, bool A64 = false>
+          bool MF16 = false, bool A64 = false, int NSTAGE_ = 2>
 struct Engine {
+  // LDS stages in flight: 2 (double buffering), or 3 for tiles whose stages
+  // are small enough (a K step of a 256x128 tile is half as long as one of a
+  // 256x256 tile, too short to hide an L2/MALL miss with one stage of
+  // look-ahead).  A K tail and the 16x16 form keep 2.
+  static constexpr int NSTAGE = (KTAIL || MF16) ? 2 : NSTAGE_;
+  static_assert(NSTAGE == 2 || NSTAGE == 3, "2 or 3 LDS stages");
   // Fragment read-ahead in sub-steps: 1 = the next sub-step (two register
   // slots), 2 = two sub-steps ahead (four slots, one per sub-step; needs the
   // register room of one wave per SIMD).  A K tail, and the 16x16 form (whose
@@ -163,8 +169,8 @@ struct Engine {
   static constexpr int A_STAGE = BM * 128;
   static constexpr int B_ROW = BN * 2;
   static constexpr int B_STAGE = 64 * B_ROW;
-  static constexpr int LDS_B = 2 * A_STAGE;             // B stages follow both A stages
-  static constexpr int LDS_BYTES = 2 * (A_STAGE + B_STAGE);
+  static constexpr int LDS_B = NSTAGE * A_STAGE;        // B stages follow the A stages
+  static constexpr int LDS_BYTES = NSTAGE * (A_STAGE + B_STAGE);
   static constexpr int A_ROWS = BM / NW;                // A rows each wave stages
   static constexpr int A_DMA = A_ROWS / 8;              // DMA instructions per wave per stage
   static constexpr int B_CPR = BN / 8;                  // 16-byte chunks per B row
@@ -441,14 +447,25 @@ struct Engine {
   // sub-steps 0 and 1 of stage kt+1 and issue the DMA of stage kt+2 into
   // buffer cur in two halves.  Every read has a whole sub-step more slack.
   __device__ __forceinline__ void step2(int kt) {
-    const int cur = kt & 1;
+    const int cur = kt % NSTAGE, nxt = (kt + 1) % NSTAGE;
     substep_g(0, cur, 2, 2, true, -1, 0, 0, 0);
     substep_g(1, cur, 3, 3, true, -1, 0, 0, 0);
-    wait_all0();
+    wait_stage();
     __syncthreads();
-    const int dk = min(kt + 2, KT - 1);
-    substep_g(2, cur ^ 1, 0, 0, true, dk, cur, 0, DMA / 2);
-    substep_g(3, cur ^ 1, 1, 1, true, dk, cur, DMA / 2, DMA);
+    const int dk = min(kt + NSTAGE, KT - 1);
+    substep_g(2, nxt, 0, 0, true, dk, cur, 0, DMA / 2);
+    substep_g(3, nxt, 1, 1, true, dk, cur, DMA / 2, DMA);
+  }
+
+  // Before the barrier of K step kt: stage kt+1 has landed (the later stages
+  // may still be in flight) and this wave's LDS reads are done.
+  __device__ __forceinline__ void wait_stage() {
+    if constexpr (NSTAGE == 2) {
+      wait_all0();
+    } else {
+      wait_vmcnt<(NSTAGE - 2) * DMA>();
+      wait_lgkm_mem();
+    }
   }
 
 
@@ -464,7 +481,7 @@ struct Engine {
   // its own LDS rows, and its loads complete in order, so a later tile's
   // data is never overwritten).  The accumulators thus stay in one place.
   __device__ __forceinline__ void step(int kt) {
-    const int cur = kt & 1;
+    const int cur = kt % NSTAGE;
     if constexpr (MF16) {
       // two sub-steps of 32: the second reads sub-step 0 of stage kt+1
       substep(0, cur, 1, true, -1, 0);
@@ -481,10 +498,10 @@ struct Engine {
     substep(0, cur, 1, true, -1, 0);
     substep(1, cur, 2, true, -1, 0);
     substep(0, cur, 3, true, -1, 0);
-    wait_all0();
+    wait_stage();
     __syncthreads();
     if constexpr (!KTAIL) {
-      substep(1, cur ^ 1, 0, true, min(kt + 2, KT - 1), cur);
+      substep(1, (kt + 1) % NSTAGE, 0, true, min(kt + NSTAGE, KT - 1), cur);
     } else {
       if (kt + 2 < KT) dma(kt + 2, cur, kt + 3 == KT);
       substep(1, cur ^ 1, 0, true, -1, 0);
@@ -510,12 +527,21 @@ struct Engine {
       after_first_wait();
       return;
     }
-    dma(0, 0, KTAIL && KT == 1);
-    if (KT > 1) dma(1, 1, KTAIL && KT == 2);
-    if (KT > 1 && !(KTAIL && KT == 2))
-      wait_vmcnt<DMA>();   // stage 0 landed; the full stage 1 may still be in flight
-    else
-      wait_vmcnt<0>();     // a masked stage issues fewer loads: wait for all
+    if constexpr (NSTAGE == 3) {
+      // stages 0, 1 and 2, always three loads so the wait counts them (a
+      // short loop loads its last stage again into a buffer it never reads)
+      dma(0, 0, false);
+      dma(min(1, KT - 1), 1, false);
+      dma(min(2, KT - 1), 2, false);
+      wait_vmcnt<2 * DMA>();   // stage 0 landed; stages 1 and 2 may be in flight
+    } else {
+      dma(0, 0, KTAIL && KT == 1);
+      if (KT > 1) dma(1, 1, KTAIL && KT == 2);
+      if (KT > 1 && !(KTAIL && KT == 2))
+        wait_vmcnt<DMA>();   // stage 0 landed; the full stage 1 may still be in flight
+      else
+        wait_vmcnt<0>();     // a masked stage issues fewer loads: wait for all
+    }
     __syncthreads();
     after_first_wait();
     read_frags(0, 0, 0);
