@@ -18,8 +18,8 @@ def built_library():
     """libfluxmi.so, compiled first (hipcc, gfx950; no GPU needed) when a fresh
     checkout has none yet."""
     import tile_gemm_communication_amd as fm
-    if not os.path.exists(fm.LIB_PATH):
-        from tile_gemm_communication_amd import build
+    from tile_gemm_communication_amd import build
+    if not os.path.exists(fm.LIB_PATH) or not os.path.exists(build.RESOURCES):
         build.build(verbose=False)
     return fm.lib()
 
