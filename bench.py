@@ -87,6 +87,9 @@ def parse():
     ap.add_argument("--serial-arrival", action="store_true",
                     help="let every chunk land before fm_ag_gemm starts (for profilers that "
                          "serialise kernel dispatches, where a concurrent arrival cannot happen)")
+    ap.add_argument("--parts", type=int, default=1, choices=(1, 2, 4, 8),
+                    help="communication parts per pushed chunk, each with its own flag "
+                         "(finer communication tiles)")
     ap.add_argument("--arrival", choices=("kernel", "dma"), default="kernel",
                     help="emulated peer push: fm_chunk_push (copy kernel) or "
                          "fm_chunk_push_dma (copy engines, no compute units)")
@@ -132,8 +135,12 @@ class Workload:
         _, W2, seeds = wl.rs_inputs(self.M, self.N2, self.K2, self.P, wl.F16, seed=rs["seed"])
         self.W2 = up(W2, f16)
         self.dst = [torch.from_numpy(seeds[r]).to(dev) for r in range(self.P)]
-        self.flags = torch.zeros(self.n, dtype=torch.int32, device=dev)
-        self.counters = torch.zeros(self.n, dtype=torch.int32, device=dev)
+        # one flag per communication part: each rank's chunk is pushed and
+        # published as `parts` row blocks (pull mode and the in-launch
+        # producers use the first n flags, one per chunk)
+        self.parts = 1
+        self.flags = torch.zeros(self.n * 8, dtype=torch.int32, device=dev)
+        self.counters = torch.zeros(self.n * 8, dtype=torch.int32, device=dev)
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
         self.epoch = 0
 
@@ -157,8 +164,8 @@ class Workload:
         self.mpeers = [up(inp["X"][c * self.mTc:(c + 1) * self.mTc], bf16) for c in range(self.n)]
         self.mXg = torch.empty_like(self.mX)
         self.mXg[: self.mTc].copy_(self.mpeers[0])
-        self.mflags = torch.zeros(self.n, dtype=torch.int32, device=dev)
-        self.mcounters = torch.zeros(self.n, dtype=torch.int32, device=dev)
+        self.mflags = torch.zeros(self.n * 8, dtype=torch.int32, device=dev)
+        self.mcounters = torch.zeros(self.n * 8, dtype=torch.int32, device=dev)
         self.H = torch.empty((self.T * self.topk, self.ffn), dtype=bf16, device=dev)
         self.sp = torch.empty(self.T * self.topk, dtype=torch.int32, device=dev)
         self.off = torch.zeros(self.n_local + 1, dtype=torch.int32, device=dev)
@@ -178,27 +185,43 @@ class Workload:
         torch.cuda.synchronize()
 
     # -- pieces of a step ----------------------------------------------------
+    def part_order(self):
+        """Arrival order of the communication parts: chunk by chunk in
+        self.order, each chunk's parts in row order."""
+        return [c * self.parts + q for c in self.order for q in range(self.parts)]
+
     def push_all(self, epoch, events=None, moe=False):
-        """Publish the local chunk and push the seven peer chunks, peer i on
-        side stream i % 3.  events: optional per-chunk events recorded after
-        each push.  moe: the token chunks of MoE layer 0 instead of the dense
-        AllGather's row chunks."""
+        """Publish the local chunk and push the seven peer chunks, each as
+        self.parts row blocks with a flag of its own, part i of the sequence
+        on side stream i % 3.  events: optional per-chunk events recorded
+        after each chunk's last part.  moe: the token chunks of MoE layer 0
+        instead of the dense AllGather's row chunks."""
         import tile_gemm_communication_amd as fm
         import torch
         peers, X, Mc = (self.mpeers, self.mXg, self.mTc) if moe else (self.peers, self.X, self.Mc)
         flags, counters = (self.mflags, self.mcounters) if moe else (self.flags, self.counters)
+        P = self.parts
+        rows = Mc // P
         cs = torch.cuda.current_stream()
         for s in self.sides:
             s.wait_stream(cs)
-        def push(src, dst, c, s):
+        def push(src, dst, f, s):
             if self.arrival == "dma":
-                fm.fm_chunk_push_dma(src, dst, flags[c:c + 1], epoch, stream=s)
+                fm.fm_chunk_push_dma(src, dst, flags[f:f + 1], epoch, stream=s)
             else:
-                fm.fm_chunk_push(src, dst, flags[c:c + 1], counters[c:c + 1], epoch, stream=s)
-        push(None, None, 0, self.sides[0])
-        for i, c in enumerate(self.order[1:]):
-            s = self.sides[i % self.n_sides]
-            push(peers[c], X[c * Mc:(c + 1) * Mc], c, s)
+                fm.fm_chunk_push(src, dst, flags[f:f + 1], counters[f:f + 1], epoch, stream=s)
+        # the local chunk is in place: its flags are written by the stream
+        # itself (no kernel)
+        for q in range(P):
+            f = self.order[0] * P + q
+            fm.fm_chunk_push_dma(None, None, flags[f:f + 1], epoch, stream=self.sides[0])
+        i = 0
+        for c in self.order[1:]:
+            for q in range(P):
+                s = self.sides[i % self.n_sides]
+                push(peers[c][q * rows:(q + 1) * rows],
+                     X[c * Mc + q * rows:c * Mc + (q + 1) * rows], c * P + q, s)
+                i += 1
             if events is not None:
                 events[c].record(s)
 
@@ -210,8 +233,9 @@ class Workload:
 
     def ag(self, epoch):
         import tile_gemm_communication_amd as fm
-        fm.fm_ag_gemm(self.X, self.W1, self.Out1, self.flags, epoch, self.n, order=self.order,
-                      err_word=self.err)
+        n = self.n * self.parts
+        fm.fm_ag_gemm(self.X, self.W1, self.Out1, self.flags[:n], epoch, n,
+                      order=self.part_order(), err_word=self.err)
 
     def rs(self):
         import tile_gemm_communication_amd as fm
@@ -224,8 +248,9 @@ class Workload:
 
     def moe0_ag(self, epoch):
         import tile_gemm_communication_amd as fm
+        n = self.n * self.parts
         fm.fm_moe_ag_gather_gemm(self.mXg, self.ids, self.mW1, self.H, self.sp, self.off, self.e0,
-                                 self.mflags, epoch, self.n, self.mws, order=self.order,
+                                 self.mflags[:n], epoch, n, self.mws, order=self.part_order(),
                                  err_word=self.err)
 
     def moe1(self):
@@ -245,7 +270,10 @@ class Workload:
         if evs: evs[0].record(cs)
         self.ag(self.epoch)
         if evs: evs[1].record(cs)
-        self.join_sides()
+        # GEMM-RS does not depend on the arrival streams (only the AllGather's
+        # tiles wait for their chunks' flags), so the compute stream does not
+        # join them here: the next step's pushes wait for the compute stream,
+        # and the timed region ends with a device-wide synchronize.
         self.rs()
         if evs: evs[2].record(cs)
         self.moe0()
@@ -255,6 +283,14 @@ class Workload:
 
 
 LINK_BYTES_PER_S = 153e9   # one MI355X xGMI link, per direction
+
+
+def check_err(w, what):
+    """Stop with the status a kernel wrote to the shared err_word during `what`."""
+    import tile_gemm_communication_amd as fm
+    code = int(w.err.item())
+    if code != 0:
+        raise RuntimeError(f"{what}: a kernel reported {fm.status_str(code)}")
 
 
 def time_loop(fn, iters, warmup):
@@ -318,21 +354,24 @@ def ect_block(w, iters):
     def ns_blas():
         torch.matmul(w.X, w.W1, out=w.Out1)
 
+    # The fused forms end with their last kernel on the compute stream: it
+    # cannot finish before every chunk it reads has arrived, and the next
+    # iteration's pushes wait for the compute stream, so no join is needed
+    # (a cross-stream join only adds its own latency to the measured time).
     def fused():
         w.epoch += 1
         w.push_all(w.epoch)
         if w.serial_arrival:
             w.join_sides()
         w.ag(w.epoch)
-        w.join_sides()
 
     chunk_ev = [torch.cuda.Event() for _ in range(w.n)]
 
     def producers():
         # the copies run on producer workgroups of the GEMM's own launch
         w.epoch += 1
-        fm.fm_ag_gemm_producers([None] + w.peers[1:], w.X, w.W1, w.Out1, w.flags, w.counters,
-                                w.epoch, order=w.order, err_word=w.err)
+        fm.fm_ag_gemm_producers([None] + w.peers[1:], w.X, w.W1, w.Out1, w.flags[:w.n],
+                                w.counters[:w.n], w.epoch, order=w.order, err_word=w.err)
 
     def naive():
         # the prior-art sequence: one GEMM launch per chunk, each after its chunk
@@ -343,7 +382,6 @@ def ect_block(w, iters):
                 cs.wait_event(chunk_ev[c])
             rows = slice(c * w.Mc, (c + 1) * w.Mc)
             fm.fm_gemm(w.X[rows], w.W1, w.Out1[rows])
-        w.join_sides()
 
     log("ECT: AllGather-GEMM")
     for name, fn in [("nonsplit_fm_gemm", ns_fm), ("nonsplit_hipblaslt", ns_blas),
@@ -372,8 +410,8 @@ def ect_block(w, iters):
             w.epoch += 1
             s = w.sides[0]
             s.wait_stream(cs)
-            fm.fm_chunk_signal_paced(w.flags, times, w.epoch, order=w.order, stream=s)
-            fm.fm_ag_gemm_pull(w.peers, w.W1, w.Out1, w.flags, w.epoch, order=w.order,
+            fm.fm_chunk_signal_paced(w.flags[:w.n], times, w.epoch, order=w.order, stream=s)
+            fm.fm_ag_gemm_pull(w.peers, w.W1, w.Out1, w.flags[:w.n], w.epoch, order=w.order,
                                err_word=w.err)
             cs.wait_stream(s)
         return fn
@@ -383,7 +421,7 @@ def ect_block(w, iters):
             w.epoch += 1
             s = w.sides[0]
             s.wait_stream(cs)
-            fm.fm_chunk_signal_paced(w.flags, times, w.epoch, order=w.order, stream=s)
+            fm.fm_chunk_signal_paced(w.flags[:w.n], times, w.epoch, order=w.order, stream=s)
             cs.wait_stream(s)                   # the whole AllGather first
             fm.fm_gemm(w.X, w.W1, w.Out1)
         return fn
@@ -442,7 +480,6 @@ def ect_block(w, iters):
         if w.serial_arrival:
             w.join_sides()
         w.moe0_ag(w.epoch)
-        w.join_sides()
 
     def moe_naive():
         # the whole AllGather first, then the layer
@@ -455,8 +492,8 @@ def ect_block(w, iters):
         # the token copies run on producer workgroups of layer 0's own launch
         w.epoch += 1
         fm.fm_moe_ag_gather_gemm_producers([None] + w.mpeers[1:], w.mXg, w.ids, w.mW1, w.H, w.sp,
-                                           w.off, w.e0, w.mflags, w.mcounters, w.epoch, w.mws,
-                                           order=w.order, err_word=w.err)
+                                           w.off, w.e0, w.mflags[:w.n], w.mcounters[:w.n],
+                                           w.epoch, w.mws, order=w.order, err_word=w.err)
 
     # pull mode: layer 0 reads each owner's 16 MiB chunk in place, signals
     # timed at one link's rate (direct: all seven land at t_link)
@@ -467,9 +504,9 @@ def ect_block(w, iters):
             w.epoch += 1
             s = w.sides[0]
             s.wait_stream(cs)
-            fm.fm_chunk_signal_paced(w.mflags, times, w.epoch, order=w.order, stream=s)
+            fm.fm_chunk_signal_paced(w.mflags[:w.n], times, w.epoch, order=w.order, stream=s)
             fm.fm_moe_ag_gather_gemm_pull(w.mpeers, w.ids, w.mW1, w.H, w.sp, w.off, w.e0,
-                                          w.mflags, w.epoch, w.mws, order=w.order,
+                                          w.mflags[:w.n], w.epoch, w.mws, order=w.order,
                                           err_word=w.err)
             cs.wait_stream(s)
         return fn
@@ -479,7 +516,7 @@ def ect_block(w, iters):
             w.epoch += 1
             s = w.sides[0]
             s.wait_stream(cs)
-            fm.fm_chunk_signal_paced(w.mflags, times, w.epoch, order=w.order, stream=s)
+            fm.fm_chunk_signal_paced(w.mflags[:w.n], times, w.epoch, order=w.order, stream=s)
             cs.wait_stream(s)                   # the whole AllGather first
             w.moe0()
         return fn
@@ -489,6 +526,7 @@ def ect_block(w, iters):
                      ("producers", moe_producers)]:
         med, best = time_loop(fn, iters, 3)
         res[f"moe_ag_{name}_ms"] = round(med, 4)
+        check_err(w, f"MoE layer 0 {name}")
     res["moe_ag_ect_ms"] = round(res["moe_ag_fused_ms"] - res["moe_ag_nonsplit_ms"], 4)
     res["moe_ag_ect_naive_ms"] = round(res["moe_ag_gather_then_gemm_ms"]
                                        - res["moe_ag_nonsplit_ms"], 4)
@@ -500,6 +538,7 @@ def ect_block(w, iters):
                         ("ring", [a * t_link_moe for a in range(w.n)])]:
         med, _ = time_loop(moe_pull(times), iters, 3)
         res[f"moe_pull_{name}_fused_ms"] = round(med, 4)
+        check_err(w, f"MoE layer 0 pull {name}")
         res[f"moe_pull_{name}_ect_ms"] = round(med - res["moe_ag_nonsplit_ms"], 4)
         med, _ = time_loop(moe_pull_naive(times), iters, 3)
         res[f"moe_pull_{name}_gather_then_gemm_ms"] = round(med, 4)
@@ -628,6 +667,7 @@ def main():
     w = Workload()
     w.serial_arrival = args.serial_arrival
     w.arrival = args.arrival
+    w.parts = args.parts
     cs = torch.cuda.current_stream()
 
     log(f"warmup {args.warmup} steps")
@@ -635,15 +675,27 @@ def main():
         w.step()
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        w.step(evs[k])
+        w.step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     assert int(w.err.item()) == 0, f"a kernel reported {fm.status_str(int(w.err.item()))}"
     ms_step = (t1 - t0) * 1e3 / args.steps
+    # Per-operator times: the same K steps again with HIP events between the
+    # operators on the compute stream.  Each timing event costs the stream a
+    # few microseconds, so `value` comes from the loop above, which has none.
+    log(f"timing {args.steps} steps with per-operator events")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for k in range(args.steps):
+        w.step(evs[k])
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    assert int(w.err.item()) == 0, f"a kernel reported {fm.status_str(int(w.err.item()))}"
+    ms_step_events = (t3 - t2) * 1e3 / args.steps
     names = ["ag_gemm", "gemm_rs", "moe_gather_gemm", "moe_gemm_scatter"]
     per_step = {n: sorted(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps))
                 for i, n in enumerate(names)}
@@ -671,6 +723,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_with_op_events": round(ms_step_events, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
