@@ -254,3 +254,32 @@ def test_combine_and_layer0_beyond_the_cached_tile_ranges(oracle):
     assert arr.err.item() == 0
     assert np.array_equal(off2.cpu().numpy(), roff)
     assert torch.equal(H2[:rows].view(torch.int16), lay.H[:rows].view(torch.int16))
+
+
+@pytest.mark.parametrize("T,hidden,ffn,topk", [(3000, 520, 264, 2), (700, 200, 136, 4),
+                                                (5000, 1024, 512, 2)])
+def test_combine_epilogue_forms_bit_identical(oracle, monkeypatch, T, hidden, ffn, topk):
+    """The combine's two epilogues, the register-fetch form over a buffer
+    resource (the default below 2 GiB of out) and the LDS-DMA form
+    (FM_COMBINE_DMA=1, the one for larger outputs), add the same products in
+    the same order: out is bit-identical, and both match the oracle.  Hidden
+    sizes past a 256-column tile edge, rows past an expert's last tile, a
+    ragged K (136: the 4-wave tail kernel, whose epilogue is always the DMA
+    form) and top-4 routing."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    E, nl, e0 = 16, 8, 8
+    say(f"combine epilogue forms T={T} hidden={hidden} ffn={ffn} topk={topk}")
+    inp = wl.moe_inputs(T, hidden, ffn, E, nl, topk, BF16, seed=T + hidden, zipf_s=1.2)
+    lay = Layer(inp, e0, nl)
+    outs = {}
+    for form, env in (("vgpr", "0"), ("dma", "1")):
+        monkeypatch.setenv("FM_COMBINE_DMA", env)
+        out = devf32(inp["out_seed"])
+        lay.run(out=out)
+        torch.cuda.synchronize()
+        assert lay.err.item() == 0
+        outs[form] = out
+    assert torch.equal(outs["vgpr"].view(torch.int32), outs["dma"].view(torch.int32))
+    ref = _oracle_combine(oracle, inp, e0, nl)
+    assert_close(host64(outs["vgpr"]) - inp["out_seed"], ref - inp["out_seed"], "combine forms")

@@ -34,8 +34,14 @@ def _guards_intact(big, n_words, sentinel):
 
 
 @pytest.mark.parametrize("T,hidden,ffn,tile", [(700, 200, 136, "256x256"), (1100, 328, 264, "256x256w8"),
-                                               (300, 72, 520, "128x128"), (9000, 128, 200, "256x256")])
+                                               (300, 72, 520, "128x128"), (9000, 128, 200, "256x256"),
+                                               (2000, 328, 256, "256x256"), (1500, 200, 192, "128x128")])
 def test_moe_epilogues_stay_in_bounds(monkeypatch, T, hidden, ffn, tile):
+    """Layer 0's H stores and the combine's out read-modify-writes stay in
+    their buffers (sentinels on both sides).  A ragged K runs the tail
+    kernels (the combine's LDS-DMA epilogue); K a multiple of 64 with a
+    ragged hidden size runs the combine's register-fetch epilogue, whose
+    lanes past the last column or row address past the end of out."""
     import torch
     import tile_gemm_communication_amd as fm
     monkeypatch.setenv("FM_MOE_TILE", tile)

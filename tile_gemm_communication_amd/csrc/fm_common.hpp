@@ -70,6 +70,14 @@ __device__ __forceinline__ void store_through(float* p, const f32x4& v) {
 }
 #pragma clang diagnostic pop
 
+// Raw buffer resources (stride 0): word 3 carries the 32-bit data format,
+// which untyped dword loads and stores need.  An access at an offset >= the
+// record count is out of range: a load returns 0 and a store is dropped.
+// kBufStoreThrough is the store cache policy sc0 | sc1 (written through to
+// memory, as store_through).
+constexpr int kBufRsrcWord3 = 0x00020000;
+constexpr int kBufStoreThrough = 17;
+
 // Device properties cached once per device (compute-unit count).
 int device_cu_count();
 

@@ -46,6 +46,14 @@ constexpr int kCtlEpoch = 0;     // the last combine launch's epoch
 constexpr int kCtlDone = 1;      // workgroups of the running combine that finished
 constexpr int kCtlTicket = 2;    // next tile ticket of the running combine
 constexpr int kCtlAbort = 3;     // = epoch once a wait of that launch gave up
+// The combine's register-fetch epilogue addresses out (at most
+// kVepMaxRecords bytes) by 32-bit offsets, each the sum of a row part and a
+// column part.  A missing row adds kVepNoRow, a missing column kVepNoCol: any
+// sum with a missing part lies in [kVepMaxRecords, 2^32), past the end of out,
+// where a buffer load returns 0 and a store is dropped.
+constexpr uint32_t kVepMaxRecords = 0x7FFFFFF0u;
+constexpr uint32_t kVepNoRow = 0x80000000u;
+constexpr uint32_t kVepNoCol = 0x7FFFFFF0u;
 constexpr int64_t kWsSink = 64;
 constexpr int64_t kWsRoute = kWsSink + 256;
 constexpr int64_t kRouteWords = 16384;
@@ -187,6 +195,10 @@ struct MoeArgs {
   // remaining tiles as 256x128 halves.  tiles_n always counts 256-wide tiles.
   int split, part, g_ref;
   int64_t rows_cap;           // T * topk: an upper bound on the local rows
+  // Combine: bytes of out (T x N fp32) when at most kVepMaxRecords, which
+  // selects the register-fetch epilogue over a buffer resource; 0 selects the
+  // LDS-DMA one.
+  uint32_t out_records;
   // Layer 0 behind a token AllGather (flags != null): chunk c holds tokens
   // [c*chunk_tokens, (c+1)*chunk_tokens) and is read after flags[c] >= epoch.
   const uint32_t* flags;
@@ -302,7 +314,7 @@ __device__ __forceinline__ void combine_tile(const MoeArgs& a, const int* s_off,
 }
 
 template <class E, int BM, int BN, int NW, bool SCATTER, bool KTAIL, bool PULL = false,
-          bool ACT = false>
+          bool ACT = false, bool VEP = false>
 __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   // One wave per SIMD has the register room for a two-sub-step read-ahead.
   // PULL: the token rows are gathered from the owners' chunk buffers, one
@@ -311,6 +323,8 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   // ACT: layer 0 with an activation (a.act); a separate instantiation, so
   // the plain form carries none of its code.
   static_assert(!(ACT && (SCATTER || PULL)), "the activation is a plain layer-0 form");
+  // VEP: the combine's register-fetch epilogue (out below 4 GiB, a.out_records).
+  static_assert(!VEP || SCATTER, "the register-fetch epilogue is the combine's");
   using Eng = Engine<E, BM, BN, KTAIL, NW, 4, NW == 4 ? 2 : 1, false, PULL, BN == 128 ? 3 : 2>;
   // the combine's epilogue also keeps its destination rows in LDS
   constexpr int kSmem =
@@ -578,7 +592,11 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       // one expert (an input the combine does not accept) are neighbours.
       if (t == 0) s_next[it & 1] = (int)next_ticket;
       if (t < BM) {
-        s_tok[t] = my_p >= 0 ? my_p / a.topk : -1;
+        if constexpr (VEP)   // the row's byte offset in out (or the no-row mark)
+          s_tok[t] = (int)(my_p >= 0 ? (uint32_t)(my_p / a.topk) * ((uint32_t)a.N * 4u)
+                                     : kVepNoRow);
+        else
+          s_tok[t] = my_p >= 0 ? my_p / a.topk : -1;
         s_wt[t] = my_p >= 0 ? a.weights[my_p] : 0.f;
         if (my_p >= 0 && prev_p >= 0 && my_p / a.topk == prev_p / a.topk) s_dup = 1;
       }
@@ -600,84 +618,150 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       if (t == 0 && s_dup && a.err_word)
         __hip_atomic_store(a.err_word, (int32_t)FM_ERR_INVALID_ARG, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-      // Per wave and 32-row block i: the destination rows come into LDS by
-      // DMA, the accumulators are staged, and weight * row is added and
-      // stored through.  Block i+1's rows are requested before block i's
-      // stores, so a store never delays the next loads (vmcnt counts loads
-      // and stores in issue order).  Each block goes in two halves of H
-      // reads, which bounds the registers the results hold.  Lanes past the
-      // last row or column read and write the sink instead, so every live
-      // block issues exactly H loads and H stores per half and the waits can
-      // count them; blocks past the last row (or a wave past the last
-      // column) issue nothing.  Issue order: D(i) h0, D(i) h1 [block 0 only],
-      // then per half h of block i: D(i+1) h, S(i) h.
-      constexpr int H = Eng::EP_READS / 2;
-      const int col = eng.ep_col();
-      const bool col_ok = n0 + col < N;
-      float* const sink = reinterpret_cast<float*>(a.ws + kWsSink) + 4 * (t & 63);
-      const int row_w = m0 + eng.ep_row0();
-      const int live = (!skip && n0 + eng.ep_col0() < N && row_w < rows_e)
-                           ? min(Eng::FM, (int)cdiv(rows_e - row_w, 32))
-                           : 0;
-      // destinations of half h of block i (the token reads go out together)
-      auto dests = [&](int i, int h, float* (&p)[H]) {
-        int tok[H];
+      if constexpr (VEP) {
+        // Register-fetch form.  Per wave and 32-row block i: the accumulators
+        // are staged through LDS into whole rows, weight * row is added to
+        // the destination values and the sums are stored through.  The
+        // destination rows of two blocks are in flight at a time, in
+        // registers (the K loop's fragment registers are free here): block
+        // i+2's are requested right after block i's stores.  Loads and stores
+        // go through a buffer resource over out, so the compiler counts
+        // them in its waits; a lane with nothing to add (a row past the
+        // expert's rows, a column past N, a skipped tile) uses an offset past
+        // the end of out, which loads 0 and drops the store.
+        constexpr int R = Eng::EP_READS;
+        constexpr int H = R / 2;
+        static_assert(Eng::FM >= 2, "two blocks in flight");
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(a.out, 0, (int)a.out_records, kBufRsrcWord3);
+        // Offset = the row's part (s_tok, kVepNoRow for no row) + the
+        // lane's column part (kVepNoCol past N or for a skipped tile): one
+        // add per access, no branch (a branch per row would make each row's
+        // read wait on its own).
+        const int col = eng.ep_col();
+        const uint32_t col_bytes =
+            (!skip && n0 + col < N) ? (uint32_t)(n0 + col) * 4u : kVepNoCol;
+        auto offsets = [&](int i, uint32_t(&o)[R]) {
 #pragma unroll
-        for (int u = 0; u < H; ++u) tok[u] = s_tok[eng.ep_row(i, h * H + u)];
+          for (int q = 0; q < R; ++q) o[q] = (uint32_t)s_tok[eng.ep_row(i, q)] + col_bytes;
+        };
+        f32x4 d[2][R];
+        auto fetch = [&](int i, f32x4(&dd)[R]) {
+          uint32_t o[R];
+          offsets(i, o);
 #pragma unroll
-        for (int u = 0; u < H; ++u)
-          p[u] = (tok[u] >= 0 && col_ok)
-                     ? reinterpret_cast<float*>(a.out) + (int64_t)tok[u] * N + n0 + col
-                     : sink;
-      };
-      if (live > 0) {
-        float* p0[H];
-        float* p1[H];
-        dests(0, 0, p0);
-        dests(0, 1, p1);
+          for (int q = 0; q < R; ++q)
+            dd[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o[q], 0, 0));
+        };
+        fetch(0, d[0]);
+        fetch(1, d[1]);
+        static_for<Eng::FM>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          uint32_t so[R];
+          offsets(i, so);
+          float wt[R];
 #pragma unroll
-        for (int u = 0; u < H; ++u) eng.ep_fetch(u, p0[u]);
-#pragma unroll
-        for (int u = 0; u < H; ++u) eng.ep_fetch(H + u, p1[u]);
-      }
-#pragma unroll
-      for (int i = 0; i < Eng::FM; ++i) {
-        if (i < live) {
-          eng.ep_stage(i);
-          const bool next = i + 1 < live;
+          for (int q = 0; q < R; ++q) wt[q] = s_wt[eng.ep_row(i, q)];
+          eng.template ep_stage<false>(i);
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            // Wait for D(i) h.  Issued after it: block 0: D(0) h1 (h = 0);
-            // D(1) h0 if any, S(0) h0 (h = 1).  Block i > 0: S(i-1) h0,
-            // D(i) h1, S(i-1) h1 (h = 0); S(i-1) h1, D(i+1) h0 if any,
-            // S(i) h0 (h = 1).
-            if (i == 0 && h == 0) wait_vm_mem<H>();
-            else if (h == 0) wait_vm_mem<3 * H>();
-            else if (i == 0) { if (next) wait_vm_mem<2 * H>(); else wait_vm_mem<H>(); }
-            else { if (next) wait_vm_mem<3 * H>(); else wait_vm_mem<2 * H>(); }
-            f32x4 o[H];
+            f32x4 v[H];
+#pragma unroll
+            for (int u = 0; u < H; ++u) v[u] = eng.ep_read(h * H + u);
 #pragma unroll
             for (int u = 0; u < H; ++u) {
               const int q = h * H + u;
-              const f32x4 v = eng.ep_read(q);
-              const float wt = s_wt[eng.ep_row(i, q)];
-              o[u] = eng.ep_fetched(q);
-              o[u][0] += wt * v[0];
-              o[u][1] += wt * v[1];
-              o[u][2] += wt * v[2];
-              o[u][3] += wt * v[3];
+              f32x4 o = d[i & 1][q];
+              o[0] += wt[q] * v[u][0];
+              o[1] += wt[q] * v[u][1];
+              o[2] += wt[q] * v[u][2];
+              o[3] += wt[q] * v[u][3];
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs, so[q], 0,
+                                                     kBufStoreThrough);
             }
-            float* pc[H];
-            float* pn[H];
-            dests(i, h, pc);
-            if (next) dests(i + 1, h, pn);
-            wait_lgkm_mem();   // these slots are read: block i+1 may land in them
-            if (next) {
-#pragma unroll
-              for (int u = 0; u < H; ++u) eng.ep_fetch(h * H + u, pn[u]);
+          }
+          if constexpr (i + 2 < Eng::FM) fetch(i + 2, d[i & 1]);
+        });
+      } else {
+        // Per wave and 32-row block i: the destination rows come into LDS by
+        // DMA, the accumulators are staged, and weight * row is added and
+        // stored through.  Block i+1's rows are requested before block i's
+        // stores, so a store never delays the next loads (vmcnt counts loads
+        // and stores in issue order).  Each block goes in two halves of H
+        // reads, which bounds the registers the results hold.  Lanes past the
+        // last row or column read and write the sink instead, so every live
+        // block issues exactly H loads and H stores per half and the waits can
+        // count them; blocks past the last row (or a wave past the last
+        // column) issue nothing.  Issue order: D(i) h0, D(i) h1 [block 0 only],
+        // then per half h of block i: D(i+1) h, S(i) h.
+        constexpr int H = Eng::EP_READS / 2;
+        const int col = eng.ep_col();
+        const bool col_ok = n0 + col < N;
+        float* const sink = reinterpret_cast<float*>(a.ws + kWsSink) + 4 * (t & 63);
+        const int row_w = m0 + eng.ep_row0();
+        const int live = (!skip && n0 + eng.ep_col0() < N && row_w < rows_e)
+                             ? min(Eng::FM, (int)cdiv(rows_e - row_w, 32))
+                             : 0;
+        // destinations of half h of block i (the token reads go out together)
+        auto dests = [&](int i, int h, float* (&p)[H]) {
+          int tok[H];
+  #pragma unroll
+          for (int u = 0; u < H; ++u) tok[u] = s_tok[eng.ep_row(i, h * H + u)];
+  #pragma unroll
+          for (int u = 0; u < H; ++u)
+            p[u] = (tok[u] >= 0 && col_ok)
+                       ? reinterpret_cast<float*>(a.out) + (int64_t)tok[u] * N + n0 + col
+                       : sink;
+        };
+        if (live > 0) {
+          float* p0[H];
+          float* p1[H];
+          dests(0, 0, p0);
+          dests(0, 1, p1);
+  #pragma unroll
+          for (int u = 0; u < H; ++u) eng.ep_fetch(u, p0[u]);
+  #pragma unroll
+          for (int u = 0; u < H; ++u) eng.ep_fetch(H + u, p1[u]);
+        }
+  #pragma unroll
+        for (int i = 0; i < Eng::FM; ++i) {
+          if (i < live) {
+            eng.ep_stage(i);
+            const bool next = i + 1 < live;
+  #pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              // Wait for D(i) h.  Issued after it: block 0: D(0) h1 (h = 0);
+              // D(1) h0 if any, S(0) h0 (h = 1).  Block i > 0: S(i-1) h0,
+              // D(i) h1, S(i-1) h1 (h = 0); S(i-1) h1, D(i+1) h0 if any,
+              // S(i) h0 (h = 1).
+              if (i == 0 && h == 0) wait_vm_mem<H>();
+              else if (h == 0) wait_vm_mem<3 * H>();
+              else if (i == 0) { if (next) wait_vm_mem<2 * H>(); else wait_vm_mem<H>(); }
+              else { if (next) wait_vm_mem<3 * H>(); else wait_vm_mem<2 * H>(); }
+              f32x4 o[H];
+  #pragma unroll
+              for (int u = 0; u < H; ++u) {
+                const int q = h * H + u;
+                const f32x4 v = eng.ep_read(q);
+                const float wt = s_wt[eng.ep_row(i, q)];
+                o[u] = eng.ep_fetched(q);
+                o[u][0] += wt * v[0];
+                o[u][1] += wt * v[1];
+                o[u][2] += wt * v[2];
+                o[u][3] += wt * v[3];
+              }
+              float* pc[H];
+              float* pn[H];
+              dests(i, h, pc);
+              if (next) dests(i + 1, h, pn);
+              wait_lgkm_mem();   // these slots are read: block i+1 may land in them
+              if (next) {
+  #pragma unroll
+                for (int u = 0; u < H; ++u) eng.ep_fetch(h * H + u, pn[u]);
+              }
+  #pragma unroll
+              for (int u = 0; u < H; ++u) store_through(pc[u], o[u]);
             }
-#pragma unroll
-            for (int u = 0; u < H; ++u) store_through(pc[u], o[u]);
           }
         }
       }
@@ -800,7 +884,7 @@ int moe_ag_group() {
   return 2;
 }
 
-template <bool SCATTER, bool PULL = false, bool ACT = false>
+template <bool SCATTER, bool PULL = false, bool ACT = false, bool VEP = false>
 void launch_moe_part(fm_dtype_t dt, MoeTile cfg, const MoeArgs& a, hipStream_t stream);
 
 // Layer 0 splits a half-empty last wave into 256x128 halves (part 1, a second
@@ -821,7 +905,8 @@ fm_status_t launch_moe(fm_dtype_t dt, MoeTile cfg, MoeArgs& a, hipStream_t strea
   a.part = 0;
   auto launch_part = [&](MoeTile c) {
     if constexpr (SCATTER) {
-      launch_moe_part<true>(dt, c, a, stream);
+      if (a.out_records) launch_moe_part<true, false, false, true>(dt, c, a, stream);
+      else launch_moe_part<true>(dt, c, a, stream);
     } else {
       if (a.pull_src[0]) launch_moe_part<false, true>(dt, c, a, stream);
       else if (a.act != FM_ACT_NONE) launch_moe_part<false, false, true>(dt, c, a, stream);
@@ -847,16 +932,17 @@ int combine_grid() {
   return device_cu_count();
 }
 
-template <bool SCATTER, bool PULL, bool ACT>
+template <bool SCATTER, bool PULL, bool ACT, bool VEP>
 void launch_moe_part(fm_dtype_t dt, MoeTile cfg, const MoeArgs& a, hipStream_t stream) {
   const dim3 grid(SCATTER ? combine_grid() : device_cu_count());
 #define FM_LAUNCH(E, BM, BN, NW)                                                              \
   do {                                                                                        \
-    if (a.K % kBK) /* ragged K: the 4-wave form keeps the tail path spill-free */             \
-      hipLaunchKernelGGL((moe_kernel<E, BM, BN, 4, SCATTER, true, PULL, ACT>), grid,          \
+    if (a.K % kBK) /* ragged K: the 4-wave, LDS-DMA forms keep the tail path spill-free */    \
+      hipLaunchKernelGGL((moe_kernel<E, BM, BN, 4, SCATTER, true, PULL, ACT, false>), grid,   \
                          dim3(256), 0, stream, a);                                            \
     else                                                                                      \
-      hipLaunchKernelGGL((moe_kernel<E, BM, BN, NW, SCATTER, false, PULL, ACT>), grid,        \
+      hipLaunchKernelGGL((moe_kernel<E, BM, BN, NW, SCATTER, false, PULL, ACT, VEP && NW == 4>),\
+                         grid,                                                                \
                          dim3(64 * NW), 0, stream, a);                                        \
   } while (0)
 #define FM_LAUNCH_E(E)                                                                       \
@@ -1155,6 +1241,14 @@ fm_status_t launch_combine(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn
   a.tile_done = flags;   // sized for the smallest tile
   a.err_word = err_word;
   a.spin_limit = spin_limit ? spin_limit : (1ll << 24);
+  // The register-fetch epilogue addresses out through a buffer resource
+  // (32-bit offsets, out below 2 GiB); FM_COMBINE_DMA=1 selects the LDS-DMA
+  // form for any size.
+  const int64_t out_bytes = T * hidden * 4;
+  const char* env = std::getenv("FM_COMBINE_DMA");
+  a.out_records = (out_bytes <= (int64_t)kVepMaxRecords && !(env && env[0] == '1'))
+                      ? (uint32_t)out_bytes
+                      : 0u;
   return launch_moe<true>(dt, moe_tile(true), a, stream);
 }
 

@@ -595,6 +595,9 @@ struct Engine {
     __syncthreads();
   }
   __device__ __forceinline__ void ep_end() { __syncthreads(); }
+  // PIN: hold each accumulator block in place until its staging (see pin);
+  // without it the stores may take the AGPRs as they are.
+  template <bool PIN = true>
   __device__ __forceinline__ void ep_stage(int i) {
     // Keep each block's global traffic after its own staging: without this
     // fence the compiler hoists the loads of later blocks and spills.
@@ -616,7 +619,7 @@ struct Engine {
     char* reg = smem + w * (32 * EP_STRIDE) + (lane & 31) * EP_STRIDE + 16 * (lane >> 5);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      pin(i, j);
+      if constexpr (PIN) pin(i, j);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         *reinterpret_cast<f32x4*>(reg + (32 * j + 8 * r) * 4) = out_vals(i, j, r);
