@@ -622,16 +622,20 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
         // Register-fetch form.  Per wave and 32-row block i: the accumulators
         // are staged through LDS into whole rows, weight * row is added to
         // the destination values and the sums are stored through.  The
-        // destination rows of two blocks are in flight at a time, in
+        // destination rows of AHEAD blocks are in flight at a time, in
         // registers (the K loop's fragment registers are free here): block
-        // i+2's are requested right after block i's stores.  Loads and stores
+        // i+AHEAD's are requested right after block i's stores.  Loads and stores
         // go through a buffer resource over out, so the compiler counts
         // them in its waits; a lane with nothing to add (a row past the
         // expert's rows, a column past N, a skipped tile) uses an offset past
         // the end of out, which loads 0 and drops the store.
         constexpr int R = Eng::EP_READS;
         constexpr int H = R / 2;
-        static_assert(Eng::FM >= 2, "two blocks in flight");
+        // blocks in flight per wave: two with one wave per SIMD; one with
+        // two (the SIMD's other wave covers the wait, and the registers are
+        // half as many)
+        constexpr int AHEAD = NW == 4 ? 2 : 1;
+        static_assert(Eng::FM >= AHEAD, "blocks in flight");
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc(a.out, 0, (int)a.out_records, kBufRsrcWord3);
         // Offset = the row's part (s_tok, kVepNoRow for no row) + the
@@ -645,7 +649,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
 #pragma unroll
           for (int q = 0; q < R; ++q) o[q] = (uint32_t)s_tok[eng.ep_row(i, q)] + col_bytes;
         };
-        f32x4 d[2][R];
+        f32x4 d[AHEAD][R];
         auto fetch = [&](int i, f32x4(&dd)[R]) {
           uint32_t o[R];
           offsets(i, o);
@@ -653,8 +657,8 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
           for (int q = 0; q < R; ++q)
             dd[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o[q], 0, 0));
         };
-        fetch(0, d[0]);
-        fetch(1, d[1]);
+#pragma unroll
+        for (int b = 0; b < AHEAD; ++b) fetch(b, d[b]);
         static_for<Eng::FM>([&](auto ic) {
           constexpr int i = decltype(ic)::value;
           uint32_t so[R];
@@ -671,7 +675,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
 #pragma unroll
             for (int u = 0; u < H; ++u) {
               const int q = h * H + u;
-              f32x4 o = d[i & 1][q];
+              f32x4 o = d[i % AHEAD][q];
               o[0] += wt[q] * v[u][0];
               o[1] += wt[q] * v[u][1];
               o[2] += wt[q] * v[u][2];
@@ -680,7 +684,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
                                                      kBufStoreThrough);
             }
           }
-          if constexpr (i + 2 < Eng::FM) fetch(i + 2, d[i & 1]);
+          if constexpr (i + AHEAD < Eng::FM) fetch(i + AHEAD, d[i % AHEAD]);
         });
       } else {
         // Per wave and 32-row block i: the destination rows come into LDS by
@@ -941,8 +945,7 @@ void launch_moe_part(fm_dtype_t dt, MoeTile cfg, const MoeArgs& a, hipStream_t s
       hipLaunchKernelGGL((moe_kernel<E, BM, BN, 4, SCATTER, true, PULL, ACT, false>), grid,   \
                          dim3(256), 0, stream, a);                                            \
     else                                                                                      \
-      hipLaunchKernelGGL((moe_kernel<E, BM, BN, NW, SCATTER, false, PULL, ACT, VEP && NW == 4>),\
-                         grid,                                                                \
+      hipLaunchKernelGGL((moe_kernel<E, BM, BN, NW, SCATTER, false, PULL, ACT, VEP>), grid,   \
                          dim3(64 * NW), 0, stream, a);                                        \
   } while (0)
 #define FM_LAUNCH_E(E)                                                                       \
