@@ -138,23 +138,24 @@ def test_two_ranks_on_two_streams(oracle):
 
 
 def test_combine_timeout_is_reported_and_workspace_recovers(oracle):
-    """A tile that never completes: the test starts the workspace's ticket
-    counter (control word 2) at 1, so expert 0's first row tile is never
-    handed out, and expert 1's tile over the same tokens waits for it.  With
-    a spin limit of 2000 polls the launch reports FM_ERR_TIMEOUT (never a
-    silent add) and returns; its last workgroup resets the counter, so the
-    next launch on the same workspace is complete and correct."""
+    """A tile that never completes: hidden = 256 is one tile column, so one
+    tile queue, and the test starts that queue's ticket counter (control
+    word 8) at 1: expert 0's first row tile is never handed out, and expert
+    1's tile over the same tokens waits for it.  With a spin limit of 2000
+    polls the launch reports FM_ERR_TIMEOUT (never a silent add) and
+    returns; its last workgroup resets the counters, so the next launch on
+    the same workspace is complete and correct."""
     import torch
     import tile_gemm_communication_amd as fm
     T, hidden, ffn, nl = 4096, 256, 512, 2
     inp = wl.moe_inputs(T, hidden, ffn, 4, nl, 2, BF16, seed=31)
     inp["topk_ids"] = np.tile(np.array([[0, 1]], dtype=np.int32), (T, 1))
     lay = Layer(inp, 0, nl)
-    lay.ws.view(torch.int32)[2] = 1
+    lay.ws.view(torch.int32)[8] = 1
     lay.run(spin=2000)
     torch.cuda.synchronize()
     assert lay.err.item() == fm.FM_ERR_TIMEOUT
-    assert lay.ws.view(torch.int32)[2].item() == 0       # the ticket counter is reset
+    assert (lay.ws.view(torch.int32)[8:12] == 0).all()    # the ticket counters are reset
     lay.err.zero_()
     out = devf32(inp["out_seed"])
     lay.run(out=out)

@@ -44,8 +44,9 @@ constexpr int kRouteWaves = kRouteThreads / 64;
 // ---------------------------------------------------------------------------
 constexpr int kCtlEpoch = 0;     // the last combine launch's epoch
 constexpr int kCtlDone = 1;      // workgroups of the running combine that finished
-constexpr int kCtlTicket = 2;    // next tile ticket of the running combine
 constexpr int kCtlAbort = 3;     // = epoch once a wait of that launch gave up
+constexpr int kCtlQueue = 8;     // [8, 12): next ticket of each combine tile queue
+constexpr int kMaxQueues = 4;    // combine tile queues (XCDs x and x + 4 share one)
 // The combine's register-fetch epilogue addresses out (at most
 // kVepMaxRecords bytes) by 32-bit offsets, each the sum of a row part and a
 // column part.  A missing row adds kVepNoRow, a missing column kVepNoCol: any
@@ -291,26 +292,32 @@ __device__ __forceinline__ bool wait_token_range(const MoeArgs& a, const int* s_
   return true;
 }
 
-// Combine: the tile of ticket L.  Tickets count tiles in expert order (all
-// of expert 0's tiles, then expert 1's, ...), so a tile only ever waits for
-// tiles of smaller tickets.  Within one expert (whose tiles never wait for
-// each other) the tiles are permuted in windows of G tickets so that the
-// tickets an XCD takes together, which in the first round are those of
-// workgroups w, w+8, w+16, ..., cover a compact block of tiles (see
-// xcd_slot and band_coords).
-__device__ __forceinline__ void combine_tile(const MoeArgs& a, const int* s_off,
-                                             const int* s_tile0, int L, int G, int BM, int& e,
-                                             int& tm, int& tn) {
-  e = 0;
-  while (e + 1 < a.n_local && s_tile0[e + 1] <= L) ++e;
-  const int tiles_e = (int)cdiv(s_off[e + 1] - s_off[e], BM);
-  const int n_e = tiles_e * a.tiles_n;
-  const int i = L - s_tile0[e];
-  const int w0 = i - i % G;
-  const int wsz = min(G, n_e - w0);
-  const int r = i - w0;
-  const int j = w0 + ((wsz & 7) == 0 ? xcd_slot(r, wsz) : r);
-  band_coords(j, tiles_e, a.tiles_n, min(a.group_m, tiles_e), tm, tn);
+// Combine tile queues.  The N columns are dealt to Q = min(4, tiles_n)
+// queues, column tn to queue tn % Q, and a workgroup takes its tiles from
+// the queue of its XCD (XCDs x and x + 4 share one): the tiles in flight on
+// one L2 then share their B columns and, four columns to an M-tile, their A
+// rows.  A queue's tickets walk the global M-tiles in order (all of expert
+// 0's, then expert 1's, ...), each M-tile's columns of the queue in turn.  A
+// tile only waits for tiles of earlier experts in its own column: tiles of
+// the same queue with smaller tickets.  (EP=8 combine: L2 misses 29% fewer
+// than with one queue for all tiles, time equal within 1%; eight queues, one
+// per XCD, were 1.7% slower: each queue's last, small experts then wait on
+// each other among fewer workgroups.)
+struct CombineQueues {
+  int Q, total_m, tiles_n;
+  __device__ __forceinline__ int cols(int q) const { return (tiles_n - q + Q - 1) / Q; }
+  __device__ __forceinline__ int size(int q) const { return total_m * cols(q); }
+  // ticket t of queue q: global M-tile gm, column tn
+  __device__ __forceinline__ void tile(int q, int t, int& gm, int& tn) const {
+    const int c = cols(q);
+    gm = t / c;
+    tn = q + (t - gm * c) * Q;
+  }
+};
+
+// The XCD (accelerator complex die) this wave runs on.
+__device__ __forceinline__ int xcc_id() {
+  return (int)(__builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & 15u);
 }
 
 template <class E, int BM, int BN, int NW, bool SCATTER, bool KTAIL, bool PULL = false,
@@ -341,7 +348,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   // combine: this tile has a row whose token also has the previous row (two
   // pairs of one token in one expert), and the next ticket (by tile parity)
   __shared__ int s_dup;
-  __shared__ int s_next[2];
+  __shared__ int s_next_q[2], s_next_t[2];
   // token AllGather: bands of M-tiles sorted by the arrival of their chunks
   __shared__ int s_band0[SCATTER ? 1 : kMaxLocalExperts + 1];
   __shared__ uint8_t s_blvl[SCATTER ? 1 : kMaxBands];
@@ -368,11 +375,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   if constexpr (SCATTER) {
     epoch = __hip_atomic_load(a.ws + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
     if (epoch == 0) epoch = 1;
-    if (t == 0) {
-      s_next[1] = (int)__hip_atomic_fetch_add(a.ws + kCtlTicket, 1u, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-      s_dup = 0;
-    }
+    if (t == 0) s_dup = 0;
   }
   if (t <= a.n_local) s_off[t] = a.offsets[t];
   __syncthreads();
@@ -483,15 +486,61 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
     pending = -1;
   };
 
-  // Layer 0: static positions slot, slot + G, ...  Combine: tickets, one
-  // taken ahead (during the previous tile's K loop), so that a tile only ever
-  // waits for tiles that running workgroups hold.
-  int L2 = SCATTER ? s_next[1] : slot;
-  for (int it = 0; L2 < n_items; ++it) {
+  // Layer 0: static positions slot, slot + G, ...
+  // Combine: tickets of the tile queues.  A workgroup takes its tiles from
+  // its home queue (its XCD's), each ticket taken ahead during the previous
+  // tile's K loop; once the home queue is exhausted it takes tickets of the
+  // other queues one at a time, with nothing taken ahead.  A ticket taken
+  // ahead is never one the current tile waits for (a later ticket of the
+  // same queue), and a ticket taken from another queue is never held while
+  // waiting, so every ticket taken is held by a running workgroup that can
+  // finish it, whatever share of the CUs the launch gets.  Thread 0 takes
+  // the tickets; `dead` holds the queues it found exhausted.
+  CombineQueues cqs{1, 0, 1};
+  int home = 0, cq = 0, ct = -1;
+  uint32_t dead = 0;
+  auto take = [&](int q) -> int {
+    const uint32_t v = __hip_atomic_fetch_add(a.ws + kCtlQueue + q, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    if (v < (uint32_t)cqs.size(q)) return (int)v;
+    dead |= 1u << q;
+    return -1;
+  };
+  auto steal = [&](int& q) -> int {   // the home queue last
+    for (int k = 1; k <= cqs.Q; ++k) {
+      const int r = (home + k) % cqs.Q;
+      if (dead & (1u << r)) continue;
+      const int v = take(r);
+      if (v >= 0) {
+        q = r;
+        return v;
+      }
+    }
+    return -1;
+  };
+  if constexpr (SCATTER) {
+    cqs = CombineQueues{min(kMaxQueues, a.tiles_n), total_m, a.tiles_n};
+    home = xcc_id() % cqs.Q;
+    if (t == 0) {
+      int q = home;
+      int v = take(home);
+      if (v < 0) v = steal(q);
+      s_next_q[1] = q;
+      s_next_t[1] = v;
+    }
+    __syncthreads();
+    cq = s_next_q[1];
+    ct = s_next_t[1];
+  }
+  int L2 = SCATTER ? 0 : slot;
+  for (int it = 0; SCATTER ? (ct >= 0) : (L2 < n_items); ++it) {
     const int L = pos0 + L2 / sub_n, sub = L2 % sub_n;
     int e = 0, tm, tn;
     if constexpr (SCATTER) {
-      combine_tile(a, s_off, s_tile0, L, G, BM, e, tm, tn);
+      int gm;
+      cqs.tile(cq, ct, gm, tn);
+      while (e + 1 < a.n_local && s_tile0[e + 1] / a.tiles_n <= gm) ++e;
+      tm = gm - s_tile0[e] / a.tiles_n;
     } else if (by_arrival) {
       int lo = 0, hi = n_bands - 1;   // last band starting at or before L
       while (lo < hi) {
@@ -560,7 +609,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
     // Combine: fetch each tile row's pair id now, so that the load overlaps
     // the K loop (the K loop's first wait drains it with the stage-0 DMA).
     int my_p = -1, prev_p = -1;
-    uint32_t next_ticket = 0;
+    int next_q = 0, next_t = -1;
     if constexpr (SCATTER) {
       if (t < BM && m0 + t < rows_e) {
         my_p = a.sorted_pairs[row_base + m0 + t];
@@ -570,11 +619,17 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
     eng.run([&] {
       if constexpr (SCATTER) {
         publish();
-        // the next ticket, taken now and kept in a register until the
-        // epilogue (its return drains with the K loop's first wait)
-        if (t == 0)
-          next_ticket = __hip_atomic_fetch_add(a.ws + kCtlTicket, 1u, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
+        // the next ticket of the home queue, taken now and kept in a
+        // register until the epilogue (its return drains with the K loop's
+        // first wait); -2: take one of another queue after this tile
+        if (t == 0) {
+          next_q = home;
+          next_t = -2;
+          if (cq == home && !(dead & (1u << home))) {
+            const int v = take(home);
+            if (v >= 0) next_t = v;
+          }
+        }
       }
     });
 
@@ -590,7 +645,10 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       // Row metadata into LDS (token, gate weight; token -1 past the rows).
       // Rows of an expert are sorted by pair id, so two pairs of one token in
       // one expert (an input the combine does not accept) are neighbours.
-      if (t == 0) s_next[it & 1] = (int)next_ticket;
+      if (t == 0) {
+        s_next_q[it & 1] = next_q;
+        s_next_t[it & 1] = next_t;
+      }
       if (t < BM) {
         if constexpr (VEP)   // the row's byte offset in out (or the no-row mark)
           s_tok[t] = (int)(my_p >= 0 ? (uint32_t)(my_p / a.topk) * ((uint32_t)a.N * 4u)
@@ -807,7 +865,21 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
     if constexpr (SCATTER) {
       if (s_abort) break;
       if (t == 0) s_dup = 0;   // read by every thread before ep_end's barrier
-      L2 = s_next[it & 1];
+      cq = s_next_q[it & 1];
+      ct = s_next_t[it & 1];
+      if (ct == -2) {
+        // Every thread has read the slot before thread 0 refills it.
+        __syncthreads();
+        if (t == 0) {
+          int q = 0;
+          const int v = steal(q);
+          s_next_q[it & 1] = q;
+          s_next_t[it & 1] = v;
+        }
+        __syncthreads();
+        cq = s_next_q[it & 1];
+        ct = s_next_t[it & 1];
+      }
     } else {
       L2 += G;
     }
@@ -819,9 +891,9 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       publish();
     }
     // Every workgroup checks in once its tiles are done (or abandoned); the
-    // last one resets the count and the ticket counter (every ticket fetch
-    // has returned by then) and stores this launch's epoch for the next
-    // launch.  Relaxed: only the next launch reads these words, after the
+    // last one resets the count and the queues' ticket counters (every
+    // ticket fetch has returned by then) and stores this launch's epoch for
+    // the next launch.  Relaxed: only the next launch reads these words, after the
     // kernel boundary (a release here would write back this XCD's L2 once
     // per workgroup).
     __syncthreads();
@@ -830,7 +902,8 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
                                                    __HIP_MEMORY_SCOPE_AGENT);
       if (prev == (uint32_t)G - 1) {
         __hip_atomic_store(a.ws + kCtlDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(a.ws + kCtlTicket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int q = 0; q < kMaxQueues; ++q)
+          __hip_atomic_store(a.ws + kCtlQueue + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(a.ws + kCtlEpoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
