@@ -457,10 +457,11 @@ fm_status_t fm_moe_ag_gather_gemm_pull(
  * whose token ranges overlap its own, through per-(row tile, column tile)
  * completion flags in the workspace, stamped with an epoch that the kernel
  * itself advances there (so the call may be captured in a HIP graph and
- * replayed).  Tiles are handed out by an atomic ticket in expert order, so a
- * tile only ever waits for tiles that running workgroups hold: the call
- * completes whatever share of the GPU it gets (another kernel, or another
- * combine on another stream with its own workspace, may run beside it).
+ * replayed).  Tiles are handed out by atomic tickets from per-column queues
+ * (one per pair of XCDs, each in expert order), so a tile only ever waits for
+ * tiles that running workgroups hold: the call completes whatever share of
+ * the GPU it gets (another kernel, or another combine on another stream with
+ * its own workspace, may run beside it).
  */
 fm_status_t fm_moe_gemm_scatter(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn,
                                 int32_t topk, int32_t n_local, const void* H, const void* W2,
