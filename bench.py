@@ -46,12 +46,12 @@ PEAK_TFLOPS = 2516.6          # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 
 # known-size copy (`bench.py --copy-probe 256`) gives: FETCH_SIZE x2.0,
 # WRITE_SIZE x1.0.  Keyed by the digest of the kernel sources they were taken
 # on: after any change to csrc/ they no longer apply and traffic is null.
-TRAFFIC_DIGEST = "43c55a4373c26e2a"
+TRAFFIC_DIGEST = "b020d0c28cb55995"
 TRAFFIC_BYTES = {             # op name -> (read bytes, written bytes) per call
-    "ag_gemm": (1115435655, 50328564),
-    "gemm_rs": (1116919396, 201333668),
-    "moe_gather_gemm": (1342333665, 172543571),
-    "moe_gemm_scatter": (1661725561, 504405893),
+    "ag_gemm": (1119385004, 50328564),
+    "gemm_rs": (1128463463, 201316176),
+    "moe_gather_gemm": (1337253472, 172561132),
+    "moe_gemm_scatter": (2226826959, 501668013),
 }
 
 
