@@ -258,7 +258,7 @@ def test_combine_and_layer0_beyond_the_cached_tile_ranges(oracle):
 
 
 @pytest.mark.parametrize("T,hidden,ffn,topk", [(3000, 520, 264, 2), (700, 200, 136, 4),
-                                                (5000, 1024, 512, 2)])
+                                                (5000, 1024, 512, 2), (2500, 1672, 256, 2)])
 def test_combine_epilogue_forms_bit_identical(oracle, monkeypatch, T, hidden, ffn, topk):
     """The combine's two epilogues, the register-fetch form over a buffer
     resource (the default below 2 GiB of out) and the LDS-DMA form
@@ -266,7 +266,8 @@ def test_combine_epilogue_forms_bit_identical(oracle, monkeypatch, T, hidden, ff
     the same order: out is bit-identical, and both match the oracle.  Hidden
     sizes past a 256-column tile edge, rows past an expert's last tile, a
     ragged K (136: the 4-wave tail kernel, whose epilogue is always the DMA
-    form) and top-4 routing."""
+    form) and top-4 routing; hidden = 1672 is 7 tile columns over the 4
+    tile queues (two columns to three queues, one to the last)."""
     import torch
     import tile_gemm_communication_amd as fm
     E, nl, e0 = 16, 8, 8
