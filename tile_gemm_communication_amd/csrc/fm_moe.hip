@@ -369,8 +369,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   }
   const int t = threadIdx.x;
   const int gmb = SCATTER ? 1 : a.ag_group;
-  // Combine: this launch's epoch (never 0, the flags' initial value), and
-  // the first tile ticket.
+  // Combine: this launch's epoch (never 0, the flags' initial value).
   uint32_t epoch = 0;
   if constexpr (SCATTER) {
     epoch = __hip_atomic_load(a.ws + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
