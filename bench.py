@@ -339,6 +339,68 @@ def cold_ops(w):
     return {n: round(a.elapsed_time(b), 4) for (n, _), (a, b) in zip(ops, evs)}
 
 
+def moe_baselines(w, iters):
+    """The MoE layer (layer 0 + the combine, one call each) against its
+    unfused forms on the same inputs and routing: the expert rows gathered
+    first (torch index_select), then one fm_gemm per expert and layer and a
+    torch index_add_ of the weighted products ("pre-gathered grouped GEMM");
+    and a plain torch loop of gather, matmul (hipBLASLt) and index_add_ per
+    expert.  The pre-gathered form is checked against the fused result."""
+    import torch
+
+    import tile_gemm_communication_amd as fm
+    dev = w.mX.device
+    w.moe0()
+    torch.cuda.synchronize()
+    off = [int(v) for v in w.off.cpu().tolist()]
+    rows = off[-1]
+    sp = w.sp[:rows].long()
+    tok = sp // w.topk
+    wt = w.wts.reshape(-1)[sp].unsqueeze(1)          # the row's gate weight (fp32)
+    Xg = torch.empty((rows, w.hidden), dtype=w.mX.dtype, device=dev)
+    Hg = torch.empty((rows, w.ffn), dtype=w.mX.dtype, device=dev)
+    Y = torch.empty((rows, w.hidden), dtype=torch.float32, device=dev)
+    seed = w.mout.clone()
+    experts = [(e, off[e], off[e + 1]) for e in range(w.n_local) if off[e + 1] > off[e]]
+
+    def fused(out):
+        w.moe0()
+        fm.fm_moe_gemm_scatter(w.H, w.mW2, w.sp, w.off, w.wts, out, w.mws, err_word=w.err)
+
+    def pregathered(out):
+        torch.index_select(w.mX, 0, tok, out=Xg)
+        for e, a, b in experts:
+            fm.fm_gemm(Xg[a:b], w.mW1[e], Hg[a:b])
+        for e, a, b in experts:
+            fm.fm_gemm(Hg[a:b], w.mW2[e], Y[a:b])
+        Y.mul_(wt)
+        out.index_add_(0, tok, Y)
+
+    def torch_loop(out):
+        for e, a, b in experts:
+            xe = w.mX.index_select(0, tok[a:b])
+            ye = torch.matmul(torch.matmul(xe, w.mW1[e]), w.mW2[e]).float()
+            out.index_add_(0, tok[a:b], ye * wt[a:b])
+
+    o1, o2 = seed.clone(), seed.clone()
+    fused(o1)
+    pregathered(o2)
+    torch.cuda.synchronize()
+    check_err(w, "MoE layer (fused)")
+    d1, d2 = (o1 - seed).double(), (o2 - seed).double()
+    rel = float(torch.linalg.norm(d1 - d2) / torch.linalg.norm(d1))
+    if not rel < 1e-3:
+        raise RuntimeError(f"pre-gathered MoE layer differs from the fused one: {rel:.3e}")
+    res = {"rows_local": rows, "pregathered_vs_fused_rel_frobenius": rel}
+    out = seed.clone()
+    for name, fn in (("fused", fused), ("pregathered_fm_gemm", pregathered),
+                     ("torch_loop", torch_loop)):
+        med, _ = time_loop(lambda: fn(out), iters, 3)
+        res[f"moe_layer_{name}_ms"] = round(med, 4)
+    check_err(w, "MoE layer (fused)")
+    return res
+
+
 def ect_block(w, iters):
     """ECT of the fused AllGather / ReduceScatter operators."""
     import torch
@@ -747,6 +809,8 @@ def main():
         out["cold_ms"] = cold_ops(w)
     if not args.no_ect:
         out["ect"] = ect_block(w, args.ect_iters)
+        log("MoE layer against its unfused forms")
+        out["moe_baselines"] = moe_baselines(w, args.ect_iters)
     if not args.no_cpu_baseline:
         log(f"CPU oracle sample ({args.cpu_rows} rows)")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
