@@ -285,3 +285,47 @@ def test_combine_epilogue_forms_bit_identical(oracle, monkeypatch, T, hidden, ff
     assert torch.equal(outs["vgpr"].view(torch.int32), outs["dma"].view(torch.int32))
     ref = _oracle_combine(oracle, inp, e0, nl)
     assert_close(host64(outs["vgpr"]) - inp["out_seed"], ref - inp["out_seed"], "combine forms")
+
+
+@pytest.mark.parametrize("T", [131000, 140000])
+def test_combine_outputs_near_and_past_2gib(oracle, T):
+    """out of 131000 x 4096 fp32 (2.146e9 bytes: the register-fetch epilogue,
+    whose 32-bit offsets then reach just under its limit) and of 140000 x
+    4096 (2.29e9 bytes: past the limit, so the LDS-DMA epilogue runs).  H is
+    drawn directly (ffn = 64, one K step) and out starts at zero; tokens
+    sampled across the whole range, the last 64 among them, match the
+    oracle's combine, and the routing is bit-exact."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    hidden, ffn, E, nl, topk, e0 = 4096, 64, 16, 8, 2, 0
+    say(f"combine with a {T * hidden * 4 / 1e9:.3f} GB out")
+    rng = np.random.default_rng(T)
+    first = rng.integers(0, E, T)
+    ids = np.stack([first, (first + 1 + rng.integers(0, E - 1, T)) % E], 1).astype(np.int32)
+    wts = rng.random((T, topk), dtype=np.float32)
+    roff, rsp = oracle.moe_route(ids, e0, nl)
+    rows = int(roff[-1])
+    Hb = wl.normal_bits((rows, ffn), T + 1, BF16)
+    W2b = wl.normal_bits((nl, ffn, hidden), T + 2, BF16, 1.0 / np.sqrt(ffn))
+    dev = "cuda:0"
+    H = torch.zeros((T * topk, ffn), dtype=torch.bfloat16, device=dev)
+    H[:rows] = dev16(Hb, BF16)
+    W2 = dev16(W2b, BF16)
+    ids_d = _i32(ids)
+    wts_d = devf32(wts)
+    sp = torch.full((T * topk,), -1, dtype=torch.int32, device=dev)
+    off = torch.zeros(nl + 1, dtype=torch.int32, device=dev)
+    out = torch.zeros((T, hidden), dtype=torch.float32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = fm.moe_workspace(T, topk, hidden, nl)
+    fm.fm_moe_route(ids_d, e0, nl, sp, off, ws)
+    fm.fm_moe_gemm_scatter(H, W2, sp, off, wts_d, out, ws, err_word=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert np.array_equal(off.cpu().numpy(), roff)
+    assert np.array_equal(sp[:rows].cpu().numpy(), rsp)
+    toks = np.unique(np.concatenate([rng.integers(0, T, 200), np.arange(T - 64, T)]))
+    seed = np.zeros((T, hidden), dtype=np.float32)      # never touched: pages stay unmapped
+    ref = oracle.moe_layer1_tokens(BF16, Hb, W2b, ids, wts, rsp, roff, seed, e0, toks)
+    got = host64(out[torch.from_numpy(toks).to(dev)])
+    assert_close(got, ref, f"combine, out of {T} rows")
