@@ -641,7 +641,9 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       // read-modify-write after every earlier expert's tiles of that column
       // (count per column, in expert order).  The adds are plain fp32 loads
       // and stores, in a fixed order: the combine is deterministic.
-      // Row metadata into LDS (token, gate weight; token -1 past the rows).
+      // Row metadata into LDS: the token (the register-fetch form: its row's
+      // byte offset in out) and the gate weight, with a no-row mark past the
+      // expert's rows.
       // Rows of an expert are sorted by pair id, so two pairs of one token in
       // one expert (an input the combine does not accept) are neighbours.
       if (t == 0) {
@@ -681,8 +683,8 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
         // the destination values and the sums are stored through.  The
         // destination rows of AHEAD blocks are in flight at a time, in
         // registers (the K loop's fragment registers are free here): block
-        // i+AHEAD's are requested right after block i's stores.  Loads and stores
-        // go through a buffer resource over out, so the compiler counts
+        // i+AHEAD's are requested right after block i's stores.  Loads and
+        // stores go through a buffer resource over out, so the compiler counts
         // them in its waits; a lane with nothing to add (a row past the
         // expert's rows, a column past N, a skipped tile) uses an offset past
         // the end of out, which loads 0 and drops the store.
