@@ -330,7 +330,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   // ACT: layer 0 with an activation (a.act); a separate instantiation, so
   // the plain form carries none of its code.
   static_assert(!(ACT && (SCATTER || PULL)), "the activation is a plain layer-0 form");
-  // VEP: the combine's register-fetch epilogue (out below 4 GiB, a.out_records).
+  // VEP: the combine's register-fetch epilogue (out below 2 GiB, a.out_records).
   static_assert(!VEP || SCATTER, "the register-fetch epilogue is the combine's");
   using Eng = Engine<E, BM, BN, KTAIL, NW, 4, NW == 4 ? 2 : 1, false, PULL, BN == 128 ? 3 : 2>;
   // the combine's epilogue also keeps its destination rows in LDS
