@@ -37,8 +37,13 @@ def _route(ids, e0, nl):
 
 @pytest.mark.parametrize("T,E,topk,e0,nl", [(256, 16, 2, 4, 4), (5000, 64, 2, 0, 8),
                                             (3, 8, 1, 0, 8), (1000, 64, 4, 56, 8),
-                                            (20000, 128, 2, 0, 64)])
+                                            (20000, 128, 2, 0, 64), (3000, 64, 2, 3, 5),
+                                            (9000, 96, 2, 8, 48), (40000, 128, 2, 0, 64)])
 def test_route_bit_exact(oracle, T, E, topk, e0, nl):
+    """Chunks of 256 pairs, one workgroup each; expert counts that do not
+    divide the 256 threads summing the chunk histograms (5, 48); and 80000
+    pairs over 64 local experts, whose histograms need chunks of 512 (two
+    rounds per workgroup)."""
     ids, _ = wl.moe_routing(T, E, topk, seed=T + E)
     off, sp = _route(ids, e0, nl)
     roff, rsp = oracle.moe_route(ids, e0, nl)

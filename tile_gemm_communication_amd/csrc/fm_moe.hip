@@ -62,10 +62,10 @@ constexpr int64_t kWsFlags = kWsRoute + kRouteWords;
 constexpr int kMinTileEdge = 128;   // the smallest BM and BN of any combine tile
 static_assert((kWsSink * 4) % 16 == 0, "the sink must be 16-byte aligned");
 
-// Pairs per route workgroup: 2048, doubled until the per-chunk histograms fit
-// the route region.
+// Pairs per route workgroup: one round of kRouteThreads, doubled until the
+// per-chunk histograms fit the route region.
 inline int64_t route_chunk_pairs(int64_t P, int n_local) {
-  int64_t ch = 2048;
+  int64_t ch = kRouteThreads;
   while (std::max<int64_t>(1, cdiv(P, ch)) * n_local > kRouteWords) ch *= 2;
   return ch;
 }
@@ -82,8 +82,8 @@ inline size_t moe_ws_bytes(int64_t pairs, int64_t hidden, int n_local) {
 }
 
 // ---------------------------------------------------------------------------
-// Route: a counting sort over chunks of `ch` consecutive pairs, one
-// workgroup per chunk.
+// Route: a counting sort over chunks of `ch` consecutive pairs (256 unless
+// the histograms need larger chunks), one workgroup per chunk.
 //   count: per-chunk histogram of local experts.
 //   place: every workgroup derives its chunk's first slot per expert from
 //          the histograms (totals -> expert_offsets, plus the counts of the
@@ -118,14 +118,26 @@ __global__ __launch_bounds__(kRouteThreads) void route_place_kernel(
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int c = blockIdx.x;
   if (t < n_local) {
-    int tot = 0, pre = 0;
-    for (int cc = 0; cc < n_chunks; ++cc) {
-      const int v = (int)counts[(int64_t)cc * n_local + t];
-      pre += cc < c ? v : 0;
-      tot += v;
+    s_tot[t] = 0;
+    s_base[t] = 0;
+  }
+  __syncthreads();
+  {
+    // Every thread sums part of the histograms: thread t takes expert
+    // t % n_local of every (S / n_local)-th chunk from t / n_local on, and
+    // adds its totals (all chunks, and the chunks before this one) into LDS.
+    const int S = (kRouteThreads / n_local) * n_local;
+    if (t < S) {
+      const int e = t % n_local;
+      int tot = 0, pre = 0;
+      for (int cc = t / n_local; cc < n_chunks; cc += S / n_local) {
+        const int v = (int)counts[(int64_t)cc * n_local + e];
+        pre += cc < c ? v : 0;
+        tot += v;
+      }
+      if (tot) atomicAdd(&s_tot[e], tot);
+      if (pre) atomicAdd(&s_base[e], pre);
     }
-    s_tot[t] = tot;
-    s_base[t] = pre;
   }
   __syncthreads();
   if (t == 0) {
