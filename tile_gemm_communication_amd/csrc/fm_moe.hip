@@ -1108,14 +1108,16 @@ fm_status_t moe_gather_impl(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t ff
                                     ws, ws_bytes);
   if (st != FM_OK) return st;
   if (hidden < 0 || ffn < 0 || hidden % 8 || ffn % 8) return FM_ERR_INVALID_ARG;
-  // pull mode reads the chunks in place: no gathered X
+  // pull mode reads the chunks in place: no gathered X.  With hidden = 0 the
+  // sum over K is empty (H = act(0) on the local rows): X and W1 may be null.
   if (T > 0 && ffn > 0 &&
-      ((!pull && (!X || !aligned16(X))) || !W1 || !H || !aligned16(W1) || !aligned16(H)))
+      (!H || !aligned16(H) ||
+       (hidden > 0 && ((!pull && (!X || !aligned16(X))) || !W1 || !aligned16(W1)))))
     return FM_ERR_INVALID_ARG;
   if (pull) {
     if (!flags || n_chunks < 1 || n_chunks > 64) return FM_ERR_INVALID_ARG;
     for (int c = 0; c < n_chunks; ++c)
-      if (!pull[c] || !aligned16(pull[c])) return FM_ERR_INVALID_ARG;
+      if (hidden > 0 && (!pull[c] || !aligned16(pull[c]))) return FM_ERR_INVALID_ARG;
   }
   uint8_t pos[64] = {};
   if (flags) {
@@ -1299,8 +1301,10 @@ fm_status_t check_combine_args(fm_dtype_t dt, int64_t T, int64_t hidden, int64_t
   if (hidden < 0 || ffn < 0 || hidden % 8 || ffn % 8 || spin_limit < 0) return FM_ERR_INVALID_ARG;
   if (!expert_offsets) return FM_ERR_INVALID_ARG;
   if (T == 0 || hidden == 0) return FM_OK;
-  if (!H || !W2 || !sorted_pairs || !topk_weights || !out || !aligned16(H) || !aligned16(W2) ||
-      !aligned16(out))
+  // With ffn = 0 the sum over K is empty (each local pair adds weight x 0):
+  // H and W2 may be null.
+  if ((ffn > 0 && (!H || !W2 || !aligned16(H) || !aligned16(W2))) || !sorted_pairs ||
+      !topk_weights || !out || !aligned16(out))
     return FM_ERR_INVALID_ARG;
   if (hidden >= (1ll << 22) || ffn >= (1ll << 22) || T * topk * ffn >= (1ll << 31))
     return FM_ERR_UNSUPPORTED;
