@@ -446,15 +446,24 @@ struct Engine {
   // of this stage; after the wait and barrier, sub-steps 2 and 3 read
   // sub-steps 0 and 1 of stage kt+1 and issue the DMA of stage kt+2 into
   // buffer cur in two halves.  Every read has a whole sub-step more slack.
+  // KIND (two LDS stages only): 0 loads stage kt+2 and reads ahead as
+  // usual; 1 (the step before the last) loads nothing; 2 (the last) loads
+  // and reads ahead nothing.  With two stages every wait drains all loads,
+  // so the steps near the end can skip the loads past K without changing
+  // any wait, and the epilogue finds no load in flight; the main loop's body
+  // stays free of branches.  With three stages the waits count the loads in
+  // flight, so past the end every step loads the last stage again into a
+  // buffer nobody reads (KIND 0 throughout).
+  template <int KIND = 0>
   __device__ __forceinline__ void step2(int kt) {
     const int cur = kt % NSTAGE, nxt = (kt + 1) % NSTAGE;
     substep_g(0, cur, 2, 2, true, -1, 0, 0, 0);
     substep_g(1, cur, 3, 3, true, -1, 0, 0, 0);
     wait_stage();
     __syncthreads();
-    const int dk = min(kt + NSTAGE, KT - 1);
-    substep_g(2, nxt, 0, 0, true, dk, cur, 0, DMA / 2);
-    substep_g(3, nxt, 1, 1, true, dk, cur, DMA / 2, DMA);
+    const int dk = KIND != 0 ? -1 : min(kt + NSTAGE, KT - 1);
+    substep_g(2, nxt, 0, 0, KIND != 2, dk, cur, 0, DMA / 2);
+    substep_g(3, nxt, 1, 1, KIND != 2, dk, cur, DMA / 2, DMA);
   }
 
   // Before the barrier of K step kt: stage kt+1 has landed (the later stages
@@ -476,10 +485,10 @@ struct Engine {
   //                   complete and buffer cur is drained;
   //   sub-step 3:     MFMAs while sub-step 0 of stage kt+1 is read and the
   //                   DMA of stage kt+2 is issued into buffer cur.
-  // Without a K tail the DMA is unconditional: past the end it re-loads the
-  // last stage into a buffer nobody reads again (each wave only ever writes
-  // its own LDS rows, and its loads complete in order, so a later tile's
-  // data is never overwritten).  The accumulators thus stay in one place.
+  // Without a K tail the loads follow KIND as in step2 (each wave only ever
+  // writes its own LDS rows, and its loads complete in order, so a later
+  // tile's data is never overwritten).
+  template <int KIND = 0>
   __device__ __forceinline__ void step(int kt) {
     const int cur = kt % NSTAGE;
     if constexpr (MF16) {
@@ -501,7 +510,8 @@ struct Engine {
     wait_stage();
     __syncthreads();
     if constexpr (!KTAIL) {
-      substep(1, (kt + 1) % NSTAGE, 0, true, min(kt + NSTAGE, KT - 1), cur);
+      const int dk = KIND != 0 ? -1 : min(kt + NSTAGE, KT - 1);
+      substep(1, (kt + 1) % NSTAGE, 0, KIND != 2, dk, cur);
     } else {
       if (kt + 2 < KT) dma(kt + 2, cur, kt + 3 == KT);
       substep(1, cur ^ 1, 0, true, -1, 0);
@@ -545,11 +555,22 @@ struct Engine {
     __syncthreads();
     after_first_wait();
     read_frags(0, 0, 0);
-    if constexpr (DEPTH == 2) {
-      read_frags(0, 1, 1);
-      for (int kt = 0; kt < KT; ++kt) step2(kt);
+    if constexpr (DEPTH == 2) read_frags(0, 1, 1);
+    if constexpr (NSTAGE == 2 && !KTAIL && !MF16) {
+      // the last two steps load nothing past K (KT >= 1 here)
+      int kt = 0;
+      for (; kt + 2 < KT; ++kt) {
+        if constexpr (DEPTH == 2) step2<0>(kt); else step<0>(kt);
+      }
+      if (kt + 1 < KT) {
+        if constexpr (DEPTH == 2) step2<1>(kt); else step<1>(kt);
+        ++kt;
+      }
+      if constexpr (DEPTH == 2) step2<2>(kt); else step<2>(kt);
     } else {
-      for (int kt = 0; kt < KT; ++kt) step(kt);
+      for (int kt = 0; kt < KT; ++kt) {
+        if constexpr (DEPTH == 2) step2(kt); else step(kt);
+      }
     }
   }
 
