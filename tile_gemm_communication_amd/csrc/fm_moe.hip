@@ -254,54 +254,90 @@ __device__ __forceinline__ float apply_act(int act, float x) {
   }
 }
 
-// Called by one thread: wait until every tile of an expert before e in
-// column tn whose token range overlaps that of global M-tile gm has published
-// this call's epoch, then acquire.  Beyond kMaxMTiles tiles the ranges are not
-// cached and every earlier tile of the column is waited for.
-// Returns false if the wait gave up: after spin_limit polls of one flag (this
-// thread then writes FM_ERR_TIMEOUT to err_word and marks the launch aborted
-// in the workspace), or once another workgroup has marked it aborted.
+// Called by the 64 lanes of one wave: wait until every tile of an expert
+// before e in column tn whose token range overlaps that of global M-tile gm
+// has published this call's epoch, then acquire.  The tiles to wait for are
+// a range of global M-tiles per earlier expert: lane ep finds expert ep's
+// range, a scan over the wave lays the ranges end to end in s_wr ([0, 64):
+// first tile, [64, 128): first position), and lane l polls positions l,
+// l + 64, ..., so the polls are in flight together (one lane polling them
+// in turn paid a round trip per flag).  Beyond kMaxMTiles tiles the ranges
+// are not cached and every earlier tile of the column is waited for.
+// Returns false (on every lane) if the wait gave up: after spin_limit polls
+// of one flag (that lane then writes FM_ERR_TIMEOUT to err_word and marks
+// the launch aborted in the workspace), or once another workgroup has
+// marked it aborted.
 __device__ __forceinline__ bool wait_token_range(const MoeArgs& a, const int* s_tile0,
                                                  const int* s_ftok, const int* s_ltok,
-                                                 int total_m, int e, int gm, int tn,
-                                                 uint32_t epoch) {
+                                                 int* s_wr, int total_m, int e, int gm, int tn,
+                                                 uint32_t epoch, int lane) {
   const bool cached = total_m <= kMaxMTiles;
   const int lo_tok = cached ? s_ftok[gm] : 0;
   const int hi_tok = cached ? s_ltok[gm] : 0x7FFFFFFF;
   uint32_t* const abort_word = a.ws + kCtlAbort;
-  for (int ep = 0; ep < e; ++ep) {
-    const int g0 = s_tile0[ep] / a.tiles_n, g1 = s_tile0[ep + 1] / a.tiles_n;
-    int m = g0;
-    if (cached) {   // first tile of expert ep whose last token is >= lo_tok
-      int lo = g0, hi = g1;
-      while (lo < hi) {
+  // this lane's expert (e <= 63 < 64): its tiles [m_lo, m_hi) overlap
+  int m_lo = 0, cnt = 0;
+  if (lane < e) {
+    const int g0 = s_tile0[lane] / a.tiles_n, g1 = s_tile0[lane + 1] / a.tiles_n;
+    int lo = g0, hi = g1;
+    if (cached) {
+      while (lo < hi) {   // first tile whose last token is >= lo_tok
         const int mid = (lo + hi) >> 1;
         if (s_ltok[mid] < lo_tok) lo = mid + 1; else hi = mid;
       }
-      m = lo;
+      m_lo = lo;
+      hi = g1;
+      while (lo < hi) {   // first tile whose first token is > hi_tok
+        const int mid = (lo + hi) >> 1;
+        if (s_ftok[mid] <= hi_tok) lo = mid + 1; else hi = mid;
+      }
+      cnt = lo - m_lo;
+    } else {
+      m_lo = g0;
+      cnt = g1 - g0;
     }
-    for (; m < g1 && (!cached || s_ftok[m] <= hi_tok); ++m) {
-      const uint32_t* f = a.tile_done + (int64_t)m * a.tiles_n + tn;
-      int64_t polls = 0;
-      while (!flag_reached(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                           epoch)) {
-        __builtin_amdgcn_s_sleep(2);
-        ++polls;
-        if ((polls & 63) == 0 &&
-            __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch)
-          return false;
-        if (polls > a.spin_limit) {
-          if (a.err_word)
-            __hip_atomic_store(a.err_word, (int32_t)FM_ERR_TIMEOUT, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(abort_word, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          return false;
-        }
+  }
+  int incl = cnt;   // inclusive scan over the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
+  }
+  const int total = __shfl(incl, 63);
+  s_wr[lane] = m_lo;
+  s_wr[64 + lane] = incl - cnt;
+  bool ok = true;
+  for (int j = lane; ok && j < total; j += 64) {
+    int lo = 0, hi = e - 1;   // the last expert whose first position is <= j
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_wr[64 + mid] <= j) lo = mid; else hi = mid - 1;
+    }
+    const int m = s_wr[lo] + (j - s_wr[64 + lo]);
+    const uint32_t* f = a.tile_done + (int64_t)m * a.tiles_n + tn;
+    int64_t polls = 0;
+    while (!flag_reached(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                         epoch)) {
+      __builtin_amdgcn_s_sleep(2);
+      ++polls;
+      if ((polls & 63) == 0 &&
+          __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) {
+        ok = false;
+        break;
+      }
+      if (polls > a.spin_limit) {
+        if (a.err_word)
+          __hip_atomic_store(a.err_word, (int32_t)FM_ERR_TIMEOUT, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(abort_word, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = false;
+        break;
       }
     }
   }
+  ok = __all(ok);
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return true;
+  return ok;
 }
 
 // Combine tile queues.  The N columns are dealt to Q = min(4, tiles_n)
@@ -356,6 +392,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
   // combine: first and last token of every M-tile (all experts, in order)
   __shared__ int s_ftok[SCATTER ? kMaxMTiles : 1];
   __shared__ int s_ltok[SCATTER ? kMaxMTiles : 1];
+  __shared__ int s_wr[SCATTER ? 128 : 1];   // combine: wave 0's table of tiles to wait for
   __shared__ int s_abort;
   // combine: this tile has a row whose token also has the previous row (two
   // pairs of one token in one expert), and the next ticket (by tile parity)
@@ -676,11 +713,12 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_kernel(const MoeArgs a) {
       // this tile's tokens, and are usually long finished (each expert walks
       // its tokens in order, about one expert's worth of tiles earlier).
       const int gm = s_tile0[e] / a.tiles_n + tm;   // this tile's global M-tile
-      if (t == 0)
-        s_abort = (e > 0 && !wait_token_range(a, s_tile0, s_ftok, s_ltok, total_m, e, gm, tn,
-                                               epoch))
-                      ? 1
-                      : 0;
+      if (t < 64) {   // wave 0
+        const bool ok =
+            e == 0 ||
+            wait_token_range(a, s_tile0, s_ftok, s_ltok, s_wr, total_m, e, gm, tn, epoch, t);
+        if (t == 0) s_abort = ok ? 0 : 1;
+      }
       __syncthreads();
       // A wait that gave up ends this workgroup's work (err_word is set, out
       // is undefined); a duplicated token skips the tile's adds and is
