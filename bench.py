@@ -46,12 +46,12 @@ PEAK_TFLOPS = 2516.6          # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 
 # known-size copy (`bench.py --copy-probe 256`) gives: FETCH_SIZE x2.0,
 # WRITE_SIZE x1.0.  Keyed by the digest of the kernel sources they were taken
 # on: after any change to csrc/ they no longer apply and traffic is null.
-TRAFFIC_DIGEST = "eeb2e609ef831e79"
+TRAFFIC_DIGEST = "5770d0f34cc2c329"
 TRAFFIC_BYTES = {             # op name -> (read bytes, written bytes) per call
-    "ag_gemm": (1111424891, 50328564),
-    "gemm_rs": (1117333720, 201327900),
-    "moe_gather_gemm": (1347522764, 172613346),
-    "moe_gemm_scatter": (2216530460, 501668013),
+    "ag_gemm": (1119624959, 50328564),
+    "gemm_rs": (1115677704, 201317328),
+    "moe_gather_gemm": (1337121233, 172566322),
+    "moe_gemm_scatter": (2224136528, 501668013),
 }
 
 
