@@ -431,6 +431,126 @@ def pin_golden_moe(o):
     assert np.array_equal(out, np.asarray(g["expected_out"], dtype=np.float64))
 
 
+
+# ---------------------------------------------------------------------------
+# every-element forms (oracle/full.py): C loops, brute force, fixtures
+# ---------------------------------------------------------------------------
+
+def pin_full_decode_exhaustive(o):
+    from oracle import full
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    for dt in (F16, BF16):
+        mine = full.decode(dt, allbits)
+        ref = o.decode(dt, allbits)
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(mine), nan)
+        assert np.array_equal(mine[~nan], ref[~nan])
+        assert np.array_equal(np.signbit(mine[~nan]), np.signbit(ref[~nan]))
+
+
+def pin_full_dense_vs_loops(o):
+    from oracle import full
+    for (M, N, K), dt in itertools.product([(1, 1, 1), (3, 5, 7), (33, 17, 129), (64, 40, 48)],
+                                           (F16, BF16)):
+        A, B = wl.gemm_inputs(M, N, K, dt, seed=M * 1000 + N * 10 + K + 7)
+        assert _rel(full.gemm(dt, A, B), o.gemm(dt, A, B)) <= 1e-12, (M, N, K, dt)
+    chunks, W, order = wl.ag_inputs(4, 8, 24, 32, BF16, seed=33, arrival="random")
+    assert _rel(full.ag_gemm(BF16, list(chunks), W),
+                o.ag_gemm(BF16, list(chunks), W, arrival=order)) <= 1e-12
+    A, W, seeds = wl.rs_inputs(32, 24, 40, 4, F16, seed=44)
+    for got, ref in zip(full.gemm_rs(F16, A, W, list(seeds)), o.gemm_rs(F16, A, W, list(seeds))):
+        assert np.abs(got - ref).max() <= 1e-12
+
+
+def pin_full_dense_bruteforce(o):
+    from oracle import full
+    A = wl.normal_bits((3, 4), 23, F16)
+    B = wl.normal_bits((4, 5), 24, F16)
+    a = np_decode(A, F16).tolist()
+    b = np_decode(B, F16).tolist()
+    C = full.gemm(F16, A, B)
+    for i in range(3):
+        for j in range(5):
+            s = sum(a[i][k] * b[k][j] for k in range(4))
+            assert abs(C[i, j] - s) <= 1e-14 * max(1.0, abs(s))
+    # two ranks' slices, each seeded, on a K that does not divide evenly
+    A2 = wl.normal_bits((4, 3), 25, BF16)
+    W2 = wl.normal_bits((3, 2), 26, BF16)
+    seeds = [np.full((2, 2), 1.5, np.float32), np.full((2, 2), -2.0, np.float32)]
+    a2, w2 = np_decode(A2, BF16), np_decode(W2, BF16)
+    dst = full.gemm_rs(BF16, A2, W2, seeds)
+    for r in range(2):
+        for i in range(2):
+            for j in range(2):
+                s = float(seeds[r][i, j]) + sum(a2[2 * r + i, k] * w2[k, j] for k in range(3))
+                assert abs(dst[r][i, j] - s) <= 1e-14 * max(1.0, abs(s))
+
+
+def pin_full_moe_bruteforce(o):
+    from oracle import full
+    for seed, topk, dt in [(67, 2, BF16), (68, 3, F16)]:
+        inp, e0, nl, _, _ = _tiny_moe(seed=seed, topk=topk, dt=dt)
+        off, sp = o.moe_route(inp["topk_ids"], e0, nl)
+        H = full.moe_layer0(dt, inp["X"], inp["W1"], sp, off, topk)
+        x = np_decode(inp["X"], dt)
+        w1 = np_decode(inp["W1"], dt)
+        assert H.shape == (int(off[-1]), w1.shape[2]) and H.shape[0] > 0
+        for e in range(nl):
+            for r in range(off[e], off[e + 1]):
+                assert np.abs(H[r] - x[sp[r] // topk] @ w1[e]).max() <= 1e-12
+        assert np.abs(H - o.moe_layer0(dt, inp["X"], inp["W1"], sp, off, topk)).max() <= 1e-12
+        Hb = o.round_bf16(H) if dt == BF16 else o.round_f16(H)
+        ids, wts = inp["topk_ids"], inp["topk_weights"]
+        out = full.moe_layer1(dt, Hb, inp["W2"], ids, wts, sp, off, inp["out_seed"], e0)
+        h = np_decode(Hb, dt)
+        w2 = np_decode(inp["W2"], dt)
+        pos = {int(p): r for r, p in enumerate(sp)}
+        ref = inp["out_seed"].astype(np.float64).copy()
+        for t in range(ids.shape[0]):
+            for k in range(topk):
+                e = int(ids[t, k]) - e0
+                if 0 <= e < nl:
+                    ref[t] += float(wts[t, k]) * (h[pos[t * topk + k]] @ w2[e])
+        assert np.abs(out - ref).max() <= 1e-12
+        assert np.abs(out - o.moe_layer1(dt, Hb, inp["W2"], ids, wts, sp, off, inp["out_seed"],
+                                         e0)).max() <= 1e-12
+
+
+def pin_full_moe_nothing_local(o):
+    from oracle import full
+    inp, _, nl, topk, dt = _tiny_moe(seed=69)
+    e0 = 64                                   # no expert id reaches this range
+    off, sp = o.moe_route(inp["topk_ids"], e0, nl)
+    H = full.moe_layer0(dt, inp["X"], inp["W1"], sp, off, topk)
+    assert H.shape == (0, inp["W1"].shape[2])
+    out = full.moe_layer1(dt, np.zeros((0, H.shape[1]), np.uint16), inp["W2"], inp["topk_ids"],
+                          inp["topk_weights"], sp, off, inp["out_seed"], e0)
+    assert np.array_equal(out, inp["out_seed"].astype(np.float64))
+
+
+def pin_full_golden(o):
+    from oracle import full
+    g = _load_golden("tiny_mlp_handworked.json")
+    for dt in (F16, BF16):
+        ag = g["ag_gemm"]
+        C = full.ag_gemm(dt, [_bits(c, dt) for c in ag["chunks"]], _bits(ag["W"], dt))
+        assert np.array_equal(C, np.asarray(ag["expected"], dtype=np.float64))
+        rs = g["gemm_rs"]
+        seeds = [np.asarray(s, dtype=np.float32) for s in rs["seeds"]]
+        dst = full.gemm_rs(dt, _bits(rs["A"], dt), _bits(rs["W"], dt), seeds)
+        for d, want in zip(dst, rs["expected"]):
+            assert np.array_equal(d, np.asarray(want, dtype=np.float64))
+    m = _load_golden("moe_handworked.json")
+    ids = np.asarray(m["topk_ids"], dtype=np.int32)
+    wts = np.asarray(m["topk_weights"], dtype=np.float32)
+    off = np.asarray(m["expected_offsets"], dtype=np.int32)
+    sp = np.asarray(m["expected_sorted_pairs"], dtype=np.int32)
+    H = full.moe_layer0(BF16, _bits(m["X"], BF16), _bits(m["W1"], BF16), sp, off, 2)
+    assert np.array_equal(H, np.asarray(m["expected_H"], dtype=np.float64))
+    out = full.moe_layer1(BF16, _bits(m["expected_H"], BF16), _bits(m["W2"], BF16), ids, wts, sp,
+                          off, np.asarray(m["seed"], dtype=np.float32), 2)
+    assert np.array_equal(out, np.asarray(m["expected_out"], dtype=np.float64))
+
 ALL_PINS = [
     pin_decode_exhaustive, pin_round_f16, pin_round_bf16,
     pin_gemm_numpy, pin_gemm_identity, pin_gemm_bruteforce, pin_gemm_entries,
@@ -442,4 +562,6 @@ ALL_PINS = [
     pin_moe_layer1_token_loop,
     pin_moe_identical_experts_chain, pin_moe_ep_ranks_sum,
     pin_golden_mlp, pin_golden_moe,
+    pin_full_decode_exhaustive, pin_full_dense_vs_loops, pin_full_dense_bruteforce,
+    pin_full_moe_bruteforce, pin_full_moe_nothing_local, pin_full_golden,
 ]

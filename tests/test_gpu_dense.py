@@ -1,11 +1,13 @@
 """GPU parity of the dense operators (fm_gemm, fm_ag_gemm, fm_gemm_rs) against
 the CPU oracle, through the C ABI, on seeded inputs: small shapes spanning
 several tiles with ragged tails and the edge cases, then the full-size TP=8
-rank-0 workloads on sampled outputs."""
+rank-0 workloads on every output element (the oracle's every-element forms)
+and on sampled outputs of the oracle's loops."""
 import numpy as np
 import pytest
 
 import workloads as wl
+from oracle import full
 from gpu_util import (BF16, F16, Arrival, assert_close, bits16, dev16, devf32, host64, say,
                       sample_coords)
 
@@ -237,6 +239,7 @@ def test_full_dense_gemm(oracle):
     rows, cols = sample_coords(M, N, 3000, seed=1)
     assert_close(_at(C, rows, cols), oracle.gemm_entries(F16, A, B, rows, cols),
                  "full gemm samples")
+    assert_close(host64(C), full.gemm(F16, A, B), "full gemm, every element")
 
 
 def test_full_ag_gemm(oracle):
@@ -254,6 +257,7 @@ def test_full_ag_gemm(oracle):
     rows, cols = sample_coords(n * Mc, N, 3000, seed=2, tile=(256, 128))
     assert_close(_at(C, rows, cols), oracle.gemm_entries(F16, X, W, rows, cols),
                  "full ag samples")
+    assert_close(host64(C), full.ag_gemm(F16, list(chunks), W), "full ag, every element")
     ref = torch.empty_like(C)
     import tile_gemm_communication_amd as fm
     fm.fm_gemm(arr.X, Wd, ref)
@@ -273,6 +277,8 @@ def test_full_gemm_rs(oracle):
     delta = np.array([got[r // Ms][r % Ms, cc] - seeds[r // Ms][r % Ms, cc]
                       for r, cc in zip(rows, cols)])
     assert_close(delta, ref, "full rs samples")
+    for p, want in enumerate(full.gemm_rs(F16, A, W, list(seeds))):
+        assert_close(got[p] - seeds[p], want - seeds[p], f"full rs slice {p}, every element")
 
 
 def _cus():

@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 
 import workloads as wl
+from oracle import full
 from gpu_util import BF16, F16, assert_close, bits16, dev16, devf32, host64, say, side_stream
 
 pytestmark = pytest.mark.gpu
@@ -173,23 +174,44 @@ def test_moe_one_hot_expert(oracle):
     assert_close(host64(out) - inp["out_seed"], ref - inp["out_seed"], "one-hot combine")
 
 
+_EP8: dict = {}
+
+
+def _ep8_reference(oracle):
+    """EP=8 rank-0 inputs, their routing and every row of layer 0 from the
+    oracle's every-element form, built once per process and shared by the
+    full-size tests of every layer-0 form."""
+    if not _EP8:
+        c = wl.MOE_EP8
+        inp = wl.moe_inputs(c["T"], c["hidden"], c["ffn"], c["n_experts"], c["n_local"],
+                            c["topk"], BF16, seed=c["seed"], zipf_s=c["zipf_s"])
+        e0 = c["rank"] * c["n_local"]
+        roff, rsp = oracle.moe_route(inp["topk_ids"], e0, c["n_local"])
+        say("full moe EP=8: oracle layer 0, every row")
+        _EP8.update(inp=inp, e0=e0, roff=roff, rsp=rsp,
+                    H=full.moe_layer0(BF16, inp["X"], inp["W1"], rsp, roff, c["topk"]))
+    return _EP8
+
+
 def test_full_moe_rank0(oracle):
     """EP=8 rank 0: 16384 tokens x 4096, 64 experts top-2 (log-Zipf bias), 8
     local experts, ffn 2816, bf16, chained on the GPU: layer 0, then the
-    combine on the GPU's own H.  Routing bit-exact; layer 0 on sampled rows;
-    the combine on every token of each expert's first and last row tile, at
-    least 100 tokens with both pairs local and random tokens (over 512 in
-    all), against the oracle's combine run on the GPU's H bits."""
+    combine on the GPU's own H.  Routing bit-exact; every row of layer 0 and
+    every token of the combine against the oracle's every-element forms (the
+    combine run on the GPU's H bits); sampled rows of layer 0 and over 512
+    tokens of the combine (every token of each expert's first and last row
+    tile, at least 100 with both pairs local, random ones) against the
+    oracle's loops."""
     import torch
     c = wl.MOE_EP8
     say("full moe EP=8 rank 0")
-    inp = wl.moe_inputs(c["T"], c["hidden"], c["ffn"], c["n_experts"], c["n_local"], c["topk"],
-                        BF16, seed=c["seed"], zipf_s=c["zipf_s"])
-    e0, nl = c["rank"] * c["n_local"], c["n_local"]
-    roff, rsp = oracle.moe_route(inp["topk_ids"], e0, nl)
+    ep8 = _ep8_reference(oracle)
+    inp, e0, nl = ep8["inp"], ep8["e0"], c["n_local"]
+    roff, rsp = ep8["roff"], ep8["rsp"]
     off, sp, H, out = _moe_run(inp, e0, nl, BF16)
     rows = int(roff[-1])
     assert np.array_equal(off, roff) and np.array_equal(sp[:rows], rsp)
+    assert_close(host64(H[:rows]), ep8["H"], "full layer0, every row")
     rng = np.random.default_rng(7)
     srows = np.unique(np.concatenate([rng.integers(0, rows, 48), roff[:-1], roff[1:] - 1]))
     srows = srows[(srows >= 0) & (srows < rows)]
@@ -217,6 +239,10 @@ def test_full_moe_rank0(oracle):
     tidx = torch.from_numpy(toks).to("cuda:0")
     assert_close(host64(out[tidx]) - inp["out_seed"][toks], ref - inp["out_seed"][toks],
                  "full combine tokens")
+    want = full.moe_layer1(BF16, Hbits, inp["W2"], ids, inp["topk_weights"], rsp, roff,
+                           inp["out_seed"], e0)
+    assert_close(host64(out) - inp["out_seed"], want - inp["out_seed"],
+                 "full combine, every token")
 
 
 @pytest.mark.parametrize("T,hidden,ffn,E,nl,topk", [(4096, 1024, 512, 16, 8, 2),
@@ -599,8 +625,9 @@ def test_moe_ag_producers(oracle, T, n, n_prod, local):
 
 def test_full_moe_ag_producers_rank0(oracle):
     """EP=8 rank 0 with the default producer count, the local chunk in place
-    and seven copied: sampled rows against the oracle, bit-identical to the
-    non-fused layer 0, and a second call on the same counters."""
+    and seven copied: every row against the oracle's every-element form,
+    sampled rows against its loops, bit-identical to the non-fused layer 0,
+    and a second call on the same counters."""
     import torch
     import tile_gemm_communication_amd as fm
     c = wl.MOE_EP8
@@ -621,6 +648,8 @@ def test_full_moe_ag_producers_rank0(oracle):
     Hs = oracle.moe_layer0_rows(BF16, inp["X"], inp["W1"], rsp, roff, 2, srows)
     idx = torch.from_numpy(srows).to("cuda:0")
     assert_close(host64(H[idx]), Hs, "full moe ag producers rows")
+    assert_close(host64(H[:rows]), _ep8_reference(oracle)["H"],
+                 "full moe ag producers, every row")
     H2 = torch.zeros_like(H)
     sp2 = torch.full((c["T"] * 2,), -1, dtype=torch.int32, device="cuda:0")
     off2 = torch.zeros(c["n_local"] + 1, dtype=torch.int32, device="cuda:0")
@@ -731,8 +760,9 @@ def test_moe_ag_pull_withheld_chunk_times_out():
 
 def test_full_moe_ag_pull_link_paced(oracle):
     """EP=8 rank 0 reading the 8 owners' 2048-token chunks in place, signalled
-    in ring order at the one-link rate (16 MiB at 153 GB/s apart): sampled rows
-    against the oracle, bit-identical to the non-fused layer 0."""
+    in ring order at the one-link rate (16 MiB at 153 GB/s apart): every row
+    against the oracle's every-element form, sampled rows against its loops,
+    bit-identical to the non-fused layer 0."""
     import torch
     import tile_gemm_communication_amd as fm
     c = wl.MOE_EP8
@@ -754,6 +784,7 @@ def test_full_moe_ag_pull_link_paced(oracle):
     Hs = oracle.moe_layer0_rows(BF16, inp["X"], inp["W1"], rsp, roff, 2, srows)
     idx = torch.from_numpy(srows).to("cuda:0")
     assert_close(host64(H[idx]), Hs, "full moe ag pull rows")
+    assert_close(host64(H[:rows]), _ep8_reference(oracle)["H"], "full moe ag pull, every row")
     H2 = torch.zeros_like(H)
     sp2 = torch.full((c["T"] * 2,), -1, dtype=torch.int32, device="cuda:0")
     off2 = torch.zeros(c["n_local"] + 1, dtype=torch.int32, device="cuda:0")
@@ -777,8 +808,9 @@ def test_moe_ag_withheld_chunk_times_out():
 
 def test_full_moe_ag_rank0(oracle):
     """EP=8 rank 0 with the 16384 tokens gathered from 8 ranks (2048 each,
-    the local chunk first, then ring order): routing bit-exact, sampled rows
-    against the oracle, and bit-identical to the non-fused layer 0."""
+    the local chunk first, then ring order): routing bit-exact, every row
+    against the oracle's every-element form, sampled rows against its loops,
+    and bit-identical to the non-fused layer 0."""
     import torch
     import tile_gemm_communication_amd as fm
     from gpu_util import Arrival
@@ -802,6 +834,7 @@ def test_full_moe_ag_rank0(oracle):
     Hs = oracle.moe_layer0_rows(BF16, inp["X"], inp["W1"], rsp, roff, 2, srows)
     idx = torch.from_numpy(srows).to("cuda:0")
     assert_close(host64(H[idx]), Hs, "full moe ag rows")
+    assert_close(host64(H[:rows]), _ep8_reference(oracle)["H"], "full moe ag, every row")
     H2 = torch.zeros_like(H)
     sp2 = torch.full((c["T"] * 2,), -1, dtype=torch.int32, device="cuda:0")
     off2 = torch.zeros(c["n_local"] + 1, dtype=torch.int32, device="cuda:0")
