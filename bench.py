@@ -90,6 +90,12 @@ def parse():
     ap.add_argument("--parts", type=int, default=1, choices=(1, 2, 4, 8),
                     help="communication parts per pushed chunk, each with its own flag "
                          "(finer communication tiles)")
+    ap.add_argument("--link-parts", type=int, default=2, choices=(1, 2, 4, 8),
+                    help="row blocks per chunk in the link-paced pull schedules, each "
+                         "signalled once its bytes have crossed the link (2: one 256-row "
+                         "tile row of the AllGather-GEMM)")
+    ap.add_argument("--moe-link-parts", type=int, default=4, choices=(1, 2, 4, 8),
+                    help="token blocks per chunk in the link-paced pull of MoE layer 0")
     ap.add_argument("--arrival", choices=("kernel", "dma"), default="kernel",
                     help="emulated peer push: fm_chunk_push (copy kernel) or "
                          "fm_chunk_push_dma (copy engines, no compute units)")
@@ -139,6 +145,8 @@ class Workload:
         # published as `parts` row blocks (pull mode and the in-launch
         # producers use the first n flags, one per chunk)
         self.parts = 1
+        self.link_parts = 1
+        self.moe_link_parts = 1
         self.flags = torch.zeros(self.n * 8, dtype=torch.int32, device=dev)
         self.counters = torch.zeros(self.n * 8, dtype=torch.int32, device=dev)
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -291,6 +299,42 @@ def check_err(w, what):
     code = int(w.err.item())
     if code != 0:
         raise RuntimeError(f"{what}: a kernel reported {fm.status_str(code)}")
+
+
+def time_rounds(variants, iters, rounds=3, warmup=3):
+    """Median over `rounds` passes of each variant's median time (ms).  The
+    variants take turns within each pass, so a clock that drifts during the
+    run (the chip is power-limited) moves them all alike and the differences
+    (ECT) stay fair."""
+    per = {name: [] for name, _ in variants}
+    for _ in range(rounds):
+        for name, fn in variants:
+            per[name].append(time_loop(fn, iters, warmup)[0])
+    return {name: sorted(v)[len(v) // 2] for name, v in per.items()}
+
+
+def link_schedule(order, parts, t_link, kind):
+    """Arrival times of the chunks' row blocks in the link-paced pull.
+
+    The local chunk (order[0]) is in place at t = 0.  A chunk crosses one
+    link in t_link, so its row block q of `parts` has landed (q+1)/parts of
+    t_link after its transfer began.  Direct: every peer sends over a link of
+    its own, all starting at 0.  Ring: the chunk at ring position a >= 1
+    starts at (a-1) * t_link.  Returns the block indices (c * parts + q)
+    sorted by arrival and their times in ns."""
+    t = {}
+    for a, c in enumerate(order):
+        start = 0 if kind == "direct" else (a - 1) * t_link
+        for q in range(parts):
+            t[c * parts + q] = 0 if a == 0 else int(start + (q + 1) * t_link // parts)
+    seq = sorted(t, key=lambda i: (t[i], i))
+    return seq, [t[i] for i in seq]
+
+
+def part_views(chunks, parts):
+    """Row block q of chunk c at index c * parts + q (views, no copies)."""
+    r = chunks[0].shape[0] // parts
+    return [x[q * r:(q + 1) * r] for x in chunks for q in range(parts)]
 
 
 def time_loop(fn, iters, warmup):
@@ -446,9 +490,10 @@ def ect_block(w, iters):
             fm.fm_gemm(w.X[rows], w.W1, w.Out1[rows])
 
     log("ECT: AllGather-GEMM")
-    for name, fn in [("nonsplit_fm_gemm", ns_fm), ("nonsplit_hipblaslt", ns_blas),
-                     ("fused", fused), ("naive_chunked", naive), ("producers", producers)]:
-        med, best = time_loop(fn, iters, 3)
+    meds = time_rounds([("nonsplit_fm_gemm", ns_fm), ("nonsplit_hipblaslt", ns_blas),
+                        ("fused", fused), ("naive_chunked", naive), ("producers", producers)],
+                       iters)
+    for name, med in meds.items():
         res[f"ag_{name}_ms"] = round(med, 4)
     nonsplit = min(res["ag_nonsplit_fm_gemm_ms"], res["ag_nonsplit_hipblaslt_ms"])
     res["ag_ect_ms"] = round(res["ag_fused_ms"] - nonsplit, 4)
@@ -461,43 +506,62 @@ def ect_block(w, iters):
     # --- AllGather-GEMM in pull mode, chunks signalled at link speed --------
     # One xGMI link moves a 12.58 MB chunk in t_link = bytes / 153 GB/s.  Ring:
     # the chunk at position a lands at a * t_link.  Direct: every peer pushes
-    # over its own link, so all seven land at t_link.  The chunks are read in
-    # place from the peers' buffers: no copy competes with the GEMM.
+    # over its own link, so all seven land at t_link.  Each chunk is signalled
+    # as w.link_parts row blocks, block q once (q+1)/parts of it has crossed
+    # the link; the whole-chunk figures (one signal per chunk) are kept beside
+    # them.  The chunks are read in place from the peers' buffers: no copy
+    # competes with the GEMM.
     t_link = int(w.Mc * w.K1 * 2 / LINK_BYTES_PER_S * 1e9)
-    sched = {"ring": [a * t_link for a in range(w.n)],
-             "direct": [0] + [t_link] * (w.n - 1)}
 
-    def pull(times):
+    def pull(kind, parts):
+        seq, times = link_schedule(w.order, parts, t_link, kind)
+        views = part_views(w.peers, parts)
+        flags = w.flags[:w.n * parts]
+
         def fn():
             w.epoch += 1
             s = w.sides[0]
             s.wait_stream(cs)
-            fm.fm_chunk_signal_paced(w.flags[:w.n], times, w.epoch, order=w.order, stream=s)
-            fm.fm_ag_gemm_pull(w.peers, w.W1, w.Out1, w.flags[:w.n], w.epoch, order=w.order,
-                               err_word=w.err)
+            fm.fm_chunk_signal_paced(flags, times, w.epoch, order=seq, stream=s)
+            fm.fm_ag_gemm_pull(views, w.W1, w.Out1, flags, w.epoch, order=seq, err_word=w.err)
             cs.wait_stream(s)
         return fn
 
-    def pull_naive(times):
+    def pull_naive(kind):
+        seq, times = link_schedule(w.order, 1, t_link, kind)
+
         def fn():
             w.epoch += 1
             s = w.sides[0]
             s.wait_stream(cs)
-            fm.fm_chunk_signal_paced(w.flags[:w.n], times, w.epoch, order=w.order, stream=s)
+            fm.fm_chunk_signal_paced(w.flags[:w.n], times, w.epoch, order=seq, stream=s)
             cs.wait_stream(s)                   # the whole AllGather first
             fm.fm_gemm(w.X, w.W1, w.Out1)
         return fn
 
     log("ECT: pull-mode AllGather-GEMM, link-paced arrival")
     res["pull_link_chunk_us"] = round(t_link / 1e3, 1)
-    for name, times in sched.items():
-        med, _ = time_loop(pull(times), iters, 3)
-        res[f"pull_{name}_fused_ms"] = round(med, 4)
-        med, _ = time_loop(pull_naive(times), iters, 3)
-        res[f"pull_{name}_gather_then_gemm_ms"] = round(med, 4)
-        res[f"pull_{name}_ect_ms"] = round(res[f"pull_{name}_fused_ms"] - nonsplit, 4)
+    res["pull_link_parts"] = w.link_parts
+    variants = [("nonsplit", ns_fm)]
+    for name in ("ring", "direct"):
+        variants.append((f"{name}_fused", pull(name, w.link_parts)))
+        if w.link_parts != 1:
+            variants.append((f"{name}_fused_whole_chunks", pull(name, 1)))
+        variants.append((f"{name}_gather_then_gemm", pull_naive(name)))
+    meds = time_rounds(variants, iters)
+    # baseline: the lower of the non-split GEMM timed in these passes and the
+    # one of the AllGather passes above
+    ns_pull = min(meds.pop("nonsplit"), nonsplit)
+    res["pull_nonsplit_ms"] = round(ns_pull, 4)
+    for key, med in meds.items():
+        res[f"pull_{key}_ms"] = round(med, 4)
+    for name in ("ring", "direct"):
+        res[f"pull_{name}_ect_ms"] = round(res[f"pull_{name}_fused_ms"] - ns_pull, 4)
+        if w.link_parts != 1:
+            res[f"pull_{name}_ect_whole_chunks_ms"] = round(
+                res[f"pull_{name}_fused_whole_chunks_ms"] - ns_pull, 4)
         res[f"pull_{name}_ect_naive_ms"] = round(res[f"pull_{name}_gather_then_gemm_ms"]
-                                                 - nonsplit, 4)
+                                                 - ns_pull, 4)
     assert int(w.err.item()) == 0, "fm_ag_gemm_pull reported a timeout"
 
     # --- GEMM-ReduceScatter -------------------------------------------------
@@ -522,9 +586,9 @@ def ect_block(w, iters):
             w.dst[r].add_(tmp32[rows])
 
     log("ECT: GEMM-ReduceScatter")
-    for name, fn in [("nonsplit_fm_gemm", rs_ns_fm), ("nonsplit_hipblaslt", rs_ns_blas),
-                     ("fused", rs_fused), ("naive_chunked", rs_naive)]:
-        med, best = time_loop(fn, iters, 3)
+    meds = time_rounds([("nonsplit_fm_gemm", rs_ns_fm), ("nonsplit_hipblaslt", rs_ns_blas),
+                        ("fused", rs_fused), ("naive_chunked", rs_naive)], iters)
+    for name, med in meds.items():
         res[f"rs_{name}_ms"] = round(med, 4)
     nonsplit = min(res["rs_nonsplit_fm_gemm_ms"], res["rs_nonsplit_hipblaslt_ms"])
     res["rs_ect_ms"] = round(res["rs_fused_ms"] - nonsplit, 4)
@@ -558,53 +622,65 @@ def ect_block(w, iters):
                                            w.epoch, w.mws, order=w.order, err_word=w.err)
 
     # pull mode: layer 0 reads each owner's 16 MiB chunk in place, signals
-    # timed at one link's rate (direct: all seven land at t_link)
+    # timed at one link's rate (direct: all seven land at t_link), each chunk
+    # signalled as w.moe_link_parts token blocks (layer 0 gathers its rows
+    # token by token, so a block need not be a whole tile row)
     t_link_moe = int(w.mTc * w.hidden * 2 / LINK_BYTES_PER_S * 1e9)
 
-    def moe_pull(times):
+    def moe_pull(kind, parts):
+        seq, times = link_schedule(w.order, parts, t_link_moe, kind)
+        views = part_views(w.mpeers, parts)
+        flags = w.mflags[:w.n * parts]
+
         def fn():
             w.epoch += 1
             s = w.sides[0]
             s.wait_stream(cs)
-            fm.fm_chunk_signal_paced(w.mflags[:w.n], times, w.epoch, order=w.order, stream=s)
-            fm.fm_moe_ag_gather_gemm_pull(w.mpeers, w.ids, w.mW1, w.H, w.sp, w.off, w.e0,
-                                          w.mflags[:w.n], w.epoch, w.mws, order=w.order,
-                                          err_word=w.err)
+            fm.fm_chunk_signal_paced(flags, times, w.epoch, order=seq, stream=s)
+            fm.fm_moe_ag_gather_gemm_pull(views, w.ids, w.mW1, w.H, w.sp, w.off, w.e0, flags,
+                                          w.epoch, w.mws, order=seq, err_word=w.err)
             cs.wait_stream(s)
         return fn
 
-    def moe_pull_naive(times):
+    def moe_pull_naive(kind):
+        seq, times = link_schedule(w.order, 1, t_link_moe, kind)
+
         def fn():
             w.epoch += 1
             s = w.sides[0]
             s.wait_stream(cs)
-            fm.fm_chunk_signal_paced(w.mflags[:w.n], times, w.epoch, order=w.order, stream=s)
+            fm.fm_chunk_signal_paced(w.mflags[:w.n], times, w.epoch, order=seq, stream=s)
             cs.wait_stream(s)                   # the whole AllGather first
             w.moe0()
         return fn
 
     log("ECT: token AllGather + MoE layer 0")
-    for name, fn in [("nonsplit", moe_ns), ("fused", moe_fused), ("gather_then_gemm", moe_naive),
-                     ("producers", moe_producers)]:
-        med, best = time_loop(fn, iters, 3)
-        res[f"moe_ag_{name}_ms"] = round(med, 4)
-        check_err(w, f"MoE layer 0 {name}")
-    res["moe_ag_ect_ms"] = round(res["moe_ag_fused_ms"] - res["moe_ag_nonsplit_ms"], 4)
-    res["moe_ag_ect_naive_ms"] = round(res["moe_ag_gather_then_gemm_ms"]
-                                       - res["moe_ag_nonsplit_ms"], 4)
-    res["moe_ag_ect_frac_of_nonsplit"] = round(res["moe_ag_ect_ms"] / res["moe_ag_nonsplit_ms"], 4)
-    res["moe_ag_ect_producers_ms"] = round(res["moe_ag_producers_ms"] - res["moe_ag_nonsplit_ms"],
-                                           4)
+    P = w.moe_link_parts
+    variants = [("ag_nonsplit", moe_ns), ("ag_fused", moe_fused),
+                ("ag_gather_then_gemm", moe_naive), ("ag_producers", moe_producers)]
+    for name in ("direct", "ring"):
+        variants.append((f"pull_{name}_fused", moe_pull(name, P)))
+        if P != 1:
+            variants.append((f"pull_{name}_fused_whole_chunks", moe_pull(name, 1)))
+        variants.append((f"pull_{name}_gather_then_gemm", moe_pull_naive(name)))
+    meds = time_rounds(variants, iters)
+    check_err(w, "MoE layer 0 with its token AllGather")
+    for key, med in meds.items():
+        res[f"moe_{key}_ms"] = round(med, 4)
+    ns = res["moe_ag_nonsplit_ms"]
+    res["moe_ag_ect_ms"] = round(res["moe_ag_fused_ms"] - ns, 4)
+    res["moe_ag_ect_naive_ms"] = round(res["moe_ag_gather_then_gemm_ms"] - ns, 4)
+    res["moe_ag_ect_frac_of_nonsplit"] = round(res["moe_ag_ect_ms"] / ns, 4)
+    res["moe_ag_ect_producers_ms"] = round(res["moe_ag_producers_ms"] - ns, 4)
     res["moe_pull_link_chunk_us"] = round(t_link_moe / 1e3, 1)
-    for name, times in [("direct", [0] + [t_link_moe] * (w.n - 1)),
-                        ("ring", [a * t_link_moe for a in range(w.n)])]:
-        med, _ = time_loop(moe_pull(times), iters, 3)
-        res[f"moe_pull_{name}_fused_ms"] = round(med, 4)
-        check_err(w, f"MoE layer 0 pull {name}")
-        res[f"moe_pull_{name}_ect_ms"] = round(med - res["moe_ag_nonsplit_ms"], 4)
-        med, _ = time_loop(moe_pull_naive(times), iters, 3)
-        res[f"moe_pull_{name}_gather_then_gemm_ms"] = round(med, 4)
-        res[f"moe_pull_{name}_ect_naive_ms"] = round(med - res["moe_ag_nonsplit_ms"], 4)
+    res["moe_pull_link_parts"] = P
+    for name in ("direct", "ring"):
+        res[f"moe_pull_{name}_ect_ms"] = round(res[f"moe_pull_{name}_fused_ms"] - ns, 4)
+        if P != 1:
+            res[f"moe_pull_{name}_ect_whole_chunks_ms"] = round(
+                res[f"moe_pull_{name}_fused_whole_chunks_ms"] - ns, 4)
+        res[f"moe_pull_{name}_ect_naive_ms"] = round(
+            res[f"moe_pull_{name}_gather_then_gemm_ms"] - ns, 4)
     assert int(w.err.item()) == 0, "fm_moe_ag_gather_gemm reported a timeout"
     res["nonsplit_fm_gemm_tflops_4096x12288x6144"] = round(
         w.flop_rs / (res["rs_nonsplit_fm_gemm_ms"] * 1e-3) / 1e12, 1)
@@ -730,6 +806,8 @@ def main():
     w.serial_arrival = args.serial_arrival
     w.arrival = args.arrival
     w.parts = args.parts
+    w.link_parts = args.link_parts
+    w.moe_link_parts = args.moe_link_parts
     cs = torch.cuda.current_stream()
 
     log(f"warmup {args.warmup} steps")

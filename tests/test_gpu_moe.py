@@ -794,6 +794,28 @@ def test_full_moe_ag_pull_link_paced(oracle):
     assert torch.equal(H[:rows].view(torch.int16), H2[:rows].view(torch.int16))
 
 
+def test_full_moe_ag_pull_link_parts(oracle):
+    """EP=8 rank 0 reading the 8 owners' chunks in place, each signalled as two
+    1024-token blocks, the first once half the chunk has crossed its link
+    (direct schedule), the bands ordered by that arrival: routing bit-exact
+    and every row against the oracle's every-element form."""
+    c = wl.MOE_EP8
+    P, n = 2, 8
+    say(f"full moe ag pull EP=8 rank 0, {P} link blocks per chunk")
+    ep8 = _ep8_reference(oracle)
+    inp, e0 = ep8["inp"], ep8["e0"]
+    blocks = inp["X"].reshape(n * P, c["T"] // (n * P), c["hidden"])
+    t_link = int(blocks[0].size * 2 * P / 153e9 * 1e9)
+    times = {ch * P + q: 0 if ch == 0 else (q + 1) * t_link // P
+             for ch in range(n) for q in range(P)}
+    seq = sorted(times, key=lambda i: (times[i], i))
+    off, sp, H, err = _moe_pull_run(inp, blocks, e0, c["n_local"], seq, [times[i] for i in seq])
+    assert err == 0
+    roff, rsp = ep8["roff"], ep8["rsp"]
+    rows = int(roff[-1])
+    assert np.array_equal(off, roff) and np.array_equal(sp[:rows], rsp)
+    assert_close(host64(H[:rows]), ep8["H"], "full moe ag pull blocks, every row")
+
 def test_moe_ag_withheld_chunk_times_out():
     """A token chunk that never arrives: the bounded wait writes
     FM_ERR_TIMEOUT to err_word and the kernel exits (no hang)."""

@@ -162,6 +162,30 @@ def test_full_pull_ag_gemm_link_paced(oracle):
     assert np.array_equal(bits16(C), bits16(_gemm_concat(chunks, Wd, F16)))
 
 
+
+def test_full_pull_ag_gemm_link_parts():
+    """TP=8 rank 0 with each 512-row chunk signalled as two 256-row blocks, the
+    first once half the chunk has crossed its link (direct schedule: every
+    peer's first block at t_link/2, its second at t_link), the tile order
+    following that arrival: every element against the oracle's every-element
+    form, and bit-identical to fm_gemm on the concatenation."""
+    from oracle import full
+    c = wl.AG_TP8
+    n, Mc, N, K = c["n_chunks"], c["Mc"], c["N"], c["K"]
+    P = 2
+    say(f"full fm_ag_gemm_pull {n}x{Mc} x {N} x {K}, {P} link blocks per chunk")
+    chunks, W, _ = wl.ag_inputs(n, Mc, N, K, F16, seed=c["seed"], arrival="ring")
+    t_link = int(Mc * K * 2 / 153e9 * 1e9)
+    times = {ch * P + q: 0 if ch == 0 else (q + 1) * t_link // P
+             for ch in range(n) for q in range(P)}
+    seq = sorted(times, key=lambda i: (times[i], i))
+    p = Pull(chunks.reshape(n * P, Mc // P, K), F16)
+    Wd = dev16(W, F16)
+    C = p.run(Wd, N, seq, [times[i] for i in seq], hint=seq)
+    assert p.err.item() == 0
+    assert_close(host64(C), full.ag_gemm(F16, list(chunks), W), "full pull blocks, every element")
+    assert np.array_equal(bits16(C), bits16(_gemm_concat(chunks, Wd, F16)))
+
 # ---------------------------------------------------------------------------
 # AllGather-GEMM with producer workgroups in the same launch
 # ---------------------------------------------------------------------------
