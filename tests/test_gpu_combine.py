@@ -292,9 +292,10 @@ def test_combine_outputs_near_and_past_2gib(oracle, T):
     """out of 131000 x 4096 fp32 (2.146e9 bytes: the register-fetch epilogue,
     whose 32-bit offsets then reach just under its limit) and of 140000 x
     4096 (2.29e9 bytes: past the limit, so the LDS-DMA epilogue runs).  H is
-    drawn directly (ffn = 64, one K step) and out starts at zero; tokens
-    sampled across the whole range, the last 64 among them, match the
-    oracle's combine, and the routing is bit-exact."""
+    drawn directly (ffn = 64, one K step) and out starts at zero; every token
+    matches the oracle's every-element combine (compared in row blocks),
+    tokens sampled across the whole range, the last 64 among them, match its
+    loops, and the routing is bit-exact."""
     import torch
     import tile_gemm_communication_amd as fm
     hidden, ffn, E, nl, topk, e0 = 4096, 64, 16, 8, 2, 0
@@ -329,3 +330,10 @@ def test_combine_outputs_near_and_past_2gib(oracle, T):
     ref = oracle.moe_layer1_tokens(BF16, Hb, W2b, ids, wts, rsp, roff, seed, e0, toks)
     got = host64(out[torch.from_numpy(toks).to(dev)])
     assert_close(got, ref, f"combine, out of {T} rows")
+    from oracle import full
+    want = full.moe_layer1(BF16, Hb, W2b, ids, wts, rsp, roff, seed, e0)
+    del seed
+    for r0 in range(0, T, 16384):
+        r1 = min(T, r0 + 16384)
+        assert_close(host64(out[r0:r1]), want[r0:r1],
+                     f"combine, out of {T} rows, rows {r0}..{r1}")
