@@ -290,7 +290,8 @@ def _cus():
 def test_split_tail_bit_identical(oracle, monkeypatch, extra_tiles, K):
     """A last wave of at most half the CUs runs as 256x128 halves in a second
     launch.  Per output element the K sum is unchanged, so the result equals
-    the unsplit schedule bit for bit, and the oracle within the parity bar.
+    the unsplit schedule bit for bit, and the oracle (every element, and
+    sampled against its loops) within the parity bar.
     Shapes: one full wave plus half a wave; one full wave plus 7 tiles (and a
     ragged K); fewer tiles than half the CUs (halves only)."""
     import torch
@@ -315,6 +316,7 @@ def test_split_tail_bit_identical(oracle, monkeypatch, extra_tiles, K):
     rows, cols = sample_coords(M, N, 2000, seed=5, tile=(256, 128))
     assert_close(_at(C1, rows, cols), oracle.gemm_entries(F16, A, B, rows, cols),
                  "split tail samples")
+    assert_close(host64(C1), full.gemm(F16, A, B), "split tail, every element")
 
 
 def test_more_row_tiles_than_the_ordered_table(oracle):

@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 
 import workloads as wl
+from oracle import full
 from gpu_util import (F16, BF16, assert_close, bits16, dev16, host64, say, sample_coords,
                       side_stream)
 
@@ -142,7 +143,8 @@ def test_pull_withheld_signal_times_out():
 def test_full_pull_ag_gemm_link_paced(oracle):
     """TP=8 rank 0 (8 chunks of 512 x 12288 fp16, W 12288 x 6144), chunks in
     ring order signalled at the one-link rate (12.58 MB at 153 GB/s apart):
-    sampled outputs against the oracle, and bit-identical to fm_gemm."""
+    every element against the oracle's every-element form, sampled outputs
+    against its loops, and bit-identical to fm_gemm."""
     c = wl.AG_TP8
     n, Mc, N, K = c["n_chunks"], c["Mc"], c["N"], c["K"]
     say(f"full fm_ag_gemm_pull {n}x{Mc} x {N} x {K}, link-paced")
@@ -159,6 +161,7 @@ def test_full_pull_ag_gemm_link_paced(oracle):
     cc = torch.from_numpy(cols).to(C.device)
     got = C[r, cc].float().cpu().numpy().astype(np.float64)
     assert_close(got, oracle.gemm_entries(F16, X, W, rows, cols), "full pull samples")
+    assert_close(host64(C), full.ag_gemm(F16, list(chunks), W), "full pull, every element")
     assert np.array_equal(bits16(C), bits16(_gemm_concat(chunks, Wd, F16)))
 
 
@@ -169,7 +172,6 @@ def test_full_pull_ag_gemm_link_parts():
     peer's first block at t_link/2, its second at t_link), the tile order
     following that arrival: every element against the oracle's every-element
     form, and bit-identical to fm_gemm on the concatenation."""
-    from oracle import full
     c = wl.AG_TP8
     n, Mc, N, K = c["n_chunks"], c["Mc"], c["N"], c["K"]
     P = 2
@@ -253,7 +255,8 @@ def test_producers_layouts(oracle, n_chunks, Mc, dt, n_prod, local):
 
 def test_full_producers_ag_gemm(oracle):
     """TP=8 rank 0 with the default producer count: the local chunk in place,
-    seven copied in ring order; sampled outputs against the oracle, X and C
+    seven copied in ring order; every element against the oracle's
+    every-element form and sampled outputs against its loops, X and C
     bit-identical to the concatenation and to fm_gemm; a second call with the
     same counters (left at zero) gives the same bits."""
     import torch
@@ -271,6 +274,7 @@ def test_full_producers_ag_gemm(oracle):
     cc = torch.from_numpy(cols).to(C.device)
     got = C[r, cc].float().cpu().numpy().astype(np.float64)
     assert_close(got, oracle.gemm_entries(F16, Xh, W, rows, cols), "full producers samples")
+    assert_close(host64(C), full.ag_gemm(F16, list(chunks), W), "full producers, every element")
     ref = bits16(_gemm_concat(chunks, Wd, F16))
     assert np.array_equal(bits16(C), ref)
     C2, _ = _producers_run(chunks, F16, Wd, N, order, local=(0,), counters=counters)
