@@ -22,7 +22,9 @@ fp16/bf16 MFMA peak, and the effective communication time
 ECT = OverallTime - GEMM_non-split (FLUX review, "核心公式") of the fused
 AllGather and ReduceScatter operators against the non-split GEMM (this
 library's and hipBLASLt's through torch.matmul) and against the naive
-chunk-by-chunk launch sequence.
+chunk-by-chunk launch sequence; the pull forms with link-paced signals, each
+chunk signalled as row blocks as they cross the link.  Each comparison is
+timed in alternating passes of its variants, so clock drift moves them alike.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
