@@ -242,6 +242,19 @@ def test_full_dense_gemm(oracle):
     assert_close(host64(C), full.gemm(F16, A, B), "full gemm, every element")
 
 
+
+@pytest.mark.parametrize("out32", [False, True])
+def test_full_dense_gemm_bf16(out32):
+    """The full-size non-split GEMM (4096 x 12288 x 6144) with bf16 inputs,
+    C in bf16 or fp32: every element against the oracle's every-element
+    form."""
+    c = wl.DENSE_GEMM
+    M, N, K = c["M"], c["N"], c["K"]
+    say(f"full fm_gemm bf16 {M}x{N}x{K} out32={out32}")
+    A, B = wl.gemm_inputs(M, N, K, BF16, seed=c["seed"] + 7)
+    C = _gemm(A, B, BF16, out32=out32)
+    assert_close(host64(C), full.gemm(BF16, A, B), f"full bf16 gemm (fp32 C: {out32})")
+
 def test_full_ag_gemm(oracle):
     import torch
     c = wl.AG_TP8

@@ -245,6 +245,31 @@ def test_full_moe_rank0(oracle):
                  "full combine, every token")
 
 
+@pytest.mark.parametrize("act", [1, 2, 3])
+def test_full_moe_layer0_activation(oracle, act):
+    """EP=8 rank 0 layer 0 with the fused activation (ReLU, tanh-form GELU,
+    SiLU): every row against the oracle's every-element layer 0 followed by
+    its activation."""
+    import torch
+    import tile_gemm_communication_amd as fm
+    c = wl.MOE_EP8
+    say(f"full moe layer0 EP=8 rank 0, act={act}")
+    ep8 = _ep8_reference(oracle)
+    inp, e0, nl, T = ep8["inp"], ep8["e0"], c["n_local"], c["T"]
+    roff = ep8["roff"]
+    rows = int(roff[-1])
+    sp = torch.full((T * 2,), -1, dtype=torch.int32, device="cuda:0")
+    off = torch.zeros(nl + 1, dtype=torch.int32, device="cuda:0")
+    H = torch.zeros((T * 2, c["ffn"]), dtype=torch.bfloat16, device="cuda:0")
+    fm.fm_moe_gather_gemm_act(dev16(inp["X"], BF16), _i32(inp["topk_ids"]),
+                              dev16(inp["W1"], BF16), H, sp, off, e0, act,
+                              fm.moe_workspace(T, 2, c["hidden"], nl))
+    torch.cuda.synchronize()
+    assert np.array_equal(off.cpu().numpy(), roff)
+    assert_close(host64(H[:rows]), oracle.activation(act, ep8["H"]),
+                 f"full layer0 act {act}, every row")
+
+
 @pytest.mark.parametrize("T,hidden,ffn,E,nl,topk", [(4096, 1024, 512, 16, 8, 2),
                                                     (1500, 392, 200, 8, 8, 4)])
 def test_moe_combine_deterministic(oracle, T, hidden, ffn, E, nl, topk):
