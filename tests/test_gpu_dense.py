@@ -255,22 +255,24 @@ def test_full_dense_gemm_bf16(out32):
     C = _gemm(A, B, BF16, out32=out32)
     assert_close(host64(C), full.gemm(BF16, A, B), f"full bf16 gemm (fp32 C: {out32})")
 
-def test_full_ag_gemm(oracle):
+
+@pytest.mark.parametrize("dt", [F16, BF16])
+def test_full_ag_gemm(oracle, dt):
     import torch
     c = wl.AG_TP8
     n, Mc, N, K = c["n_chunks"], c["Mc"], c["N"], c["K"]
-    say(f"full fm_ag_gemm {n}x{Mc} x {N} x {K}")
-    chunks, W, order = wl.ag_inputs(n, Mc, N, K, F16, seed=c["seed"], arrival="ring")
-    arr = Arrival(chunks, F16, K)
-    Wd = dev16(W, F16)
+    say(f"full fm_ag_gemm {n}x{Mc} x {N} x {K} dt={dt}")
+    chunks, W, order = wl.ag_inputs(n, Mc, N, K, dt, seed=c["seed"], arrival="ring")
+    arr = Arrival(chunks, dt, K)
+    Wd = dev16(W, dt)
     arr.poison()
     C = _ag_run(arr, Wd, N, order, arr.next_epoch(), local=0)
     assert arr.err.item() == 0
     X = np.concatenate(list(chunks), axis=0)
     rows, cols = sample_coords(n * Mc, N, 3000, seed=2, tile=(256, 128))
-    assert_close(_at(C, rows, cols), oracle.gemm_entries(F16, X, W, rows, cols),
+    assert_close(_at(C, rows, cols), oracle.gemm_entries(dt, X, W, rows, cols),
                  "full ag samples")
-    assert_close(host64(C), full.ag_gemm(F16, list(chunks), W), "full ag, every element")
+    assert_close(host64(C), full.ag_gemm(dt, list(chunks), W), "full ag, every element")
     ref = torch.empty_like(C)
     import tile_gemm_communication_amd as fm
     fm.fm_gemm(arr.X, Wd, ref)
@@ -278,19 +280,20 @@ def test_full_ag_gemm(oracle):
     assert torch.equal(C.view(torch.int16), ref.view(torch.int16)), "AG != non-split GEMM bitwise"
 
 
-def test_full_gemm_rs(oracle):
+@pytest.mark.parametrize("dt", [F16, BF16])
+def test_full_gemm_rs(oracle, dt):
     c = wl.RS_TP8
     M, N, K, P = c["M"], c["N"], c["K"], c["n_ranks"]
-    say(f"full fm_gemm_rs {M}x{N}x{K} P={P}")
-    A, W, seeds = wl.rs_inputs(M, N, K, P, F16, seed=c["seed"])
-    got = _rs(A, W, seeds, F16, rank=0)
+    say(f"full fm_gemm_rs {M}x{N}x{K} P={P} dt={dt}")
+    A, W, seeds = wl.rs_inputs(M, N, K, P, dt, seed=c["seed"])
+    got = _rs(A, W, seeds, dt, rank=0)
     rows, cols = sample_coords(M, N, 3000, seed=3)
-    ref = oracle.gemm_entries(F16, A, W, rows, cols)
+    ref = oracle.gemm_entries(dt, A, W, rows, cols)
     Ms = M // P
     delta = np.array([got[r // Ms][r % Ms, cc] - seeds[r // Ms][r % Ms, cc]
                       for r, cc in zip(rows, cols)])
     assert_close(delta, ref, "full rs samples")
-    for p, want in enumerate(full.gemm_rs(F16, A, W, list(seeds))):
+    for p, want in enumerate(full.gemm_rs(dt, A, W, list(seeds))):
         assert_close(got[p] - seeds[p], want - seeds[p], f"full rs slice {p}, every element")
 
 

@@ -245,6 +245,29 @@ def test_full_moe_rank0(oracle):
                  "full combine, every token")
 
 
+def test_full_moe_rank0_f16(oracle):
+    """The EP=8 rank-0 layer with fp16 inputs: routing bit-exact, every row of
+    layer 0 and every token of the combine (run on the GPU's own H) against
+    the oracle's every-element forms."""
+    import torch
+    c = wl.MOE_EP8
+    say("full moe EP=8 rank 0, fp16")
+    inp = wl.moe_inputs(c["T"], c["hidden"], c["ffn"], c["n_experts"], c["n_local"], c["topk"],
+                        F16, seed=c["seed"] + 11, zipf_s=c["zipf_s"])
+    e0, nl = c["rank"] * c["n_local"], c["n_local"]
+    roff, rsp = oracle.moe_route(inp["topk_ids"], e0, nl)
+    off, sp, H, out = _moe_run(inp, e0, nl, F16)
+    rows = int(roff[-1])
+    assert np.array_equal(off, roff) and np.array_equal(sp[:rows], rsp)
+    assert_close(host64(H[:rows]), full.moe_layer0(F16, inp["X"], inp["W1"], rsp, roff, 2),
+                 "full fp16 layer0, every row")
+    Hbits = H[:rows].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    want = full.moe_layer1(F16, Hbits, inp["W2"], inp["topk_ids"], inp["topk_weights"], rsp,
+                           roff, inp["out_seed"], e0)
+    assert_close(host64(out) - inp["out_seed"], want - inp["out_seed"],
+                 "full fp16 combine, every token")
+
+
 @pytest.mark.parametrize("act", [1, 2, 3])
 def test_full_moe_layer0_activation(oracle, act):
     """EP=8 rank 0 layer 0 with the fused activation (ReLU, tanh-form GELU,
