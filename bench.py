@@ -439,9 +439,10 @@ def moe_baselines(w, iters):
         raise RuntimeError(f"pre-gathered MoE layer differs from the fused one: {rel:.3e}")
     res = {"rows_local": rows, "pregathered_vs_fused_rel_frobenius": rel}
     out = seed.clone()
-    for name, fn in (("fused", fused), ("pregathered_fm_gemm", pregathered),
-                     ("torch_loop", torch_loop)):
-        med, _ = time_loop(lambda: fn(out), iters, 3)
+    meds = time_rounds([(name, lambda fn=fn: fn(out))
+                        for name, fn in (("fused", fused), ("pregathered_fm_gemm", pregathered),
+                                         ("torch_loop", torch_loop))], iters)
+    for name, med in meds.items():
         res[f"moe_layer_{name}_ms"] = round(med, 4)
     check_err(w, "MoE layer (fused)")
     return res
