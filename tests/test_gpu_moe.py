@@ -842,13 +842,15 @@ def test_full_moe_ag_pull_link_paced(oracle):
     assert torch.equal(H[:rows].view(torch.int16), H2[:rows].view(torch.int16))
 
 
-def test_full_moe_ag_pull_link_parts(oracle):
-    """EP=8 rank 0 reading the 8 owners' chunks in place, each signalled as two
-    1024-token blocks, the first once half the chunk has crossed its link
-    (direct schedule), the bands ordered by that arrival: routing bit-exact
-    and every row against the oracle's every-element form."""
+@pytest.mark.parametrize("P", [2, 4])
+def test_full_moe_ag_pull_link_parts(oracle, P):
+    """EP=8 rank 0 reading the 8 owners' chunks in place, each signalled as P
+    token blocks (4 is the benchmark's default), block q once (q+1)/P of the
+    chunk has crossed its link (direct schedule), the bands ordered by that
+    arrival: routing bit-exact and every row against the oracle's
+    every-element form."""
     c = wl.MOE_EP8
-    P, n = 2, 8
+    n = 8
     say(f"full moe ag pull EP=8 rank 0, {P} link blocks per chunk")
     ep8 = _ep8_reference(oracle)
     inp, e0 = ep8["inp"], ep8["e0"]
