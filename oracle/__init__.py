@@ -7,6 +7,8 @@ product path never does, and it shares no code with the HIP library.
 
 The arithmetic lives in ``fm_oracle.c`` (fp64 accumulation, explicit gather,
 scatter and reduce loops).  This module only marshals numpy arrays into it.
+``full.py`` computes the same definitions for every element of the full-size
+workloads, with numpy's float64 matrix product as the one library step.
 
 Sources, by page and section:
   * FLUX paper review ("FLUX: Fast Software-based Communication Overlap On GPUs
