@@ -1,6 +1,7 @@
 """bench.py on the GPU: a short run prints one JSON line that carries the
 contract's keys, a roofline for the dominant kernel, per-op median and
-minimum times, and the cold-cache timing of each op."""
+minimum times, and the cold-cache timing of each op; and the two probe modes
+behind the profiles (the matrix-core ceiling and the byte-counter copy)."""
 import json
 import os
 import subprocess
@@ -44,3 +45,35 @@ def test_short_bench_line():
     rf = d["roofline"]
     assert rf["kernel"] in names and rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s"
     assert 0 < rf["frac"] < 1 and abs(rf["achieved"] / rf["peak"] - rf["frac"]) < 1e-3
+
+
+def _bench_json(args, timeout=110):
+    r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py")] + args,
+                       capture_output=True, text=True, timeout=timeout, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [x for x in r.stdout.strip().splitlines() if x.startswith("{")]
+    assert len(lines) == 1
+    return json.loads(lines[0])
+
+
+def test_mfma_ceiling_mode():
+    """bench.py --mfma-ceiling (the register-only matrix-core probe behind the
+    clock evidence): every form reports a rate, a clock and a fraction of the
+    peak at that clock that a real chip can reach."""
+    say("bench.py --mfma-ceiling")
+    rows = _bench_json(["--mfma-ceiling"])["mfma_ceiling"]
+    assert len(rows) == 16
+    forms = {(r["dtype"], r["mfma"], r["waves_per_simd"], r["operands"]) for r in rows}
+    assert len(forms) == 16
+    for r in rows:
+        assert r["tflops"] > 0 and 0.3 < r["clock_ghz"] < 3.0, r
+        assert 0 < r["frac_at_clock"] <= 1.02, r
+
+
+def test_copy_probe_mode():
+    """bench.py --copy-probe (the known-size copy that calibrates the HBM
+    byte counters) copies what it says and reports the sizes."""
+    say("bench.py --copy-probe 16")
+    d = _bench_json(["--copy-probe", "16"])
+    assert d == {"copy_probe_bytes_read": 16 << 20, "copy_probe_bytes_written": 16 << 20,
+                 "dispatches": 3}
