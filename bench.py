@@ -790,7 +790,7 @@ def mfma_ceiling():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the fused kernels "
+        print(json.dumps({"error": "bench.py measures one GPU only: the fused kernels "
                                    "emulate the peers of a TP=8/EP=8 group on one device; "
                                    "run with --gpus 1"}))
         sys.exit(2)
